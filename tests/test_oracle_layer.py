@@ -1,0 +1,155 @@
+"""Pins of the oracle's full layer: dense brute force, exact dot products, an independent
+decode through torch's float8 type, gate/up orientation and finalization."""
+
+from fractions import Fraction
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import layer as olayer
+from moe_inputs import TINY
+from tests.problem import build_layer_problem, oracle_forward, oracle_dense
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    p = build_layer_problem(TINY)
+    return p, oracle_forward(p)
+
+
+def test_grouped_equals_dense_bit_for_bit(tiny):
+    p, g = tiny
+    d = oracle_dense(p)
+    assert np.array_equal(g["out"], d["out"])
+    k = p["cfg"].k
+    for t in range(p["cfg"].T):
+        for j in range(k):
+            i = g["expanded_row_idx"][t * k + j]
+            assert np.array_equal(g["a_codes"][i], d["a_codes"][t, j])
+            assert np.array_equal(g["a_scales"][i], d["a_scales"][t, j])
+            assert np.array_equal(g["o"][i], d["o"][t, j])
+            assert np.array_equal(g["h"][i], d["h"][t, j])
+
+
+def test_output_is_not_trivial(tiny):
+    p, g = tiny
+    out = oracle.bf16_bits_to_f32(g["out"])
+    assert np.all(np.isfinite(out)) and np.std(out) > 0
+    assert np.count_nonzero(out) > 0.9 * out.size
+    # the intermediate uses many codes and scales, not a degenerate corner
+    assert len(np.unique(g["a_codes"])) >= 14 and len(np.unique(g["a_scales"])) > 10
+
+
+def _torch_decode(codes_packed, scales):
+    """Independent decode: nibble table lookup times torch's float8_e4m3fn conversion."""
+    lut = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6],
+                       dtype=torch.float64)
+    p = torch.from_numpy(np.ascontiguousarray(codes_packed))
+    lo, hi = (p & 0xF).long(), (p >> 4).long()
+    vals = torch.stack([lut[lo], lut[hi]], dim=-1).reshape(*p.shape[:-1], p.shape[-1] * 2)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).to(torch.float64)
+    return (vals.reshape(*vals.shape[:-1], -1, 16) * s[..., None]).reshape(vals.shape)
+
+
+def test_fc1_against_independent_torch_decode(tiny):
+    p, g = tiny
+    k, I = p["cfg"].k, p["cfg"].I
+    xc = oracle.pack_nibbles(g["x_codes"])
+    xdec = _torch_decode(xc, g["x_scales"])
+    for i in range(p["cfg"].T * k):
+        e = int(g["sorted_ids"][i])
+        t = int(g["sorted_row_idx"][i]) // k
+        w = _torch_decode(p["w13"][e], p["w13_sf"][e])
+        s = (xdec[t] @ w.T).numpy().astype(np.float32)          # exact: small sums
+        h = (s * p["alpha1"][e]).astype(np.float32)
+        assert np.array_equal(h, g["h"][i])
+        a = oracle.situ(h[:I], h[I:], 4.0, 25.0)
+        assert np.array_equal(a, g["a"][i])
+
+
+def test_fc2_against_independent_torch_decode(tiny):
+    p, g = tiny
+    adec = _torch_decode(oracle.pack_nibbles(g["a_codes"]), g["a_scales"])
+    for i in range(p["cfg"].T * p["cfg"].k):
+        e = int(g["sorted_ids"][i])
+        w = _torch_decode(p["w2"][e], p["w2_sf"][e])
+        o = ((adec[i] @ w.T).numpy().astype(np.float32) * p["alpha2"][e]).astype(np.float32)
+        assert np.array_equal(o, g["o"][i])
+
+
+def test_fc_exact_matches_rational_arithmetic_including_int64_path():
+    rng = np.random.default_rng(5)
+    grid = oracle.e2m1_decode(np.arange(16))
+    for K, smax in ((64, 2.0), (7168, 448.0)):
+        a = grid[rng.integers(0, 16, (3, K))] * smax
+        w = grid[rng.integers(0, 16, (2, K))] * smax * 1.125
+        if smax == 448.0:
+            a[0] = 6 * 448.0            # forces sum|terms| >= 2^32 -> int64 path
+            w[0] = 6 * 448.0 * 1.125
+        out = olayer.fc_exact(a, w)
+        for r in range(3):
+            for n in range(2):
+                exact = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a[r], w[n]))
+                f = np.float32(float(exact))
+                # nearest fp32 to the rational (float(exact) is already correctly rounded
+                # to double; the fp32 candidates around it decide)
+                cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+                best = min(cands, key=lambda c: (abs(Fraction(float(c)) - exact),
+                                                 int(np.array(c, np.float32).view(np.uint32)) & 1))
+                assert out[r, n] == best
+
+
+def test_gate_rows_come_before_up_rows():
+    # One input element of value 1 picks column 0 of FC1; gate row i holds g_i, up row i
+    # holds u_i there, so the SiTU input pairs are (g_i, u_i), not (u_i, g_i).
+    I, H = 16, 32
+    xdec = np.zeros((1, H)); xdec[0, 0] = 1.0
+    g = np.array([1.5, 3, -2, 0.5] * 4); u = np.array([3, 1.5, 0.5, -2] * 4)
+    w13d = np.zeros((2 * I, H)); w13d[:I, 0] = g; w13d[I:, 0] = u
+    w2d = np.zeros((H, I)); w2d[0, 0] = 1.0
+    h, a, ac, as_, o = olayer._expert_rows(xdec, w13d, w2d, 1.0, 1.0, 1.0, 4.0, 25.0)
+    assert np.array_equal(a[0], oracle.situ(g.astype(np.float32), u.astype(np.float32)))
+    assert not np.array_equal(a[0], oracle.situ(u.astype(np.float32), g.astype(np.float32)))
+
+
+def test_finalize_one_hot_and_scaling(tiny):
+    p, g = tiny
+    k = p["cfg"].k
+    q = dict(p)
+    one = np.zeros_like(p["rw"]); one[:, 1] = 0x3F80             # BF16 1.0 on the 2nd pick
+    q["rw"] = one
+    g1 = oracle_forward(q)
+    rows = g["expanded_row_idx"].reshape(-1, k)[:, 1]
+    assert np.array_equal(g1["out"], oracle.f64_to_bf16_bits(g["o"][rows].astype(np.float64)))
+    # doubling every route weight (exact in BF16) doubles every output exactly
+    q["rw"] = (p["rw"].astype(np.uint32) + (1 << 7)).astype(np.uint16)   # exponent + 1
+    g2 = oracle_forward(q)
+    assert np.array_equal(oracle.bf16_bits_to_f32(g2["out"]), 2 * oracle.bf16_bits_to_f32(g["out"]))
+
+
+def test_per_expert_situ_parameters_change_only_their_experts(tiny):
+    p, g = tiny
+    q = dict(p)
+    E = p["cfg"].E
+    beta = np.full(E, 4.0, np.float32); lam = np.full(E, 25.0, np.float32)
+    q["beta"], q["lam"] = beta, lam
+    assert np.array_equal(oracle_forward(q)["out"], g["out"])     # explicit defaults
+    e0 = int(g["sorted_ids"][0])
+    beta2 = beta.copy(); beta2[e0] = 3.0
+    q["beta"] = beta2
+    g2 = oracle_forward(q)
+    changed = np.any(g2["a"] != g["a"], axis=1)
+    assert changed.any() and np.all(g["sorted_ids"][changed] == e0)
+
+
+def test_duplicate_expert_in_a_token_is_two_rows():
+    p = build_layer_problem(dataclasses.replace(TINY, name="tiny_dup"))
+    p["ids"] = p["ids"].copy()
+    p["ids"][0, 1] = p["ids"][0, 0]
+    g = oracle_forward(p)
+    d = oracle_dense(p)
+    assert np.array_equal(g["out"], d["out"])
+    assert g["counts"].sum() == p["cfg"].T * p["cfg"].k
