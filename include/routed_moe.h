@@ -1,0 +1,191 @@
+/*
+ * routed_moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer.
+ *
+ * The layer ("Cake SiTU backend", FlashInfer docs, intro paragraph): BF16 tokens x[T,H]
+ * are quantized to group-16 NVFP4, routed to top-k experts, pushed through FC1 (fused
+ * gate/up rows), the SiTU activation, NVFP4 requantization and FC2, and combined with
+ * the BF16 route weights into BF16 out[T,H].  The routing primitive follows
+ * "torch_npu.npu_moe_init_routing_v2" (Ascend API reference, section 计算公式).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are GPU global-memory addresses; "host" are CPU memory.
+ *     The caller owns every buffer; the library never allocates, frees or retains one.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs asynchronously; the
+ *     library never reads device memory back to the host and never synchronizes, so a
+ *     whole call can be captured into a hipGraph and replayed ("Cake SiTU backend",
+ *     section "Caller-owned execution": submission allocates nothing and owns no graph).
+ *   - Arguments are validated on the host before any HIP call; a bad argument returns
+ *     an error code and enqueues nothing.  Device-side data (expert ids, scales) is
+ *     the caller's contract and is not checked (ids must lie in [0, E)).
+ *   - Calls that run concurrently need distinct workspace and output buffers.
+ *   - BF16 is passed as 16-bit patterns; "E4M3" is float8_e4m3fn (bias 7, max 448);
+ *     NVFP4 codes are E2M1 nibbles, two per byte, element 2b in the low nibble of byte b.
+ */
+#ifndef ROUTED_MOE_H
+#define ROUTED_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t;   /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = -2,        /* dimensions outside what the kernels implement */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_HIP = -4                 /* a HIP launch or runtime call failed */
+} moe_status_t;
+
+/* Layer dimensions: H (hidden), I (intermediate, per TP rank), E (experts), k (top-k).
+ * Supported: H % 128 == 0, I % 64 == 0, 128 <= H <= 16384, 64 <= I <= 4096,
+ * 1 <= E <= 4096, 1 <= k <= 64.  The page's shape is H=3584, I=384, E=896, k=16
+ * ("Cake SiTU backend", intro). */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t num_experts;
+  int32_t top_k;
+} moe_dims_t;
+
+/* Largest token count of one moe_forward call ("Cake SiTU backend", intro: 1..16384). */
+#define MOE_MAX_TOKENS 16384
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* moe_status_string(moe_status_t s);
+
+/* ------------------------------------------------------------------------------------
+ * Sizes.  Host-only: no HIP call, no device access ("Cake SiTU backend", section
+ * "Caller-owned execution": the size query uses host metadata only).
+ * ------------------------------------------------------------------------------------ */
+
+/* Workspace bytes of moe_forward for any T <= max_tokens.  Monotone in max_tokens, so a
+ * buffer sized for the maximum serves every smaller call (same section). */
+moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, size_t* bytes /*host*/);
+
+/* Bytes of the prepared (re-laid-out) weights written by moe_prepare_weights: the FC1 and
+ * FC2 codes and block scales, E * (2I*H/2 + 2I*H/16 + H*Ip/2 + H*Ip/16) with Ip = I
+ * rounded up to a multiple of 128 (zero padding). */
+moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
+
+/* Byte offsets, inside the moe_forward workspace for a call with T tokens, of the
+ * intermediates that call leaves behind (for inspection and testing; the contents are
+ * valid after the call completes and until the workspace is reused):
+ *   x_codes   u8  [T, H/2]    NVFP4 codes of x           x_scales  u8  [T, H/16] E4M3
+ *   sorted_ids      i32 [T*k] expert of each sorted row  (keyValueSort keys)
+ *   sorted_row_idx  i32 [T*k] flat id t*k+j of each sorted row
+ *   expanded_row_idx i32 [T*k] gather map: sorted position of flat id f
+ *   expert_counts   i32 [E]   rows per expert;  expert_cumsum i32 [E] inclusive prefix sum
+ *   a_codes   u8  [T*k, I/2]  requantized SiTU output, sorted row order
+ *   a_scales  u8  [T*k, I/16]
+ *   o_rows    bf16 [T*k, H]   FC2 output per sorted row, alpha2 applied
+ *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
+ *                             (0 for an expert with no rows; a calibration statistic) */
+typedef struct {
+  size_t x_codes, x_scales;
+  size_t sorted_ids, sorted_row_idx, expanded_row_idx;
+  size_t expert_counts, expert_cumsum;
+  size_t a_codes, a_scales;
+  size_t o_rows;
+  size_t a_amax;
+  size_t total;              /* bytes the call uses; <= moe_workspace_size(T) */
+} moe_workspace_layout_t;
+
+moe_status_t moe_workspace_layout(moe_dims_t d, int32_t T, moe_workspace_layout_t* out /*host*/);
+
+/* Workspace bytes of moe_route for num_rows tokens, top_k, num_experts. */
+moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t num_experts,
+                                      size_t* bytes /*host*/);
+
+/* ------------------------------------------------------------------------------------
+ * Preparation (once, before any forward call).
+ * ------------------------------------------------------------------------------------ */
+
+/* Group-16 NVFP4 quantization of BF16 rows with one fp32 encoding scale per group of
+ * rows: src is [groups, rows_per_group, K] BF16 (device, contiguous); q is float32
+ * [groups] (device); codes u8 [groups*rows_per_group, K/2], scales u8 [.., K/16] (device).
+ * Per 16 consecutive values v of a row: s = E4M3(min(fp32(fp32(amax|v| * q)/6), 448)),
+ * round-to-nearest-even; enc = q/s (0 when s = 0); code = E2M1(fp32(v*enc)),
+ * nearest-even, saturating at 6, sign kept.  This is the "group-16 NVFP4 input
+ * quantization" of "Cake SiTU backend" (intro; the scale arithmetic order is this
+ * library's reading, the pages do not give it).  Used for x inside moe_forward and for
+ * weights (one group per expert, q = qW[e]) at preparation.  K % 16 == 0, K <= 65536. */
+moe_status_t moe_quantize_nvfp4(const uint16_t* src /*device*/, int64_t groups,
+                                int64_t rows_per_group, int32_t K, const float* q /*device*/,
+                                uint8_t* codes /*device*/, uint8_t* scales /*device*/,
+                                moe_stream_t stream);
+
+/* Re-lay canonical NVFP4 expert weights into the library's private layout ("Cake SiTU
+ * backend", section "Prepared weights and scales": weights are prepared once and their
+ * block scales travel with the packed bytes).  Canonical inputs (device, contiguous):
+ *   w13 u8 [E, 2I, H/2]  FC1 codes, rows [0,I) gate then [I,2I) up;  w13_sf u8 [E, 2I, H/16]
+ *   w2  u8 [E, H, I/2]   FC2 codes;                                   w2_sf  u8 [E, H, I/16]
+ * `prepared` (device) receives moe_prepared_weights_size() bytes; it must not alias the
+ * inputs.  The layout is private: only moe_forward reads it. */
+moe_status_t moe_prepare_weights(moe_dims_t d, const uint8_t* w13, const uint8_t* w13_sf,
+                                 const uint8_t* w2, const uint8_t* w2_sf, void* prepared,
+                                 size_t prepared_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * The routing primitive ("torch_npu.npu_moe_init_routing_v2", section 计算公式, steps
+ * 1-5, dropless, full expert range, gather index type 0, cumsum histogram type 0):
+ *   sorted_expert_idx, sorted_row_idx = stable keyValueSort(expert_idx, f = t*K + j)
+ *   expanded_row_idx[sorted_row_idx[i]] = i
+ *   expert_cumsum[e] = number of rows with expert <= e          (inclusive)
+ *   quant MOE_ROUTE_QUANT_NONE:          expanded_x[i] = x[sorted_row_idx[i] / K]  (BF16)
+ *   quant MOE_ROUTE_QUANT_INT8_DYNAMIC:  scale_t = fp32(row_max|x_t| / 127),
+ *        q_t = clip(round_half_even(fp32(x_t / scale_t)), -127, 127) (0 if scale_t == 0),
+ *        expanded_x[i] = q_{sorted_row_idx[i]/K} (int8), expanded_scale[i] = scale_t.
+ * Buffers (device): x BF16 [N, H]; expert_idx i32 [N, K] with values in [0, E);
+ * expanded_x [N*K, H] (BF16 or int8); expanded_scale f32 [N*K] (INT8 mode; else NULL);
+ * expanded_row_idx, sorted_expert_idx, sorted_row_idx i32 [N*K] (the last two may be
+ * NULL); expert_cumsum i32 [E].  Limits: 1 <= N, N*K <= 2^24, H % 8 == 0, H <= 65536,
+ * 1 <= E <= 4096, 1 <= K <= 64.
+ * ------------------------------------------------------------------------------------ */
+typedef enum {
+  MOE_ROUTE_QUANT_NONE = 0,
+  MOE_ROUTE_QUANT_INT8_DYNAMIC = 1
+} moe_route_quant_t;
+
+moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
+                       const uint16_t* x, const int32_t* expert_idx, moe_route_quant_t quant,
+                       void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
+                       int32_t* expert_cumsum, int32_t* sorted_expert_idx,
+                       int32_t* sorted_row_idx, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * The whole layer ("Cake SiTU backend": intro for the stages; section "Prepared weights
+ * and scales" for the scales and SiTU; "Caller-owned execution" for the contract).
+ *   x              BF16 [T, H]            (device)
+ *   expert_ids     i32  [T, k]  in [0,E)  (device)
+ *   route_weights  BF16 [T, k]            (device; used as given, not renormalized)
+ *   prepared       moe_prepare_weights output (device)
+ *   qx             f32 [1]  activation encoding scale qX = 1/dX          (device)
+ *   alpha1         f32 [E]  FC1 dequantization dX*dW13[e]                (device)
+ *   qa             f32 [E]  intermediate encoding scale qA[e] = 1/dA[e]  (device)
+ *   alpha2         f32 [E]  FC2 dequantization dA[e]*dW2[e]              (device)
+ *   situ_beta      f32 [E] or NULL (then 4)   gate smoothing beta        (device)
+ *   situ_linear_beta f32 [E] or NULL (then 25) linear smoothing lambda   (device)
+ *   workspace      >= moe_workspace_size(d, T) bytes, 256-byte aligned   (device)
+ *   out            BF16 [T, H]                                            (device)
+ * SiTU(g, u) = (beta*tanh(g/beta)*sigmoid(g)) * (lambda*tanh(u/lambda)) with g the FC1
+ * gate row and u the matching up row.  out[t] = BF16(sum_j w[t,j] * O[t,j]) with O the
+ * FC2 output of (t, j) and the sum in j order in fp32.  1 <= T <= MOE_MAX_TOKENS.
+ * ------------------------------------------------------------------------------------ */
+moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
+                         const uint16_t* route_weights, const void* prepared, const float* qx,
+                         const float* alpha1, const float* qa, const float* alpha2,
+                         const float* situ_beta, const float* situ_linear_beta,
+                         void* workspace, size_t workspace_bytes, uint16_t* out,
+                         moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTED_MOE_H */

@@ -44,6 +44,11 @@ class LayerConfig:
     outlier_mult: float = 1.0
     per_expert_situ: bool = False
     seed_index: int = 0
+    weight_seed_index: int = -1     # -1: same as seed_index
+
+    @property
+    def wseed(self):
+        return self.seed_index if self.weight_seed_index < 0 else self.weight_seed_index
 
 
 @dataclass(frozen=True)
@@ -68,11 +73,13 @@ ROUTE_8K = RouteConfig("route_N8192_H7168_E256_K8_zipf1.1_int8", N=8192, H=7168,
                        zipf_s=1.1, outlier_frac=0.01, outlier_mult=20.0, seed_index=1)
 DECODE_16 = LayerConfig("layer_T16_H3584_I384_E896_k16_uniform", T=16, H=3584, I=384, E=896,
                         k=16, w_std=0.02, seed_index=2)
+# The mid and prefill batches use the decode workload's expert weights.
 MID_1024 = LayerConfig("layer_T1024_H3584_I384_E896_k16_zipf1.0", T=1024, H=3584, I=384,
-                       E=896, k=16, zipf_s=1.0, w_std=0.02, seed_index=3)
+                       E=896, k=16, zipf_s=1.0, w_std=0.02, seed_index=3, weight_seed_index=2)
 PREFILL_16K = LayerConfig("layer_T16384_H3584_I384_E896_k16_uniform_situE", T=16384, H=3584,
                           I=384, E=896, k=16, w_std=0.02, outlier_frac=0.005,
-                          outlier_mult=30.0, per_expert_situ=True, seed_index=4)
+                          outlier_mult=30.0, per_expert_situ=True, seed_index=4,
+                          weight_seed_index=2)
 
 LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE_16, MID_1024, PREFILL_16K)}
 
@@ -125,9 +132,9 @@ def draw_route_weights(n, k, seed_index):
 
 def draw_expert_weights(cfg: LayerConfig, e):
     """BF16 bits of expert e: W13 [2I, H] (gate rows, then up rows) and W2 [H, I]."""
-    w13 = _rng(cfg.seed_index, _TAG_W13, e).standard_normal((2 * cfg.I, cfg.H), dtype=np.float32)
+    w13 = _rng(cfg.wseed, _TAG_W13, e).standard_normal((2 * cfg.I, cfg.H), dtype=np.float32)
     w13 *= np.float32(cfg.w_std)
-    w2 = _rng(cfg.seed_index, _TAG_W2, e).standard_normal((cfg.H, cfg.I), dtype=np.float32)
+    w2 = _rng(cfg.wseed, _TAG_W2, e).standard_normal((cfg.H, cfg.I), dtype=np.float32)
     w2 *= np.float32(cfg.w_std)
     return f32_to_bf16_bits(w13), f32_to_bf16_bits(w2)
 

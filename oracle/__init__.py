@@ -25,7 +25,8 @@ through closed forms and limits (see ``oracle.layer.situ``).
 from .codecs import (E2M1_MAGNITUDES, e2m1_decode, e2m1_encode, e4m3_decode, e4m3_encode,
                      bf16_bits_to_f32, f64_to_bf16_bits)
 from .nvfp4 import quantize_nvfp4, dequantize_nvfp4, pack_nibbles, unpack_nibbles
-from .calib import global_scale_from_amax, calibrate_layer, quantize_expert_stack
+from .calib import (global_scale_from_amax, calibrate_layer, calibrate_tokens,
+                    calibrate_weights, quantize_expert_stack)
 from .routing import route, route_int8
 from .layer import (situ, fc_exact, layer_forward, layer_forward_dense, token_forward,
                     calibrate_intermediate, intermediate_amax,
@@ -35,7 +36,8 @@ __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode", "e4m3_encode",
     "bf16_bits_to_f32", "f64_to_bf16_bits",
     "quantize_nvfp4", "dequantize_nvfp4", "pack_nibbles", "unpack_nibbles",
-    "global_scale_from_amax", "calibrate_layer", "quantize_expert_stack",
+    "global_scale_from_amax", "calibrate_layer", "calibrate_tokens", "calibrate_weights",
+    "quantize_expert_stack",
     "calibrate_intermediate", "intermediate_amax",
     "route", "route_int8",
     "situ", "fc_exact", "layer_forward", "layer_forward_dense", "token_forward",

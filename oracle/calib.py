@@ -28,6 +28,18 @@ def global_scale_from_amax(amax):
     return d, q
 
 
+def calibrate_tokens(x_bits):
+    """(dX, qX) float32 of BF16 token bits: one tensor-global scale."""
+    return global_scale_from_amax(np.max(np.abs(bf16_bits_to_f32(x_bits))))
+
+
+def calibrate_weights(w_bits):
+    """(dW [E], qW [E]) float32 of stacked BF16 expert weights [E, N, K]: per-expert amax."""
+    a = np.array([np.max(np.abs(bf16_bits_to_f32(w_bits[e]))) for e in range(w_bits.shape[0])],
+                 np.float32)
+    return global_scale_from_amax(a)
+
+
 def calibrate_layer(x_bits, w13_bits, w2_bits):
     """Scales of the inputs that are known before the layer runs.
 
@@ -36,12 +48,9 @@ def calibrate_layer(x_bits, w13_bits, w2_bits):
     Returns a dict of float32 arrays: dX, qX (scalars), dW13, qW13, dW2, qW2 ([E]).
     """
     out = {}
-    out["dX"], out["qX"] = global_scale_from_amax(np.max(np.abs(bf16_bits_to_f32(x_bits))))
-    E = w13_bits.shape[0]
-    a13 = np.array([np.max(np.abs(bf16_bits_to_f32(w13_bits[e]))) for e in range(E)], np.float32)
-    a2 = np.array([np.max(np.abs(bf16_bits_to_f32(w2_bits[e]))) for e in range(E)], np.float32)
-    out["dW13"], out["qW13"] = global_scale_from_amax(a13)
-    out["dW2"], out["qW2"] = global_scale_from_amax(a2)
+    out["dX"], out["qX"] = calibrate_tokens(x_bits)
+    out["dW13"], out["qW13"] = calibrate_weights(w13_bits)
+    out["dW2"], out["qW2"] = calibrate_weights(w2_bits)
     return out
 
 

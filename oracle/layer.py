@@ -212,32 +212,35 @@ def layer_forward_dense(x_bits, expert_ids, rw_bits, w13, w13_sf, w2, w2_sf,
                          qX, alpha1, qA, alpha2, beta, lam)
 
 
-def intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, qX, alpha1, beta=None, lam=None,
-                      I=None):
+def intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
+                      beta=None, lam=None, weight_cache=None):
     """Largest |SiTU output| over the routed rows of the given tokens (calibration pass)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     E = w13.shape[0]
-    I = w13.shape[1] // 2 if I is None else I
+    I = w2.shape[2] * 2
     beta_a, lam_a = _situ_params(E, beta, lam)
+    cache = {} if weight_cache is None else weight_cache
     xc, xs = quantize_nvfp4(bf16_bits_to_f32(np.asarray(x_bits, np.uint16)[tokens]), np.float32(qX))
     xdec = dequantize_nvfp4(xc, xs)
     amax = np.float32(0.0)
     ids = np.asarray(expert_ids)[tokens]
     for e in np.unique(ids):
         rows = np.nonzero(np.any(ids == e, axis=1))[0]
-        w13d = dequantize_nvfp4(unpack_nibbles(w13[e]), w13_sf[e])
-        h = (fc_exact(xdec[rows], w13d) * np.float32(alpha1[e])).astype(np.float32)
+        if e not in cache:
+            cache[e] = expert_weights_decoded(w13, w13_sf, w2, w2_sf, e)
+        h = (fc_exact(xdec[rows], cache[e][0]) * np.float32(alpha1[e])).astype(np.float32)
         a = situ(h[:, :I], h[:, I:], beta_a[e], lam_a[e])
         amax = max(amax, np.float32(np.max(np.abs(a))))
     return np.float32(amax)
 
 
-def calibrate_intermediate(tokens, x_bits, expert_ids, w13, w13_sf, qX, alpha1, beta=None,
-                           lam=None):
+def calibrate_intermediate(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
+                           beta=None, lam=None, weight_cache=None):
     """Reading R18: one shared dA = amax|SiTU output| / 2688 over a calibration set of
     tokens, expanded to [E] (the page asks for a shared intermediate scale expanded to an
     [E] tensor during model preparation).  Returns (dA [E], qA [E]) float32."""
     E = w13.shape[0]
-    amax = intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, qX, alpha1, beta, lam)
+    amax = intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
+                             beta, lam, weight_cache)
     d, q = global_scale_from_amax(amax)
     return np.full(E, d, np.float32), np.full(E, q, np.float32)

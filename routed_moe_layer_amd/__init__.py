@@ -1,0 +1,177 @@
+"""Python binding of the routed-MoE HIP library (include/routed_moe.h).
+
+Argument marshalling only: each function has the C entry point's name, takes torch
+tensors (or raw integer device addresses) for the device buffers, passes their addresses
+and the current HIP stream to the library and raises ``MoeError`` on a non-zero status.
+Every step of the layer runs in the library's HIP kernels; there is no other
+implementation behind these names.  If the shared library has not been built, every call
+raises -- nothing falls back to another path.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "MoeError", "MoeDims", "library_path", "moe_status_string", "moe_workspace_size",
+    "moe_prepared_weights_size", "moe_workspace_layout", "moe_route_workspace_size",
+    "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_forward",
+    "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "lib", "libroutedmoe.so")
+
+MOE_ROUTE_QUANT_NONE = 0
+MOE_ROUTE_QUANT_INT8_DYNAMIC = 1
+MOE_MAX_TOKENS = 16384
+
+# Every symbol include/routed_moe.h declares.
+EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_size",
+            "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
+            "moe_prepare_weights", "moe_route", "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_status_text(status)} ({status})")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+    def __init__(self, hidden, inter, num_experts, top_k):
+        super().__init__(hidden, inter, num_experts, top_k)
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "x_codes", "x_scales", "sorted_ids", "sorted_row_idx", "expanded_row_idx",
+        "expert_counts", "expert_cumsum", "a_codes", "a_scales", "o_rows", "a_amax", "total")]
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"routed-MoE HIP library not built ({library_path} missing); run "
+                "`python -m routed_moe_layer_amd.build` (or __graft_entry__.build())")
+        lib = ctypes.CDLL(library_path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        st = ctypes.c_int
+        sig = {
+            "moe_status_string": (ctypes.c_char_p, [st]),
+            "moe_workspace_size": (st, [MoeDims, I32, ctypes.POINTER(SZ)]),
+            "moe_prepared_weights_size": (st, [MoeDims, ctypes.POINTER(SZ)]),
+            "moe_workspace_layout": (st, [MoeDims, I32, ctypes.POINTER(_Layout)]),
+            "moe_route_workspace_size": (st, [I32, I32, I32, ctypes.POINTER(SZ)]),
+            "moe_quantize_nvfp4": (st, [P, I64, I64, I32, P, P, P, P]),
+            "moe_prepare_weights": (st, [MoeDims, P, P, P, P, P, SZ, P]),
+            "moe_route": (st, [I32, I32, I32, I32, P, P, ctypes.c_int, P, P, P, P, P, P, P, SZ, P]),
+            "moe_forward": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _status_text(status):
+    try:
+        return _lib().moe_status_string(status).decode()
+    except Exception:  # the library itself failed to load
+        return "status"
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address; None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def moe_status_string(status):
+    return _lib().moe_status_string(status).decode()
+
+
+def moe_workspace_size(dims, max_tokens):
+    n = ctypes.c_size_t()
+    _check("moe_workspace_size", _lib().moe_workspace_size(dims, max_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def moe_prepared_weights_size(dims):
+    n = ctypes.c_size_t()
+    _check("moe_prepared_weights_size", _lib().moe_prepared_weights_size(dims, ctypes.byref(n)))
+    return n.value
+
+
+def moe_workspace_layout(dims, T):
+    lay = _Layout()
+    _check("moe_workspace_layout", _lib().moe_workspace_layout(dims, T, ctypes.byref(lay)))
+    return {name: getattr(lay, name) for name, _ in _Layout._fields_}
+
+
+def moe_route_workspace_size(num_rows, top_k, num_experts):
+    n = ctypes.c_size_t()
+    _check("moe_route_workspace_size",
+           _lib().moe_route_workspace_size(num_rows, top_k, num_experts, ctypes.byref(n)))
+    return n.value
+
+
+def moe_quantize_nvfp4(src, groups, rows_per_group, K, q, codes, scales, stream=None):
+    _check("moe_quantize_nvfp4", _lib().moe_quantize_nvfp4(
+        _ptr(src), groups, rows_per_group, K, _ptr(q), _ptr(codes), _ptr(scales),
+        _stream(stream)))
+
+
+def moe_prepare_weights(dims, w13, w13_sf, w2, w2_sf, prepared, prepared_bytes=None, stream=None):
+    nb = _nbytes(prepared) if prepared_bytes is None else prepared_bytes
+    _check("moe_prepare_weights", _lib().moe_prepare_weights(
+        dims, _ptr(w13), _ptr(w13_sf), _ptr(w2), _ptr(w2_sf), _ptr(prepared), nb,
+        _stream(stream)))
+
+
+def moe_route(num_rows, hidden, num_experts, top_k, x, expert_idx, quant, expanded_x,
+              expanded_scale, expanded_row_idx, expert_cumsum, sorted_expert_idx,
+              sorted_row_idx, workspace, workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_route", _lib().moe_route(
+        num_rows, hidden, num_experts, top_k, _ptr(x), _ptr(expert_idx), quant, _ptr(expanded_x),
+        _ptr(expanded_scale), _ptr(expanded_row_idx), _ptr(expert_cumsum),
+        _ptr(sorted_expert_idx), _ptr(sorted_row_idx), _ptr(workspace), nb, _stream(stream)))
+
+
+def moe_forward(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
+                situ_beta, situ_linear_beta, workspace, out, workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_forward", _lib().moe_forward(
+        dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
+        _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
+        _ptr(workspace), nb, _ptr(out), _stream(stream)))

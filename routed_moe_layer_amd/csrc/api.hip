@@ -1,0 +1,261 @@
+// C ABI of the routed-MoE library: argument validation, workspace carving and launches.
+// Declarations and the contract of every entry point are in include/routed_moe.h.
+#include "routed_moe.h"
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace rmoe;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status_t check_dims(const moe_dims_t& d) {
+  if (d.hidden <= 0 || d.inter <= 0 || d.num_experts <= 0 || d.top_k <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (d.hidden % 128 || d.inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (d.hidden < 128 || d.hidden > 16384 || d.inter < 64 || d.inter > 4096)
+    return MOE_ERR_UNSUPPORTED;
+  if (d.num_experts > 4096 || d.top_k > 64) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int padded_inter(int I) { return (I + kChunk - 1) / kChunk * kChunk; }
+
+struct Layout {
+  moe_workspace_layout_t pub;
+  size_t offsets, tile_hist, tiles, num_tiles;
+};
+
+Layout make_layout(const moe_dims_t& d, int64_t T) {
+  const int64_t H = d.hidden, I = d.inter, E = d.num_experts, R = T * d.top_k;
+  Carver c;
+  Layout L{};
+  L.pub.x_codes = c.take(T * H / 2);
+  L.pub.x_scales = c.take(T * H / 16);
+  L.pub.sorted_ids = c.take(R * 4);
+  L.pub.sorted_row_idx = c.take(R * 4);
+  L.pub.expanded_row_idx = c.take(R * 4);
+  L.pub.expert_counts = c.take(E * 4);
+  L.offsets = c.take((E + 1) * 4);
+  L.pub.expert_cumsum = c.take(E * 4);
+  L.tile_hist = c.take(static_cast<size_t>(route_tiles(R)) * E * 4);
+  L.tiles = c.take(static_cast<size_t>(max_token_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
+  L.num_tiles = c.take(4);
+  L.pub.a_codes = c.take(R * I / 2);
+  L.pub.a_scales = c.take(R * I / 16);
+  L.pub.o_rows = c.take(R * H * 2);
+  L.pub.a_amax = c.take(E * 4);
+  L.pub.total = c.off;
+  return L;
+}
+
+size_t prepared_bytes(const moe_dims_t& d) {
+  const int H = d.hidden, I = d.inter, Ip = padded_inter(I);
+  return static_cast<size_t>(d.num_experts) *
+         (prepared_codes_bytes(2 * I, H) + prepared_scales_bytes(2 * I, H) +
+          prepared_codes_bytes(H, Ip) + prepared_scales_bytes(H, Ip));
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (max_tokens < 1 || max_tokens > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  *bytes = make_layout(d, max_tokens).pub.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  *bytes = prepared_bytes(d);
+  return MOE_OK;
+}
+
+moe_status_t moe_workspace_layout(moe_dims_t d, int32_t T, moe_workspace_layout_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  *out = make_layout(d, T).pub;
+  return MOE_OK;
+}
+
+moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t num_experts,
+                                      size_t* bytes) {
+  if (!bytes || num_rows < 1 || top_k < 1 || num_experts < 1) return MOE_ERR_INVALID_ARG;
+  if (top_k > 64 || num_experts > 4096) return MOE_ERR_UNSUPPORTED;
+  const int64_t n = static_cast<int64_t>(num_rows) * top_k;
+  if (n > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
+  Carver c;
+  c.take(static_cast<size_t>(route_tiles(n)) * num_experts * 4);   // tile histograms
+  c.take(static_cast<size_t>(num_experts) * 4);                     // counts
+  c.take(static_cast<size_t>(num_experts + 1) * 4);                 // offsets
+  *bytes = c.off;
+  return MOE_OK;
+}
+
+moe_status_t moe_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
+                                int32_t K, const float* q, uint8_t* codes, uint8_t* scales,
+                                moe_stream_t stream) {
+  if (!src || !q || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (groups < 1 || rows_per_group < 1 || K < 16 || K % 16 || K > 65536)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(codes, 8) || !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_nvfp4(src, groups, rows_per_group, K, q, codes, scales,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_prepare_weights(moe_dims_t d, const uint8_t* w13, const uint8_t* w13_sf,
+                                 const uint8_t* w2, const uint8_t* w2_sf, void* prepared,
+                                 size_t prepared_size, moe_stream_t stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!w13 || !w13_sf || !w2 || !w2_sf || !prepared) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w13, 4) || !aligned(w2, 4) || !aligned(prepared, kAlign))
+    return MOE_ERR_INVALID_ARG;
+  if (prepared_size < prepared_bytes(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_prepare_weights(d.hidden, d.inter, d.num_experts, w13, w13_sf, w2,
+                                           w2_sf, static_cast<uint8_t*>(prepared),
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
+                       const uint16_t* x, const int32_t* expert_idx, moe_route_quant_t quant,
+                       void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
+                       int32_t* expert_cumsum, int32_t* sorted_expert_idx,
+                       int32_t* sorted_row_idx, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream) {
+  size_t need = 0;
+  moe_status_t st = moe_route_workspace_size(num_rows, top_k, num_experts, &need);
+  if (st != MOE_OK) return st;
+  if (hidden < 8 || hidden % 8 || hidden > 65536) return MOE_ERR_UNSUPPORTED;
+  if (quant != MOE_ROUTE_QUANT_NONE && quant != MOE_ROUTE_QUANT_INT8_DYNAMIC)
+    return MOE_ERR_INVALID_ARG;
+  if (!x || !expert_idx || !expanded_x || !expanded_row_idx || !expert_cumsum || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (quant == MOE_ROUTE_QUANT_INT8_DYNAMIC && !expanded_scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(expanded_x, 16) || !aligned(workspace, kAlign))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t n = static_cast<int64_t>(num_rows) * top_k;
+  Carver c;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  RouteBuffers b{};
+  b.tile_hist = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(route_tiles(n)) * num_experts * 4));
+  b.counts = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts) * 4));
+  b.offsets = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts + 1) * 4));
+  b.cumsum = expert_cumsum;
+  b.sorted_ids = sorted_expert_idx;
+  b.sorted_row_idx = sorted_row_idx;
+  b.expanded_row_idx = expanded_row_idx;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_route(expert_idx, n, num_experts, b, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_route_permute(x, num_rows, hidden, top_k, static_cast<int>(quant), expanded_row_idx,
+                           expanded_x, expanded_scale, s);
+  return hip_status(e);
+}
+
+moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
+                         const uint16_t* route_weights, const void* prepared, const float* qx,
+                         const float* alpha1, const float* qa, const float* alpha2,
+                         const float* situ_beta, const float* situ_linear_beta,
+                         void* workspace, size_t workspace_bytes, uint16_t* out,
+                         moe_stream_t stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  if (!x || !expert_ids || !route_weights || !prepared || !qx || !alpha1 || !qa || !alpha2 ||
+      !workspace || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(prepared, kAlign) ||
+      !aligned(workspace, kAlign) || !aligned(expert_ids, 4) || !aligned(route_weights, 2))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(d, T);
+  if (workspace_bytes < L.pub.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = d.hidden, I = d.inter, E = d.num_experts, k = d.top_k;
+  const int64_t R = static_cast<int64_t>(T) * k;
+
+  LayerArgs a{};
+  a.H = H; a.I = I; a.Ip = padded_inter(I); a.E = E; a.k = k; a.T = T;
+  a.x_codes = ws + L.pub.x_codes;
+  a.x_scales = ws + L.pub.x_scales;
+  int32_t* sorted_ids = reinterpret_cast<int32_t*>(ws + L.pub.sorted_ids);
+  int32_t* sorted_row_idx = reinterpret_cast<int32_t*>(ws + L.pub.sorted_row_idx);
+  int32_t* expanded_row_idx = reinterpret_cast<int32_t*>(ws + L.pub.expanded_row_idx);
+  a.sorted_row_idx = sorted_row_idx;
+  a.expanded_row_idx = expanded_row_idx;
+  a.tiles = reinterpret_cast<TileDesc*>(ws + L.tiles);
+  a.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  a.max_tiles = max_token_tiles(R, E);
+  const uint8_t* p = static_cast<const uint8_t*>(prepared);
+  a.w13_codes = p;
+  a.w13_scales = a.w13_codes + static_cast<size_t>(E) * prepared_codes_bytes(2 * I, H);
+  a.w2_codes = a.w13_scales + static_cast<size_t>(E) * prepared_scales_bytes(2 * I, H);
+  a.w2_scales = a.w2_codes + static_cast<size_t>(E) * prepared_codes_bytes(H, a.Ip);
+  a.alpha1 = alpha1; a.qa = qa; a.alpha2 = alpha2;
+  a.beta = situ_beta; a.lam = situ_linear_beta;
+  a.a_codes = ws + L.pub.a_codes;
+  a.a_scales = ws + L.pub.a_scales;
+  a.a_amax = reinterpret_cast<float*>(ws + L.pub.a_amax);
+  a.o_rows = reinterpret_cast<uint16_t*>(ws + L.pub.o_rows);
+  a.route_weights = route_weights;
+  a.out = out;
+
+  hipError_t e = launch_quantize_nvfp4(x, 1, T, H, qx, ws + L.pub.x_codes, ws + L.pub.x_scales, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  RouteBuffers b{};
+  b.tile_hist = reinterpret_cast<int32_t*>(ws + L.tile_hist);
+  b.counts = reinterpret_cast<int32_t*>(ws + L.pub.expert_counts);
+  b.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  b.cumsum = reinterpret_cast<int32_t*>(ws + L.pub.expert_cumsum);
+  b.sorted_ids = sorted_ids;
+  b.sorted_row_idx = sorted_row_idx;
+  b.expanded_row_idx = expanded_row_idx;
+  b.tiles = reinterpret_cast<TileDesc*>(ws + L.tiles);
+  b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  b.amax_reset = a.a_amax;
+  if ((e = launch_route(expert_ids, R, E, b, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_fc1(a, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_fc2(a, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = launch_finalize(a, s)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

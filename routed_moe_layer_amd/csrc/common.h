@@ -1,0 +1,133 @@
+// Device helpers shared by the routed-MoE kernels (gfx950 / CDNA4, wave64).
+//
+// Number formats ("Cake SiTU backend", section "Prepared weights and scales"; "Nvfp4
+// Tensor", struct NVFP4Tensor): NVFP4 = E2M1 codes (sign bit 3, magnitudes
+// {0,.5,1,1.5,2,3,4,6}) in groups of 16 sharing one float8_e4m3fn scale (bias 7, max 448,
+// no Inf), with an fp32 global scale applied after block dequantization.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmoe {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 16;          // NVFP4 block length
+constexpr int kChunk = 128;         // K elements per prepared-weight chunk (4 MFMA K-steps)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> BF16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// E4M3 byte of a non-negative finite fp32 scale: clamp to 448, then round to nearest even.
+// Subnormal range (< 2^-6): multiples of 2^-9.  Normal range: 3 mantissa bits.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float s) {
+  s = fminf(s, 448.0f);
+  if (s < 0.015625f) {                              // 2^-6, smallest normal E4M3
+    return static_cast<uint32_t>(rintf(s * 512.0f));  // exact scaling; rintf is half-even
+  }
+  uint32_t u = __float_as_uint(s);
+  int32_t e = static_cast<int32_t>(u >> 23) - 127;  // -6 .. 8
+  uint32_t m = u & 0x7FFFFFu;
+  uint32_t r = m >> 20;                             // top 3 mantissa bits
+  uint32_t rem = m & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) { r = 0u; ++e; }
+  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | r;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// fp32 value of an E4M3 byte (the byte's sign is ignored: block scales are >= 0).
+// gfx950's fp8 conversion is the OCP E4M3 ("fn") format.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(byte & 0x7Fu), false);
+  return v[0];
+}
+
+// E2M1 code of an fp32 value: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
+// saturating at 6; bit 3 carries the sign of y (so -0 and small negatives give 0x8).
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  float a = fabsf(y);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Group-16 NVFP4 quantization of one block with global encoding scale q:
+// s = E4M3(min(fp32(fp32(amax*q)/6), 448)); enc = q/s (0 if s == 0);
+// code_i = E2M1(fp32(v_i*enc)).  Returns the scale byte; codes packed two per byte,
+// element 2b in the low nibble of byte b (codes_lo: elements 0..7, codes_hi: 8..15).
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float q, float* enc_out) {
+  float s32 = (amax * q) / 6.0f;
+  uint32_t sb = e4m3_encode_nonneg(s32);
+  float s = e4m3_to_f32(sb);
+  *enc_out = (s == 0.0f) ? 0.0f : q / s;
+  return sb;
+}
+
+__device__ __forceinline__ uint32_t pack8_codes(const float* v, float enc) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_encode(v[i] * enc) << (4 * i);
+  return w;
+}
+
+// Decode 8 NVFP4 codes (one 32-bit word, element i in nibble i) times the block scale
+// into the f16x8 operand of a 16x16x32 f16 MFMA.  The conversion instruction applies only
+// a power-of-two scale, so it runs with scale 1 (exact E2M1 values) and the E4M3 scale
+// (at most 4 significant bits, range 2^-9..448) multiplies in f16: every product has at
+// most 6 significant bits and lies in [2^-10, 2688], so it is exact in f16.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 scale2) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  a *= scale2; b *= scale2; c *= scale2; d *= scale2;
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ f16x2 scale_f16x2(uint32_t e4m3_byte) {
+  _Float16 h = static_cast<_Float16>(e4m3_to_f32(e4m3_byte));   // exact: E4M3 fits f16
+  f16x2 r; r[0] = h; r[1] = h;
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Lane-mask of lanes whose value of `key` equals this lane's (keys < 2^nbits), among
+// `active` lanes, via one ballot per key bit.
+__device__ __forceinline__ uint64_t match_key(uint32_t key, int nbits, uint64_t active) {
+  uint64_t peers = active;
+  for (int b = 0; b < nbits; ++b) {
+    uint32_t bit = (key >> b) & 1u;
+    uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  uint32_t lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace rmoe

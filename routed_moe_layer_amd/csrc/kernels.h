@@ -1,0 +1,111 @@
+// Internal launcher declarations shared by the C-ABI host code and the kernel files.
+// Every launcher enqueues on `stream` and returns the hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rmoe {
+
+// One entry of the grouped-GEMM work list: `nrows` consecutive expert-sorted rows starting
+// at `row_start`, all routed to expert `expert`.
+struct TileDesc {
+  int32_t expert;
+  int32_t row_start;
+  int32_t nrows;
+  int32_t pad;
+};
+
+// Router geometry: flat ids are processed in tiles of kRouteTile by workgroups of 256.
+constexpr int kRouteTile = 1024;
+constexpr int kRouteThreads = 256;
+// Tokens per grouped-GEMM tile (the N side of both FC kernels).
+constexpr int kTokTile = 64;
+// Weight rows per grouped-GEMM workgroup (the M side): 4 waves x 32 rows.
+constexpr int kWRows = 128;
+
+inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
+inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
+// Upper bound of the number of kTokTile tiles over all experts for R routed rows.
+inline int64_t max_token_tiles(int64_t R, int E) {
+  return R / kTokTile + (R < E ? R : E);
+}
+
+hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
+                                 int K, const float* q, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
+
+// Routing: histogram, scan (+ optional GEMM tile list and stats reset), stable scatter.
+struct RouteBuffers {
+  int32_t* tile_hist;        // [route_tiles(n), E]
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E + 1] exclusive
+  int32_t* cumsum;           // [E] inclusive (may be null)
+  int32_t* sorted_ids;       // [n] (may be null)
+  int32_t* sorted_row_idx;   // [n] (may be null)
+  int32_t* expanded_row_idx; // [n]
+  TileDesc* tiles;           // [max_token_tiles] or null
+  int32_t* num_tiles;        // [1] or null
+  float* amax_reset;         // [E] zeroed by the scan kernel, or null
+};
+hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
+                        hipStream_t stream);
+
+hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
+                                const int32_t* expanded_row_idx, void* expanded_x,
+                                float* expanded_scale, hipStream_t stream);
+
+hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
+                                  const uint8_t* w13_sf, const uint8_t* w2,
+                                  const uint8_t* w2_sf, uint8_t* prepared, hipStream_t stream);
+
+struct LayerArgs {
+  int H, I, Ip, E, k, T;
+  const uint8_t* x_codes;      // [T, H/2]
+  const uint8_t* x_scales;     // [T, H/16]
+  const int32_t* sorted_row_idx;
+  const int32_t* expanded_row_idx;
+  const TileDesc* tiles;
+  const int32_t* num_tiles;
+  int64_t max_tiles;
+  const uint8_t* w13_codes;    // prepared
+  const uint8_t* w13_scales;
+  const uint8_t* w2_codes;
+  const uint8_t* w2_scales;
+  const float* alpha1;
+  const float* qa;
+  const float* alpha2;
+  const float* beta;           // may be null
+  const float* lam;            // may be null
+  uint8_t* a_codes;            // [T*k, I/2]
+  uint8_t* a_scales;           // [T*k, I/16]
+  float* a_amax;               // [E]
+  uint16_t* o_rows;            // [T*k, H] bf16
+  const uint16_t* route_weights;
+  uint16_t* out;               // [T, H]
+};
+hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream);
+
+// Prepared-weight layout (private).  For a matrix of R rows (multiple of 16) and K columns
+// padded to Kp (multiple of 128): codes [R/16][Kp/128][64 lanes][16 B] and scales
+// [R/16][Kp/128][2][16][4 B].  Lane l of row group G, chunk c holds row 16G + l%16,
+// and its dword s (s = 0..3) holds the 8 codes k = 128c + 32s + 8(l/16) + [0..7]
+// (the f16 16x16x32 MFMA operand for K-step s).  Those 8 codes lie in block
+// 8c + 2s + (l/16)/2, so lanes l and l+16 share a block: the scale dword of lane l is
+// dword (l/32)*16 + l%16 of the chunk, byte s of it being the scale of K-step s.  Both
+// parts are exactly as large as the canonical codes and scales.
+// FC1 rows are reordered so that row 2j of group G is gate row 8G+j and row 2j+1 is up
+// row 8G+j: each lane then holds g and u of the same intermediate channels.
+inline size_t prepared_codes_bytes(int R, int Kp) { return static_cast<size_t>(R) * Kp / 2; }
+inline size_t prepared_scales_bytes(int R, int Kp) { return static_cast<size_t>(R) * Kp / 16; }
+// Index of lane `lane`'s scale dword for (row group G, chunk c) of matrix slot `slot`
+// (= expert * R/16 + G), in uint32 units.
+__host__ __device__ inline int64_t prepared_scale_index(int64_t slot, int nchunks, int c,
+                                                         int lane) {
+  return (slot * nchunks + c) * 32 + (lane >> 5) * 16 + (lane & 15);
+}
+
+}  // namespace rmoe

@@ -1,0 +1,136 @@
+// Token quantization kernels.
+//
+//  * quantize_nvfp4_kernel: group-16 NVFP4 quantization of BF16 rows ("Cake SiTU
+//    backend", intro: group-16 NVFP4 input quantization with the fp32 scale qX).  One
+//    thread per 16-value block: a 32-byte load, 8 bytes of codes and 1 scale byte out.
+//    HBM-bound (34 bytes per 16 values moved).
+//  * route_permute_kernel: the token movement of "torch_npu.npu_moe_init_routing_v2"
+//    (section 计算公式, steps 4-5): per-row dynamic int8 quantization (or a BF16 copy),
+//    each token row written to its K expert-sorted positions through the gather map.
+//    One workgroup per token row: the row is read once and written K times.
+#include "common.h"
+#include "kernels.h"
+
+namespace rmoe {
+
+__global__ __launch_bounds__(256) void quantize_nvfp4_kernel(
+    const uint16_t* __restrict__ src, int64_t nblocks, int blocks_per_row,
+    int64_t rows_per_group, const float* __restrict__ q, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  int64_t row = b / blocks_per_row;
+  float qv = q[row / rows_per_group];
+  const uint4* p = reinterpret_cast<const uint4*>(src + b * kGroup);
+  uint4 lo = p[0], hi = p[1];
+  uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(wv[i] << 16);
+    v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  float enc;
+  uint32_t sb = nvfp4_block_scale(amax, qv, &enc);
+  uint2 out;
+  out.x = pack8_codes(v, enc);
+  out.y = pack8_codes(v + 8, enc);
+  reinterpret_cast<uint2*>(codes)[b] = out;
+  scales[b] = static_cast<uint8_t>(sb);
+}
+
+hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
+                                 int K, const float* q, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  int64_t nblocks = groups * rows_per_group * (K / kGroup);
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  quantize_nvfp4_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream>>>(
+      src, nblocks, K / kGroup, rows_per_group, q, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Token movement for the routing primitive.  quant == 1: dynamic int8 per row,
+//   scale = fp32(row_max|x| / 127); q = clip(rint(fp32(x / scale)), -127, 127).
+// quant == 0: BF16 copy.  Rows are written to expanded_row_idx[t*K + j], j < K.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < static_cast<int>(blockDim.x / kWave); ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+__global__ __launch_bounds__(256) void route_permute_kernel(
+    const uint16_t* __restrict__ x, int H, int K, int quant,
+    const int32_t* __restrict__ expanded_row_idx, void* __restrict__ expanded_x,
+    float* __restrict__ expanded_scale) {
+  __shared__ float red[4];
+  __shared__ int32_t dst[64];
+  const int64_t t = blockIdx.x;
+  const uint16_t* xr = x + t * H;
+  const int nvec = H / 8;                   // 16-byte vectors of 8 BF16
+  if (threadIdx.x < K) dst[threadIdx.x] = expanded_row_idx[t * K + threadIdx.x];
+  if (quant == 0) {
+    __syncthreads();
+    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+      uint4 d = reinterpret_cast<const uint4*>(xr)[v];
+      for (int j = 0; j < K; ++j) {
+        if (dst[j] < 0) continue;
+        uint16_t* o = static_cast<uint16_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
+        reinterpret_cast<uint4*>(o)[v] = d;
+      }
+    }
+    return;
+  }
+  float amax = 0.0f;
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    uint4 d = reinterpret_cast<const uint4*>(xr)[v];
+    uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    }
+  }
+  amax = block_max(amax, red);            // includes the __syncthreads for dst[]
+  const float scale = amax / 127.0f;
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    uint4 d = reinterpret_cast<const uint4*>(xr)[v];
+    uint32_t w[4] = {d.x, d.y, d.z, d.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
+      float xv = __uint_as_float(bits);
+      float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
+      qf = fminf(fmaxf(qf, -127.0f), 127.0f);
+      uint32_t qb = static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu;
+      packed[i >> 2] |= qb << (8 * (i & 3));
+    }
+    uint2 pv = make_uint2(packed[0], packed[1]);
+    for (int j = 0; j < K; ++j) {
+      if (dst[j] < 0) continue;
+      int8_t* o = static_cast<int8_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
+      reinterpret_cast<uint2*>(o)[v] = pv;
+    }
+  }
+  if (threadIdx.x < K && dst[threadIdx.x] >= 0) expanded_scale[dst[threadIdx.x]] = scale;
+}
+
+hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
+                                const int32_t* expanded_row_idx, void* expanded_x,
+                                float* expanded_scale, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  route_permute_kernel<<<dim3(static_cast<unsigned>(N)), dim3(256), 0, stream>>>(
+      x, H, K, quant, expanded_row_idx, expanded_x, expanded_scale);
+  return hipGetLastError();
+}
+
+}  // namespace rmoe

@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and its
+host-only entry points (sizes, layout, argument validation) behave as documented.
+Validation failures return before any HIP call, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_moe_layer_amd as rm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "routed_moe.h")
+FULL = rm.MoeDims(3584, 384, 896, 16)
+TINY = rm.MoeDims(256, 64, 16, 4)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z0-9_]+)\(", text, re.M)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(rm.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rm.library_path)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert rm.moe_status_string(0) == "ok"
+    assert rm.moe_status_string(-3) == "workspace too small"
+
+
+def test_workspace_size_is_monotone_and_covers_the_layout():
+    prev = 0
+    for T in (1, 2, 15, 16, 17, 64, 255, 1024, 4097, 16384):
+        n = rm.moe_workspace_size(FULL, T)
+        assert n >= prev
+        prev = n
+        lay = rm.moe_workspace_layout(FULL, T)
+        assert lay["total"] == n
+        offs = sorted(v for k, v in lay.items() if k != "total")
+        assert all(o % 256 == 0 for o in offs) and offs[-1] < n
+    assert rm.moe_workspace_size(FULL, 16384) < 4 * 2 ** 30
+
+
+def test_prepared_size_matches_the_page_storage_shapes():
+    # FC1 [896,768,1792] + [896,768,224], FC2 [896,3584,192] + [896,3584,24]: I = 384 is
+    # a multiple of 128, so the prepared layout is exactly as large as the canonical one.
+    want = 896 * (768 * 1792 + 768 * 224 + 3584 * 192 + 3584 * 24)
+    assert rm.moe_prepared_weights_size(FULL) == want
+    # I = 64 pads FC2's K to 128
+    assert rm.moe_prepared_weights_size(TINY) == 16 * (128 * 128 + 128 * 16 + 256 * 64 + 256 * 8)
+
+
+@pytest.mark.parametrize("dims,code", [
+    (rm.MoeDims(3584, 384, 896, 0), -1),
+    (rm.MoeDims(3500, 384, 896, 16), -2),     # H % 128
+    (rm.MoeDims(3584, 96, 896, 16), -2),      # I % 64
+    (rm.MoeDims(3584, 384, 5000, 16), -2),    # E too large
+    (rm.MoeDims(3584, 384, 896, 65), -2),     # k too large
+])
+def test_bad_dims_are_rejected(dims, code):
+    with pytest.raises(rm.MoeError) as ei:
+        rm.moe_workspace_size(dims, 16)
+    assert ei.value.status == code
+
+
+def test_token_count_limits():
+    for T in (0, 16385):
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_workspace_size(FULL, T)
+        assert ei.value.status == -1
+
+
+def _forward(**kw):
+    args = dict(dims=FULL, T=16, x=4096, expert_ids=8192, route_weights=8192, prepared=1 << 20,
+                qx=256, alpha1=512, qa=768, alpha2=1024, situ_beta=None, situ_linear_beta=None,
+                workspace=1 << 24, out=1 << 22, workspace_bytes=rm.moe_workspace_size(FULL, 16),
+                stream=0)
+    args.update(kw)
+    rm.moe_forward(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1),
+    (dict(out=None), -1),
+    (dict(qx=None), -1),
+    (dict(x=4097), -1),                        # misaligned
+    (dict(workspace=(1 << 24) + 16), -1),      # workspace must be 256-aligned
+    (dict(T=0), -1),
+    (dict(T=16385), -1),
+    (dict(workspace_bytes=100), -3),
+    (dict(dims=rm.MoeDims(100, 384, 896, 16)), -2),
+])
+def test_forward_validation_happens_before_any_hip_call(kw, code):
+    with pytest.raises(rm.MoeError) as ei:
+        _forward(**kw)
+    assert ei.value.status == code
+
+
+def test_route_validation():
+    ws = rm.moe_route_workspace_size(8192, 8, 256)
+    base = dict(num_rows=8192, hidden=7168, num_experts=256, top_k=8, x=4096, expert_idx=8192,
+                quant=rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, expanded_x=1 << 20, expanded_scale=1 << 21,
+                expanded_row_idx=1 << 22, expert_cumsum=1 << 23, sorted_expert_idx=None,
+                sorted_row_idx=None, workspace=1 << 24, workspace_bytes=ws, stream=0)
+    for kw, code in ((dict(expanded_scale=None), -1), (dict(quant=5), -1),
+                     (dict(workspace_bytes=ws - 1), -3), (dict(hidden=7), -2),
+                     (dict(num_experts=5000), -2), (dict(num_rows=0), -1)):
+        a = dict(base); a.update(kw)
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_route(**a)
+        assert ei.value.status == code
+
+
+def test_quantize_validation():
+    for kw in (dict(K=24), dict(src=None), dict(src=4098), dict(groups=0)):
+        a = dict(src=4096, groups=1, rows_per_group=4, K=256, q=256, codes=8192, scales=16384,
+                 stream=0)
+        a.update(kw)
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_quantize_nvfp4(**a)
+        assert ei.value.status == -1
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(rm, "_lib_handle", None)
+    monkeypatch.setattr(rm, "library_path", "/nonexistent/libroutedmoe.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        rm.moe_workspace_size(FULL, 16)

@@ -1,0 +1,245 @@
+"""GPU parity of the HIP library against the CPU oracle: quantization, routing, the int8
+routing primitive, and the whole layer at small shapes and edge cases.  Every call goes
+through the C ABI (routed_moe_layer_amd)."""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_moe_layer_amd as rm
+from moe_inputs import (TINY, ROUTE_8K, LayerConfig, draw_expert_ids, draw_route_inputs,
+                        f32_to_bf16_bits)
+from tests.problem import build_layer_problem, oracle_forward
+from tests.gpu_harness import dev, host, empty_bytes, quantize_on_gpu, prepare, DeviceLayer
+from tests import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _wide_rows(seed, n, K):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((n, K)).astype(np.float32)
+    v *= np.exp(rng.uniform(-10, 6, (n, 1))).astype(np.float32)
+    v[rng.random((n, K)) < 0.03] = 0.0
+    v[rng.random((n, K)) < 0.01] *= -1e-6
+    return f32_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("groups,rows,K", [(1, 1, 16), (1, 37, 256), (3, 50, 3584), (5, 7, 384)])
+def test_quantize_nvfp4_bit_exact(groups, rows, K):
+    _say(f"quantize groups={groups} rows={rows} K={K}")
+    bits = _wide_rows(groups * 1000 + rows, groups * rows, K)
+    q = np.exp(np.random.default_rng(K).uniform(-3, 9, groups)).astype(np.float32)
+    codes, scales = quantize_on_gpu(dev(bits), groups, rows, K, dev(q))
+    torch.cuda.synchronize()
+    qrow = np.repeat(q, rows)
+    want_c, want_s = oracle.quantize_nvfp4(oracle.bf16_bits_to_f32(bits), qrow)
+    assert np.array_equal(host(scales), want_s)
+    assert np.array_equal(host(codes), oracle.pack_nibbles(want_c))
+
+
+def _route_on_gpu(ids, E):
+    n, K = ids.shape
+    H = 8
+    x = np.zeros((n, H), np.uint16)
+    R = n * K
+    ex = torch.empty((R, H), dtype=torch.int16, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    sid = torch.empty(R, dtype=torch.int32, device="cuda")
+    sri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = empty_bytes(rm.moe_route_workspace_size(n, K, E), fill=0xFF)
+    rm.moe_route(n, H, E, K, dev(x), dev(ids.astype(np.int32)), rm.MOE_ROUTE_QUANT_NONE, ex, None,
+                 eri, cs, sid, sri, ws)
+    torch.cuda.synchronize()
+    return {"expanded_row_idx": host(eri), "cumsum": host(cs), "sorted_ids": host(sid),
+            "sorted_row_idx": host(sri)}
+
+
+ROUTE_CASES = [
+    ("T1_k16_E896", 1, 16, 896, 0.0),
+    ("T4_k4_E16", 4, 4, 16, 0.0),
+    ("T16_k16_E896", 16, 16, 896, 0.0),
+    ("T33_k3_E5_zipf", 33, 3, 5, 1.5),
+    ("T1000_k8_E256_zipf1.1", 1000, 8, 256, 1.1),
+    ("T1024_k16_E896_zipf1.0", 1024, 16, 896, 1.0),
+    ("T16384_k16_E896", 16384, 16, 896, 0.0),
+    ("T700_k1_E1", 700, 1, 1, 0.0),
+    ("T300_k64_E4096", 300, 64, 4096, 0.5),
+]
+
+
+@pytest.mark.parametrize("name,T,k,E,zipf", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_bit_exact(name, T, k, E, zipf):
+    _say(f"route {name}")
+    ids = draw_expert_ids(T, E, k, seed_index=900 + T, zipf_s=zipf)
+    got = _route_on_gpu(ids, E)
+    want = oracle.route(ids, E)
+    for key in ("expanded_row_idx", "cumsum", "sorted_ids", "sorted_row_idx"):
+        assert np.array_equal(got[key], want[key]), key
+
+
+def test_route_with_duplicates_and_one_hot_expert():
+    _say("route duplicates")
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, 4, (2000, 6)).astype(np.int32)
+    ids[::7] = 2                                        # rows entirely on one expert
+    got = _route_on_gpu(ids, 10)
+    want = oracle.route(ids, 10)
+    for key in want:
+        if key in got:
+            assert np.array_equal(got[key], want[key]), key
+
+
+def test_route_int8_full_size_bit_exact():
+    cfg = ROUTE_8K
+    _say(f"route int8 {cfg.name}")
+    x, ids = draw_route_inputs(cfg)
+    N, K, E, H = cfg.N, cfg.K, cfg.E, cfg.H
+    R = N * K
+    ex = torch.empty((R, H), dtype=torch.int8, device="cuda")
+    esc = torch.empty(R, dtype=torch.float32, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    sid = torch.empty(R, dtype=torch.int32, device="cuda")
+    sri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
+    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs,
+                 sid, sri, ws)
+    torch.cuda.synchronize()
+    want = oracle.route_int8(oracle.bf16_bits_to_f32(x), ids, E)
+    assert np.array_equal(host(eri), want["expanded_row_idx"])
+    assert np.array_equal(host(cs), want["cumsum"])
+    assert np.array_equal(host(sid), want["sorted_ids"])
+    assert np.array_equal(host(sri), want["sorted_row_idx"])
+    assert np.array_equal(host(esc), want["expanded_scale"])
+    assert np.array_equal(host(ex), want["expanded_x"])
+
+
+def test_route_bf16_copy_mode():
+    _say("route bf16 copy")
+    rng = np.random.default_rng(4)
+    N, K, E, H = 300, 4, 7, 136
+    x = f32_to_bf16_bits(rng.standard_normal((N, H)).astype(np.float32))
+    ids = draw_expert_ids(N, E, K, seed_index=44)
+    ex = torch.empty((N * K, H), dtype=torch.int16, device="cuda")
+    eri = torch.empty(N * K, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
+    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_NONE, ex, None, eri, cs, None,
+                 None, ws)
+    torch.cuda.synchronize()
+    r = oracle.route(ids, E)
+    assert np.array_equal(host(eri), r["expanded_row_idx"])
+    assert np.array_equal(host(ex, np.uint16), x[r["sorted_row_idx"] // K])
+
+
+# ------------------------------------------------------------------------------ layer
+def _run_layer(p, prepared=None):
+    cfg = p["cfg"]
+    if prepared is None:
+        prepared = prepare(cfg, p["w13"], p["w13_sf"], p["w2"], p["w2_sf"])
+    L = DeviceLayer(p, prepared)
+    out = L.forward()
+    L.check_guards()
+    return L, host(out, np.uint16), L.intermediates()
+
+
+def test_layer_tiny_parity():
+    _say(f"layer {TINY.name}")
+    p = build_layer_problem(TINY)
+    ref = oracle_forward(p)
+    _, out, inter = _run_layer(p)
+    st, ratio = compare.check_layer(p, out, inter, ref)
+    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, worst err/(2e-2 rms) {ratio:.3f}")
+
+
+def _edge(name, **kw):
+    base = dict(name=name, T=4, H=256, I=64, E=16, k=4, w_std=0.05, seed_index=30)
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+EDGE = [
+    ("T1", _edge("edge_T1", T=1, seed_index=31), None),
+    ("one_expert_many_rows", _edge("edge_E2", T=90, E=2, k=2, seed_index=32), None),
+    ("ragged_tiles", _edge("edge_ragged", T=70, E=3, k=3, H=384, I=128, seed_index=33), None),
+    ("all_on_expert_5", _edge("edge_same", T=40, E=8, k=4, seed_index=34), "same"),
+    ("duplicate_ids", _edge("edge_dup", T=24, E=16, k=4, seed_index=35), "dup"),
+    ("per_expert_situ", _edge("edge_situ", T=32, E=16, k=4, per_expert_situ=True,
+                              seed_index=36), None),
+    ("outliers", _edge("edge_out", T=32, E=16, k=4, outlier_frac=0.05, outlier_mult=30.0,
+                       seed_index=37), None),
+    ("wide_H", _edge("edge_wideH", T=8, H=1024, I=192, E=16, k=6, seed_index=38), None),
+]
+
+
+@pytest.mark.parametrize("name,cfg,mod", EDGE, ids=[c[0] for c in EDGE])
+def test_layer_edge_cases(name, cfg, mod):
+    _say(f"layer edge {name}")
+    p = build_layer_problem(cfg)
+    if mod == "same":
+        p["ids"] = p["ids"].copy()
+        p["ids"][:, 0] = 5                   # every token's first pick is expert 5
+    elif mod == "dup":
+        p["ids"] = p["ids"].copy()
+        p["ids"][:, 1] = p["ids"][:, 0]
+    ref = oracle_forward(p)
+    _, out, inter = _run_layer(p)
+    st, ratio = compare.check_layer(p, out, inter, ref)
+    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, worst err/(2e-2 rms) {ratio:.3f}")
+
+
+def test_layer_determinism_poisoned_workspace_and_reuse():
+    _say("layer determinism / poisoned workspace")
+    p = build_layer_problem(_edge("edge_det", T=48, E=16, k=4, seed_index=40))
+    prepared = prepare(p["cfg"], p["w13"], p["w13_sf"], p["w2"], p["w2_sf"])
+    L = DeviceLayer(p, prepared)
+    a = host(L.forward().clone(), np.uint16)
+    ws2 = empty_bytes(L.ws_bytes, fill=0xFF)
+    out2 = torch.full_like(L.out, -1)
+    b = host(L.forward(workspace=ws2, out=out2), np.uint16)
+    c = host(L.forward(), np.uint16)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    # a workspace sized for more tokens serves a smaller call
+    big = empty_bytes(rm.moe_workspace_size(L.dims, 4096), fill=0x5A)
+    d = host(L.forward(workspace=big), np.uint16)
+    assert np.array_equal(a, d)
+
+
+def test_layer_graph_capture_replay():
+    _say("layer hipGraph capture/replay")
+    p = build_layer_problem(_edge("edge_graph", T=20, E=16, k=4, seed_index=41))
+    prepared = prepare(p["cfg"], p["w13"], p["w13_sf"], p["w2"], p["w2_sf"])
+    L = DeviceLayer(p, prepared)
+    eager = host(L.forward().clone(), np.uint16)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.forward(stream=s)
+    for i in range(5):
+        L.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(L.out, np.uint16), eager), f"replay {i}"
+        L.forward()                     # eager work between replays
+        torch.cuda.synchronize()
