@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-MoE layer on one MI355X, with its roofline and the CPU oracle.
+
+One step = one moe_forward call (NVFP4 quantization of x, routing, FC1 + SiTU +
+requantization, FC2, finalization) over one batch of seeded synthetic tokens at the
+TP8-local shape H=3584, I=384, E=896, top-16, with every input already resident in HBM.
+
+The headline line reports the prefill batch (T=16384, per-expert SiTU parameters, 0.5%
+outlier channels x30): tokens/s, and the roofline of its dominant kernel (the FC1 grouped
+GEMM, bound by the f16 MFMA).  The decode (T=16) and mid (T=1024, Zipf 1.0) batches are
+reported under "workloads" with their HBM rooflines.  Per-stage times come from HIP
+events recorded between the stages on the launch stream (moe_forward_timed).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,decode,mid]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE tokens/s at T=16/1024/16384; % peak HBM GB/s or MFMA util"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16/bf16 MFMA
+FC1_BYTES_PER_EXPERT = 768 * 1792 + 768 * 224          # codes + E4M3 scales
+FC2_BYTES_PER_EXPERT = 3584 * 192 + 3584 * 24
+STAGES = ("quantize_x", "route", "fc1_situ_requant", "fc2", "finalize")
+KERNEL_SOURCES = ("common.h", "kernels.h", "gemm.hip", "quant.hip", "route.hip", "api.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the launch stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routed_moe_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build_weights(cfg, torch, rm):
+    """Draw every expert's BF16 weights, calibrate per-expert scales on the GPU, quantize with
+    moe_quantize_nvfp4 and re-lay with moe_prepare_weights.  Returns prepared weights and
+    the per-expert dequantization scales dW13, dW2 (device)."""
+    from moe_inputs import draw_expert_weights
+    from concurrent.futures import ThreadPoolExecutor
+    E, H, I = cfg.E, cfg.H, cfg.I
+    dims = rm.MoeDims(H, I, E, cfg.k)
+    c13 = torch.empty((E * 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((E * 2 * I, H // 16), dtype=torch.uint8, device="cuda")
+    c2 = torch.empty((E * H, I // 2), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((E * H, I // 16), dtype=torch.uint8, device="cuda")
+    d13 = torch.empty(E, dtype=torch.float32, device="cuda")
+    d2 = torch.empty(E, dtype=torch.float32, device="cuda")
+    chunk = 64
+    t0 = time.time()
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for e0 in range(0, E, chunk):
+            es = list(range(e0, min(E, e0 + chunk)))
+            pairs = list(ex.map(lambda e: draw_expert_weights(cfg, e), es))
+            w13 = torch.from_numpy(np.stack([p[0] for p in pairs]).view(np.int16)).cuda()
+            w2 = torch.from_numpy(np.stack([p[1] for p in pairs]).view(np.int16)).cuda()
+            n = len(es)
+            for w, dst_d, dst_c, dst_s, R, K in ((w13, d13, c13, s13, 2 * I, H),
+                                                 (w2, d2, c2, s2, H, I)):
+                amax = w.view(torch.bfloat16).float().abs().amax(dim=(1, 2))
+                d = torch.where(amax > 0, amax / 2688.0, torch.ones_like(amax))
+                q = (1.0 / d).contiguous()
+                dst_d[e0:e0 + n] = d
+                rm.moe_quantize_nvfp4(w, n, R, K, q, dst_c[e0 * R:(e0 + n) * R],
+                                      dst_s[e0 * R:(e0 + n) * R])
+            torch.cuda.synchronize()
+    prepared = torch.empty(rm.moe_prepared_weights_size(dims), dtype=torch.uint8, device="cuda")
+    rm.moe_prepare_weights(dims, c13, s13, c2, s2, prepared)
+    torch.cuda.synchronize()
+    log(f"weights drawn, quantized and prepared in {time.time() - t0:.1f} s")
+    del c13, s13, c2, s2
+    return prepared, d13, d2
+
+
+def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rotations):
+    """Time `steps` moe_forward calls of one workload; returns its result dict."""
+    from moe_inputs import (draw_tokens, draw_expert_ids, draw_route_weights, draw_situ_params,
+                            LayerConfig)
+    E, H, I, k, T = cfg.E, cfg.H, cfg.I, cfg.k, cfg.T
+    dims = rm.MoeDims(H, I, E, k)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = dev(draw_tokens(T, H, cfg.seed_index, cfg.outlier_frac, cfg.outlier_mult).view(np.int16))
+    rw = dev(draw_route_weights(T, k, cfg.seed_index).view(np.int16))
+    ids_host = [draw_expert_ids(T, E, k, cfg.seed_index + 100 * r, cfg.zipf_s)
+                for r in range(rotations)]
+    ids = [dev(a) for a in ids_host]
+    beta, lam = draw_situ_params(cfg)
+    beta = None if beta is None else dev(beta)
+    lam = None if lam is None else dev(lam)
+    # calibration (model preparation): dX from the batch, dA from one calibration call
+    amax_x = x.view(torch.bfloat16).float().abs().amax()
+    dX = torch.where(amax_x > 0, amax_x / 2688.0, torch.ones_like(amax_x))
+    qx = (1.0 / dX).reshape(1).contiguous()
+    alpha1 = (dX * d13).contiguous()
+    ones = torch.ones(E, dtype=torch.float32, device="cuda")
+    ws_bytes = rm.moe_workspace_size(dims, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    lay = rm.moe_workspace_layout(dims, T)
+    rm.moe_forward(dims, T, x, ids[0], rw, prepared, qx, alpha1, ones, ones, beta, lam, ws, out)
+    a_amax = ws[lay["a_amax"]: lay["a_amax"] + 4 * E].view(torch.float32).amax()
+    dA = torch.where(a_amax > 0, a_amax / 2688.0, torch.ones_like(a_amax))
+    qa = torch.full((E,), 1.0, dtype=torch.float32, device="cuda") / dA
+    alpha2 = (dA * d2).contiguous()
+    torch.cuda.synchronize()
+
+    def call(i, evs=None):
+        args = (dims, T, x, ids[i % rotations], rw, prepared, qx, alpha1, qa, alpha2, beta, lam,
+                ws, out)
+        if evs is None:
+            rm.moe_forward(*args)
+        else:
+            rm.moe_forward_timed(*args, evs)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    nev = rm.MOE_FORWARD_STAGES + 1
+    evs = [events.create(nev) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.zeros((steps, len(STAGES)))
+    for i in range(steps):
+        for s in range(len(STAGES)):
+            stage_ms[i, s] = events.elapsed_ms(evs[i][s], evs[i][s + 1])
+    gpu_ms = [events.elapsed_ms(evs[i][0], evs[i][-1]) for i in range(steps)]
+    for e in evs:
+        events.destroy(e)
+    ms_per_step = wall * 1e3 / steps
+    # algorithmic work
+    distinct = np.mean([len(np.unique(a)) for a in ids_host])
+    weight_bytes = distinct * (FC1_BYTES_PER_EXPERT + FC2_BYTES_PER_EXPERT)
+    act_bytes = T * H * 2 * 2 + T * k * (4 + 2)                  # x, out, ids, route weights
+    R = T * k
+    fc1_flops = 2.0 * R * 2 * I * H
+    fc2_flops = 2.0 * R * H * I
+    st = {name: float(np.mean(stage_ms[:, j])) for j, name in enumerate(STAGES)}
+    res = {
+        "workload": cfg.name, "T": T, "tokens_per_s": T / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step, "gpu_ms_per_step": float(np.mean(gpu_ms)),
+        "stage_ms": st, "distinct_experts": float(distinct),
+        "algorithmic_bytes": float(weight_bytes + act_bytes),
+        "hbm_frac_of_step": (weight_bytes + act_bytes) / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "flops": fc1_flops + fc2_flops,
+        "mfma_frac_of_step": (fc1_flops + fc2_flops) / (ms_per_step * 1e-3) / (PEAK_F16_TFLOPS * 1e12),
+        "fc1": {"flops": fc1_flops, "bytes": distinct * FC1_BYTES_PER_EXPERT + T * H * 9 / 16,
+                "ms": st["fc1_situ_requant"]},
+        "fc2": {"flops": fc2_flops, "bytes": distinct * FC2_BYTES_PER_EXPERT, "ms": st["fc2"]},
+        "rotations": rotations,
+    }
+    keep = dict(x=x, ids=ids_host[0], rw=rw, qx=qx, alpha1=alpha1, qa=qa, alpha2=alpha2,
+                beta=beta, lam=lam)
+    return res, keep
+
+
+def cpu_baseline(cfg, keep, torch, n_tokens):
+    """The oracle, as it stands, on a bounded sample of the same workload's tokens."""
+    import oracle
+    from tests.problem import ExpertStore
+    from moe_inputs import draw_tokens, draw_route_weights
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    x = draw_tokens(cfg.T, cfg.H, cfg.seed_index, cfg.outlier_frac, cfg.outlier_mult)
+    rw = draw_route_weights(cfg.T, cfg.k, cfg.seed_index)
+    ids = keep["ids"]
+    tokens = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    h = lambda t: t.detach().cpu().numpy()
+    a1, qa, a2 = h(keep["alpha1"]), h(keep["qa"]), h(keep["alpha2"])
+    beta = None if keep["beta"] is None else h(keep["beta"])
+    lam = None if keep["lam"] is None else h(keep["lam"])
+    qx = np.float32(h(keep["qx"])[0])
+    # canonical NVFP4 weights of the touched experts (weight preparation, not timed)
+    from moe_inputs import draw_expert_weights
+    used = np.unique(ids[tokens])
+    qW13 = np.ones(cfg.E, np.float32)
+    qW2 = np.ones(cfg.E, np.float32)
+    for e in used:
+        w13b, w2b = draw_expert_weights(cfg, int(e))
+        qW13[e] = oracle.calibrate_weights(w13b[None])[1][0]
+        qW2[e] = oracle.calibrate_weights(w2b[None])[1][0]
+    store = ExpertStore(cfg, qW13, qW2, used)
+    t0 = time.perf_counter()
+    oracle.token_forward(tokens, x, ids, rw, store.w13, store.w13_sf, store.w2, store.w2_sf,
+                         qx, a1, qa, a2, beta, lam)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_tokens} tokens of {cfg.name} ({n_tokens * cfg.k} routed rows, "
+                      f"{len(used)} experts decoded), {dt:.1f} s"}
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    no summary exists or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+        entry = data.get(kernel)
+        if not entry or entry.get("source_hash") != kernel_source_hash():
+            return None
+        return float(entry["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="prefill,decode,mid")
+    ap.add_argument("--cpu-tokens", type=int, default=32,
+                    help="tokens of the oracle's bounded CPU sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
+              "not part of this build (the layer is one TP rank's work; see the design notes "
+              "on sharding).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import routed_moe_layer_amd as rm
+    from moe_inputs import DECODE_16, MID_1024, PREFILL_16K
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    rm._lib()
+    events = HipEvents()
+    prepared, d13, d2 = build_weights(DECODE_16, torch, rm)
+    chosen = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4)}
+    results, keeps = {}, {}
+    for name in chosen:
+        cfg, rot = cfgs[name]
+        log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+        results[name], keeps[name] = layer_workload(cfg, torch, rm, prepared, d13, d2,
+                                                    args.steps, args.warmup, events, rot)
+        r = results[name]
+        log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step, stages "
+            + ", ".join(f"{k} {v:.3f}" for k, v in r["stage_ms"].items()))
+    head = "prefill" if "prefill" in results else chosen[0]
+    hr = results[head]
+    hcfg = cfgs[head][0]
+    fc1_ms = hr["fc1"]["ms"]
+    if head == "prefill":
+        roof = {"bound": "mfma", "achieved": hr["fc1"]["flops"] / (fc1_ms * 1e-3) / 1e12,
+                "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": hr["fc1"]["bytes"] / (fc1_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "fc1_kernel"
+    roof["traffic"] = traffic_from_profile(f"fc1_kernel:{hcfg.name}")
+    cpu = None
+    if args.cpu_tokens > 0:
+        log(f"oracle CPU baseline on {args.cpu_tokens} tokens of {hcfg.name}")
+        cpu = cpu_baseline(hcfg, keeps[head], torch, args.cpu_tokens)
+    line = {
+        "metric": METRIC, "value": hr["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": hr["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": hcfg.name, "T": hcfg.T, "H": hcfg.H, "I": hcfg.I, "E": hcfg.E,
+                   "top_k": hcfg.k, "parallelism": "single GPU (one TP8 rank's share)"},
+        "roofline": roof, "cpu_baseline": cpu, "workloads": results,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

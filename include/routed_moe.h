@@ -184,6 +184,22 @@ moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32
                          void* workspace, size_t workspace_bytes, uint16_t* out,
                          moe_stream_t stream);
 
+/* moe_forward with per-stage timing events, for profiling.  The work and its results are
+ * identical to moe_forward.  `events` is a host array of MOE_FORWARD_STAGES + 1 hipEvent_t
+ * handles created by the caller; event i is recorded on `stream` at the start of stage i
+ * and event MOE_FORWARD_STAGES after the last stage.  The stages are, in order: 0 NVFP4
+ * quantization of x, 1 routing (histogram, scan, scatter), 2 FC1 + SiTU + requantization,
+ * 3 FC2, 4 finalization.  The caller reads the stage durations with hipEventElapsedTime
+ * once the events have completed.  NULL events -> MOE_ERR_INVALID_ARG. */
+#define MOE_FORWARD_STAGES 5
+moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
+                               const int32_t* expert_ids, const uint16_t* route_weights,
+                               const void* prepared, const float* qx, const float* alpha1,
+                               const float* qa, const float* alpha2, const float* situ_beta,
+                               const float* situ_linear_beta, void* workspace,
+                               size_t workspace_bytes, uint16_t* out, moe_stream_t stream,
+                               void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

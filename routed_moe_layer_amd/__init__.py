@@ -15,6 +15,7 @@ __all__ = [
     "MoeError", "MoeDims", "library_path", "moe_status_string", "moe_workspace_size",
     "moe_prepared_weights_size", "moe_workspace_layout", "moe_route_workspace_size",
     "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_forward",
+    "moe_forward_timed", "MOE_FORWARD_STAGES",
     "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
 ]
 
@@ -24,11 +25,12 @@ library_path = os.path.join(_PKG, "lib", "libroutedmoe.so")
 MOE_ROUTE_QUANT_NONE = 0
 MOE_ROUTE_QUANT_INT8_DYNAMIC = 1
 MOE_MAX_TOKENS = 16384
+MOE_FORWARD_STAGES = 5
 
 # Every symbol include/routed_moe.h declares.
 EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_size",
             "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
-            "moe_prepare_weights", "moe_route", "moe_forward")
+            "moe_prepare_weights", "moe_route", "moe_forward", "moe_forward_timed")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +76,8 @@ def _lib():
             "moe_prepare_weights": (st, [MoeDims, P, P, P, P, P, SZ, P]),
             "moe_route": (st, [I32, I32, I32, I32, P, P, ctypes.c_int, P, P, P, P, P, P, P, SZ, P]),
             "moe_forward": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]),
+            "moe_forward_timed": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P,
+                                       ctypes.POINTER(P)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -175,3 +179,15 @@ def moe_forward(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa,
         dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
         _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
         _ptr(workspace), nb, _ptr(out), _stream(stream)))
+
+
+def moe_forward_timed(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
+                      situ_beta, situ_linear_beta, workspace, out, events,
+                      workspace_bytes=None, stream=None):
+    """``events``: a sequence of MOE_FORWARD_STAGES + 1 raw hipEvent_t handles (ints)."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    ev = (ctypes.c_void_p * len(events))(*events)
+    _check("moe_forward_timed", _lib().moe_forward_timed(
+        dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
+        _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
+        _ptr(workspace), nb, _ptr(out), _stream(stream), ev))

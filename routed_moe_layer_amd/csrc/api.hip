@@ -190,12 +190,13 @@ moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, in
   return hip_status(e);
 }
 
-moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
-                         const uint16_t* route_weights, const void* prepared, const float* qx,
-                         const float* alpha1, const float* qa, const float* alpha2,
-                         const float* situ_beta, const float* situ_linear_beta,
-                         void* workspace, size_t workspace_bytes, uint16_t* out,
-                         moe_stream_t stream) {
+static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
+                                 const int32_t* expert_ids, const uint16_t* route_weights,
+                                 const void* prepared, const float* qx, const float* alpha1,
+                                 const float* qa, const float* alpha2, const float* situ_beta,
+                                 const float* situ_linear_beta, void* workspace,
+                                 size_t workspace_bytes, uint16_t* out, moe_stream_t stream,
+                                 void* const* events) {
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
   if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
@@ -238,8 +239,13 @@ moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32
   a.route_weights = route_weights;
   a.out = out;
 
+  auto mark = [&](int i) -> bool {
+    return events == nullptr ||
+           hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
   hipError_t e = launch_quantize_nvfp4(x, 1, T, H, qx, ws + L.pub.x_codes, ws + L.pub.x_scales, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (e != hipSuccess || !mark(1)) return MOE_ERR_HIP;
   RouteBuffers b{};
   b.tile_hist = reinterpret_cast<int32_t*>(ws + L.tile_hist);
   b.counts = reinterpret_cast<int32_t*>(ws + L.pub.expert_counts);
@@ -251,11 +257,37 @@ moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32
   b.tiles = reinterpret_cast<TileDesc*>(ws + L.tiles);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   b.amax_reset = a.a_amax;
-  if ((e = launch_route(expert_ids, R, E, b, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = launch_fc1(a, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = launch_fc2(a, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = launch_finalize(a, s)) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+  if (launch_fc1(a, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+  if (launch_fc2(a, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+  if (launch_finalize(a, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
+                         const uint16_t* route_weights, const void* prepared, const float* qx,
+                         const float* alpha1, const float* qa, const float* alpha2,
+                         const float* situ_beta, const float* situ_linear_beta,
+                         void* workspace, size_t workspace_bytes, uint16_t* out,
+                         moe_stream_t stream) {
+  return forward_impl(d, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
+                      situ_beta, situ_linear_beta, workspace, workspace_bytes, out, stream,
+                      nullptr);
+}
+
+moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
+                               const int32_t* expert_ids, const uint16_t* route_weights,
+                               const void* prepared, const float* qx, const float* alpha1,
+                               const float* qa, const float* alpha2, const float* situ_beta,
+                               const float* situ_linear_beta, void* workspace,
+                               size_t workspace_bytes, uint16_t* out, moe_stream_t stream,
+                               void* const* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < MOE_FORWARD_STAGES + 1; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(d, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
+                      situ_beta, situ_linear_beta, workspace, workspace_bytes, out, stream,
+                      events);
 }
 
 }  // extern "C"

@@ -3,7 +3,7 @@
 //  * quantize_nvfp4_kernel: group-16 NVFP4 quantization of BF16 rows ("Cake SiTU
 //    backend", intro: group-16 NVFP4 input quantization with the fp32 scale qX).  One
 //    thread per 16-value block: a 32-byte load, 8 bytes of codes and 1 scale byte out.
-//    HBM-bound (34 bytes per 16 values moved).
+//    HBM-bound (41 bytes per 16 values moved).
 //  * route_permute_kernel: the token movement of "torch_npu.npu_moe_init_routing_v2"
 //    (section 计算公式, steps 4-5): per-row dynamic int8 quantization (or a BF16 copy),
 //    each token row written to its K expert-sorted positions through the gather map.
