@@ -266,6 +266,8 @@ def main():
     ap.add_argument("--workloads", default="prefill,decode,mid")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens of the oracle's bounded CPU sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
@@ -278,6 +280,15 @@ def main():
     from moe_inputs import DECODE_16, MID_1024, PREFILL_16K
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
     rm._lib()
     events = HipEvents()
     prepared, d13, d2 = build_weights(DECODE_16, torch, rm)

@@ -38,7 +38,7 @@ int padded_inter(int I) { return (I + kChunk - 1) / kChunk * kChunk; }
 
 struct Layout {
   moe_workspace_layout_t pub;
-  size_t offsets, tile_hist, tiles, num_tiles;
+  size_t offsets, tile_hist, tiles_small, tiles_big, num_tiles;
 };
 
 Layout make_layout(const moe_dims_t& d, int64_t T) {
@@ -54,8 +54,9 @@ Layout make_layout(const moe_dims_t& d, int64_t T) {
   L.offsets = c.take((E + 1) * 4);
   L.pub.expert_cumsum = c.take(E * 4);
   L.tile_hist = c.take(static_cast<size_t>(route_tiles(R)) * E * 4);
-  L.tiles = c.take(static_cast<size_t>(max_token_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
-  L.num_tiles = c.take(4);
+  L.tiles_small = c.take(static_cast<size_t>(max_small_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
+  L.tiles_big = c.take(static_cast<size_t>(max_big_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
+  L.num_tiles = c.take(8);
   L.pub.a_codes = c.take(R * I / 2);
   L.pub.a_scales = c.take(R * I / 16);
   L.pub.o_rows = c.take(R * H * 2);
@@ -222,9 +223,11 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   int32_t* expanded_row_idx = reinterpret_cast<int32_t*>(ws + L.pub.expanded_row_idx);
   a.sorted_row_idx = sorted_row_idx;
   a.expanded_row_idx = expanded_row_idx;
-  a.tiles = reinterpret_cast<TileDesc*>(ws + L.tiles);
+  a.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
+  a.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   a.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
-  a.max_tiles = max_token_tiles(R, E);
+  a.max_small = max_small_tiles(R, E);
+  a.max_big = max_big_tiles(R, E);
   const uint8_t* p = static_cast<const uint8_t*>(prepared);
   a.w13_codes = p;
   a.w13_scales = a.w13_codes + static_cast<size_t>(E) * prepared_codes_bytes(2 * I, H);
@@ -254,7 +257,8 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   b.sorted_ids = sorted_ids;
   b.sorted_row_idx = sorted_row_idx;
   b.expanded_row_idx = expanded_row_idx;
-  b.tiles = reinterpret_cast<TileDesc*>(ws + L.tiles);
+  b.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
+  b.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   b.amax_reset = a.a_amax;
   if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;

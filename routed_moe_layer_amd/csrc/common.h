@@ -60,10 +60,16 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
 
 // E2M1 code of an fp32 value: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
 // saturating at 6; bit 3 carries the sign of y (so -0 and small negatives give 0x8).
+// On [0,2) the grid is code/2, so the code is rint(2a); on [2,4) it is code-2, so the
+// code is 4 + rint(a-2) (a-2 is exact there); above 4 only 4 (code 6) and 6 (code 7)
+// remain, split at the tie 5 which goes to the even code 6.  rint rounds half to even,
+// which is the even-code rule because the codes are consecutive on each piece.
 __device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  float a = fabsf(y);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a < 2.0f) c = static_cast<uint32_t>(rintf(a + a));
+  else if (a < 4.0f) c = 4u + static_cast<uint32_t>(rintf(a - 2.0f));
+  else c = a > 5.0f ? 7u : 6u;
   return c | ((__float_as_uint(y) >> 28) & 8u);
 }
 

@@ -12,202 +12,356 @@
 // accumulator after block dequantization ("Nvfp4 Tensor": the global scale is applied
 // after block dequantization).
 //
-// Work decomposition: the router writes a list of token tiles (up to kTokTile expert-sorted
-// rows of one expert).  A workgroup (4 waves) takes one token tile and 128 weight rows;
-// each wave owns 32 weight rows (two 16-row MFMA groups) and all tokens of the tile.
-// Weight fragments stream straight from HBM into registers in the prepared layout (one
-// 16-byte load per lane per 128-column chunk); the token tile is staged in LDS and shared
-// by the four waves.  Both operands are decoded to f16 in registers right before the MFMA.
-// The FC1 epilogue fuses alpha1, SiTU, the group-16 requantization (each wave's 32 rows
-// are 16 intermediate channels = one NVFP4 group) and the per-expert amax statistic.
+// Work decomposition: the router writes two lists of token tiles (expert-sorted rows of
+// one expert): "small" tiles of up to 32 rows (one per lightly used expert) and "big" tiles
+// of up to 128 rows.  Each list has its own kernel instance.  A workgroup (4 waves) takes
+// one token tile and a slab of weight rows; each wave owns WRG 16-row MFMA groups of the
+// slab and all tokens of the tile:
+//   * weights stream from HBM straight into registers in the prepared layout (one 16-byte
+//     load per lane per group per 128-column chunk), one chunk ahead of the MFMAs, and are
+//     decoded to f16 in registers (each wave owns its rows, so nothing is decoded twice);
+//   * the token tile's codes for the next chunk are loaded into registers, decoded once per
+//     workgroup to f16 and written to a double-buffered LDS tile that all four waves read
+//     as MFMA operands (one barrier per chunk).
+// The FC1 epilogue fuses alpha1, SiTU, the group-16 requantization (two consecutive MFMA
+// row groups hold the gate/up pairs of 16 intermediate channels = one NVFP4 group) and the
+// per-expert amax statistic; the FC2 epilogue applies alpha2 and stores BF16 rows.
 #include "common.h"
 #include "kernels.h"
 
 namespace rmoe {
 
-constexpr int kLdsStride = 17;      // dwords per staged token row (16 + 1 pad)
-
+// SiTU(g, u) = (beta*tanh(g/beta)*sigmoid(g)) * (lam*tanh(u/lam)), written with
+// exponentials of non-positive arguments only (no overflow) and one reciprocal:
+//   tanh(x) = sign(x) (1 - t)/(1 + t), t = exp(-2|x|);
+//   sigmoid(g) = (g >= 0 ? 1 : s)/(1 + s), s = exp(-|g|);
+// so SiTU = beta*lam*sign(g u) (1-t1)(1-t2)(g>=0 ? 1 : s) / ((1+t1)(1+t2)(1+s)), every
+// denominator factor in [1, 2].  exp uses the hardware base-2 exponential.
 __device__ __forceinline__ float situ(float g, float u, float beta, float inv_beta,
                                       float lam, float inv_lam) {
-  float sig = 1.0f / (1.0f + __expf(-g));
-  float gate = beta * tanhf(g * inv_beta) * sig;
-  return gate * (lam * tanhf(u * inv_lam));
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float ag = fabsf(g), au = fabsf(u);
+  const float t1 = __builtin_amdgcn_exp2f(-2.0f * kLog2e * inv_beta * ag);
+  const float t2 = __builtin_amdgcn_exp2f(-2.0f * kLog2e * inv_lam * au);
+  const float sg = __builtin_amdgcn_exp2f(-kLog2e * ag);
+  const float num = (1.0f - t1) * (1.0f - t2) * (g >= 0.0f ? 1.0f : sg);
+  const float den = (1.0f + t1) * (1.0f + t2) * (1.0f + sg);
+  const float mag = beta * lam * num * __builtin_amdgcn_rcpf(den);
+  return ((g < 0.0f) != (u < 0.0f)) ? -mag : mag;
 }
 
-// Main loop shared by FC1 and FC2.  Token rows come from `tok_codes` (row stride
-// tok_stride bytes, scales tok_sstride bytes) at the row indices in s_row[]; valid_bytes
-// limits the row (columns past the real K read as zero codes with zero scales).
-template <int BN>
-__device__ __forceinline__ void mainloop(const uint4* __restrict__ wcodes,
-                                         const uint32_t* __restrict__ wscales, int64_t slot,
-                                         int nchunks,
-                                         const uint8_t* __restrict__ tok_codes,
-                                         const uint8_t* __restrict__ tok_scales,
-                                         int64_t tok_stride, int64_t tok_sstride,
-                                         int valid_code_bytes, int valid_scale_bytes,
-                                         const int64_t* s_row, uint32_t* s_codes,
-                                         uint32_t* s_scales, int ncb,
-                                         f32x4 (&acc)[2][BN / 16]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  for (int c = 0; c < nchunks; ++c) {
-    for (int i = tid; i < BN * 16; i += blockDim.x) {
-      const int r = i >> 4, d = i & 15;
-      const int byte = c * 64 + 4 * d;
-      uint32_t v = 0;
-      if (byte < valid_code_bytes)
-        v = *reinterpret_cast<const uint32_t*>(tok_codes + s_row[r] * tok_stride + byte);
-      s_codes[r * kLdsStride + d] = v;
+
+// ---------------------------------------------------------------------------------------
+// NW waves per workgroup, WRG 16-row MFMA groups per wave, up to BN tokens per tile.
+template <int MODE, int NW, int WRG, int BN>
+struct GemmCfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kNcb = BN / 16;                 // 16-token MFMA column blocks
+  static constexpr int kWgRows = NW * WRG * 16;        // weight rows per workgroup
+  static constexpr int kLdsRow = kChunk + 8;           // f16 per staged token row (+16 B pad)
+  static constexpr int kThreadsPerRow = kThreads / BN; // token-decode threads per row
+  static constexpr int kDwPerThread = 16 / kThreadsPerRow;   // code dwords (of 16 per row)
+  static_assert(kThreads % BN == 0 && 16 % kThreadsPerRow == 0, "token decode split");
+};
+
+// Loads, for chunk c, the code dwords and scale bytes one thread decodes.  Columns past
+// the row's real length read as zero codes with a zero scale.
+template <int NDW>
+__device__ __forceinline__ void load_token_chunk(const uint8_t* __restrict__ codes_row,
+                                                 const uint8_t* __restrict__ scales_row,
+                                                 int c, int part, int valid_code_bytes,
+                                                 uint32_t (&w)[NDW], uint32_t& sc) {
+  static_assert(NDW <= 2 || NDW % 4 == 0, "a thread decodes 1, 2 or a multiple of 4 dwords");
+  const int byte0 = c * 64 + part * NDW * 4;           // first code byte of this thread
+  if constexpr (NDW == 1) {
+    w[0] = byte0 < valid_code_bytes ? *reinterpret_cast<const uint32_t*>(codes_row + byte0) : 0u;
+  } else if constexpr (NDW == 2) {
+    if (byte0 < valid_code_bytes) {
+      const uint2 v = *reinterpret_cast<const uint2*>(codes_row + byte0);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = 0; w[1] = 0;
     }
-    for (int i = tid; i < BN * 2; i += blockDim.x) {
-      const int r = i >> 1, d = i & 1;
-      const int byte = c * 8 + 4 * d;
-      uint32_t v = 0;
-      if (byte < valid_scale_bytes)
-        v = *reinterpret_cast<const uint32_t*>(tok_scales + s_row[r] * tok_sstride + byte);
-      s_scales[r * 2 + d] = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NDW; i += 4) {
+      if (byte0 + 4 * i < valid_code_bytes) {
+        const uint4 v = *reinterpret_cast<const uint4*>(codes_row + byte0 + 4 * i);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+      } else {
+        w[i] = 0; w[i + 1] = 0; w[i + 2] = 0; w[i + 3] = 0;
+      }
     }
-    const uint4 wc0 = wcodes[(slot * nchunks + c) * 64 + lane];
-    const uint4 wc1 = wcodes[((slot + 1) * nchunks + c) * 64 + lane];
-    const uint32_t ws0 = wscales[prepared_scale_index(slot, nchunks, c, lane)];
-    const uint32_t ws1 = wscales[prepared_scale_index(slot + 1, nchunks, c, lane)];
-    __syncthreads();
-    const uint32_t wcw[2][4] = {{wc0.x, wc0.y, wc0.z, wc0.w}, {wc1.x, wc1.y, wc1.z, wc1.w}};
+  }
+  // NDW dwords = 8*NDW codes = NDW/2 blocks; scale bytes of this thread
+  const int sbyte0 = byte0 / 8;
+  sc = 0;
+  if (byte0 < valid_code_bytes) {
+    if constexpr (NDW >= 8) {
+      sc = *reinterpret_cast<const uint32_t*>(scales_row + sbyte0);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 w0 = decode8(wcw[0][s], scale_f16x2((ws0 >> (8 * s)) & 0xFFu));
-      const f16x8 w1 = decode8(wcw[1][s], scale_f16x2((ws1 >> (8 * s)) & 0xFFu));
-      const int sbyte = 2 * s + (g >> 1);            // block of this lane's 8 columns
+      for (int b = 0; b < (NDW + 1) / 2; ++b)
+        sc |= static_cast<uint32_t>(scales_row[sbyte0 + b]) << (8 * b);
+    }
+  }
+}
+
+template <int NDW>
+__device__ __forceinline__ void store_token_chunk(_Float16* __restrict__ dst,
+                                                  const uint32_t (&w)[NDW], uint32_t sc) {
 #pragma unroll
-      for (int cb = 0; cb < BN / 16; ++cb) {
-        if (cb < ncb) {
-          const int n = cb * 16 + (lane & 15);
-          const uint32_t xw = s_codes[n * kLdsStride + 4 * s + g];
-          const uint32_t xs = (s_scales[n * 2 + (sbyte >> 2)] >> (8 * (sbyte & 3))) & 0xFFu;
-          const f16x8 xf = decode8(xw, scale_f16x2(xs));
-          acc[0][cb] = mfma16x16x32(w0, xf, acc[0][cb]);
-          acc[1][cb] = mfma16x16x32(w1, xf, acc[1][cb]);
+  for (int i = 0; i < NDW; ++i) {
+    const f16x8 v = decode8(w[i], scale_f16x2((sc >> (8 * (i >> 1))) & 0xFFu));
+    *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
+  }
+}
+
+// Workgroup -> (token tile, weight slab).  Workgroups are dealt to the 8 XCDs round-robin
+// by id; kXcdRun consecutive logical ids are kept on one XCD (and in flight together),
+// and logical ids run over kTileGroup consecutive token tiles of one slab before moving to
+// the next slab.  The token tiles of an expert are adjacent in the work list, so the
+// workgroups that read the same weight slab share that XCD's L2, and a group of token
+// tiles is reread across slabs while it is still cached.
+constexpr int kXcds = 8, kXcdRun = 4, kTileGroup = 4;
+
+__device__ __forceinline__ void map_workgroup(int b, int n_wt, int* tt, int* wt) {
+  const int xcd = b % kXcds, slot = b / kXcds;
+  const int L = ((slot / kXcdRun) * kXcds + xcd) * kXcdRun + slot % kXcdRun;
+  const int per_group = n_wt * kTileGroup;
+  *tt = (L / per_group) * kTileGroup + L % kTileGroup;
+  *wt = (L / kTileGroup) % n_wt;
+}
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Everything a workgroup needs once its tile is known.
+struct TileCtx {
+  TileDesc td;
+  int e, tid, lane, w, g;
+  int nchunks, G0;
+  int64_t slot0;
+  const uint4* wcodes;
+  const uint32_t* wscales;
+  const uint8_t* trow_codes;
+  const uint8_t* trow_scales;
+  int trow, tpart, valid_code_bytes;
+};
+
+template <int WRG>
+__device__ __forceinline__ void load_weights(const TileCtx& t, int c, uint4 (&wc)[WRG],
+                                             uint32_t (&ws)[WRG]) {
+#pragma unroll
+  for (int r = 0; r < WRG; ++r) {
+    wc[r] = t.wcodes[((t.slot0 + r) * t.nchunks + c) * 64 + t.lane];
+    ws[r] = t.wscales[prepared_scale_index(t.slot0 + r, t.nchunks, c, t.lane)];
+  }
+}
+
+// Raw token codes and scale bytes of one chunk for one decoding thread.
+template <int NDW>
+struct TokRegs {
+  uint32_t w[NDW];
+  uint32_t sc;
+};
+
+// One 128-column chunk c.  Register pipelines run two chunks ahead: on entry `wc/ws` hold
+// chunk c's raw weights and `tnext` chunk c+1's raw token codes; `tfree` is free.
+//   1. decode chunk c's weight fragments (frees wc/ws),
+//   2. issue the loads of chunk c+2 (weights into wc/ws, token codes into tfree),
+//   3. wait for the LDS buffer of chunk c,
+//   4. run the MFMAs,
+//   5. decode chunk c+1's token codes into the other LDS buffer.
+template <int WRG, int NCBA, int NDW, int LROW>
+__device__ __forceinline__ void chunk_step(const TileCtx& t, int c, uint4 (&wc)[WRG],
+                                           uint32_t (&ws)[WRG], TokRegs<NDW>& tfree,
+                                           const TokRegs<NDW>& tnext, const _Float16* tb_cur,
+                                           _Float16* tb_next, f32x4 (&acc)[WRG][NCBA]) {
+  const bool tactive = t.trow < 16 * NCBA;
+  f16x8 wf[4][WRG];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int r = 0; r < WRG; ++r) {
+      const uint32_t cw = s == 0 ? wc[r].x : s == 1 ? wc[r].y : s == 2 ? wc[r].z : wc[r].w;
+      wf[s][r] = decode8(cw, scale_f16x2((ws[r] >> (8 * s)) & 0xFFu));
+    }
+  if (c + 2 < t.nchunks) {
+    load_weights<WRG>(t, c + 2, wc, ws);
+    if (tactive)
+      load_token_chunk<NDW>(t.trow_codes, t.trow_scales, c + 2, t.tpart, t.valid_code_bytes,
+                            tfree.w, tfree.sc);
+  }
+  __syncthreads();                                      // LDS buffer of chunk c complete
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int cb = 0; cb < NCBA; ++cb) {
+      const f16x8 xf = *reinterpret_cast<const f16x8*>(
+          tb_cur + (cb * 16 + (t.lane & 15)) * LROW + 32 * s + 8 * t.g);
+#pragma unroll
+      for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(wf[s][r], xf, acc[r][cb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (c + 1 < t.nchunks && tactive)
+    store_token_chunk<NDW>(tb_next + t.trow * LROW + t.tpart * NDW * 8, tnext.w, tnext.sc);
+}
+
+template <int MODE, int NW, int WRG, int BN, int NCBA>
+__device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
+                                          _Float16 (*s_tok)[BN * GemmCfg<MODE, NW, WRG, BN>::kLdsRow]) {
+  using C = GemmCfg<MODE, NW, WRG, BN>;
+  constexpr int NDW = C::kDwPerThread;
+  constexpr int LROW = C::kLdsRow;
+  f32x4 acc[WRG][NCBA];
+#pragma unroll
+  for (int i = 0; i < WRG; ++i)
+#pragma unroll
+    for (int j = 0; j < NCBA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wcA[WRG], wcB[WRG];
+  uint32_t wsA[WRG], wsB[WRG];
+  TokRegs<NDW> tA, tB;
+  const bool tactive = t.trow < 16 * NCBA;
+  load_weights<WRG>(t, 0, wcA, wsA);
+  if (t.nchunks > 1) load_weights<WRG>(t, 1, wcB, wsB);
+  if (tactive) {
+    load_token_chunk<NDW>(t.trow_codes, t.trow_scales, 0, t.tpart, t.valid_code_bytes, tA.w, tA.sc);
+    store_token_chunk<NDW>(s_tok[0] + t.trow * LROW + t.tpart * NDW * 8, tA.w, tA.sc);
+    if (t.nchunks > 1)
+      load_token_chunk<NDW>(t.trow_codes, t.trow_scales, 1, t.tpart, t.valid_code_bytes, tB.w, tB.sc);
+  }
+  // two chunks per trip so register sets and LDS buffers are named statically; an odd
+  // last chunk is peeled after the loop (no conditional MFMA block inside the loop)
+  int c = 0;
+  for (; c + 1 < t.nchunks; c += 2) {
+    chunk_step<WRG, NCBA, NDW, LROW>(t, c, wcA, wsA, tA, tB, s_tok[0], s_tok[1], acc);
+    chunk_step<WRG, NCBA, NDW, LROW>(t, c + 1, wcB, wsB, tB, tA, s_tok[1], s_tok[0], acc);
+  }
+  if (c < t.nchunks)
+    chunk_step<WRG, NCBA, NDW, LROW>(t, c, wcA, wsA, tA, tB, s_tok[0], s_tok[1], acc);
+
+  const TileDesc td = t.td;
+  const int e = t.e, lane = t.lane, g = t.g, G0 = t.G0;
+  if constexpr (MODE == 0) {
+    // Lane holds rows 4g..4g+3 of each group = (gate i, up i, gate i+1, up i+1),
+    // i = 8G + 2g.  Groups (2p, 2p+1) of the wave form NVFP4 group G0/2 + p.
+    const float al = a.alpha1[e];
+    const float qa = a.qa[e];
+    const float beta = a.beta ? a.beta[e] : 4.0f;
+    const float lam = a.lam ? a.lam[e] : 25.0f;
+    const float ib = 1.0f / beta, il = 1.0f / lam;
+    float wave_amax = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < NCBA; ++cb) {
+      const int n = cb * 16 + (lane & 15);
+      const bool valid = n < td.nrows;
+      const int64_t row = td.row_start + n;
+#pragma unroll
+      for (int p = 0; p < WRG / 2; ++p) {
+        float av[4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 h = acc[2 * p + q][cb];
+          av[2 * q] = situ(h[0] * al, h[1] * al, beta, ib, lam, il);
+          av[2 * q + 1] = situ(h[2] * al, h[3] * al, beta, ib, lam, il);
+        }
+        float m = fmaxf(fmaxf(fabsf(av[0]), fabsf(av[1])), fmaxf(fabsf(av[2]), fabsf(av[3])));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (valid) wave_amax = fmaxf(wave_amax, m);
+        float enc;
+        const uint32_t sb = nvfp4_block_scale(m, qa, &enc);
+        const uint32_t b0 = e2m1_encode(av[0] * enc) | (e2m1_encode(av[1] * enc) << 4);
+        const uint32_t b1 = e2m1_encode(av[2] * enc) | (e2m1_encode(av[3] * enc) << 4);
+        const int blk = (G0 >> 1) + p;
+        if (valid) {
+          uint8_t* ac = a.a_codes + row * (a.I / 2) + 8 * blk;
+          ac[g] = static_cast<uint8_t>(b0);
+          ac[4 + g] = static_cast<uint8_t>(b1);
+          if (g == 0) a.a_scales[row * (a.I / 16) + blk] = static_cast<uint8_t>(sb);
         }
       }
     }
-    __syncthreads();
-  }
-}
-
-template <int BN>
-__global__ __launch_bounds__(256) void fc1_kernel(LayerArgs a) {
-  const int tt = blockIdx.y;
-  if (tt >= *a.num_tiles) return;
-  const TileDesc td = a.tiles[tt];
-  const int e = td.expert;
-  __shared__ uint32_t s_codes[BN * kLdsStride];
-  __shared__ uint32_t s_scales[BN * 2];
-  __shared__ int64_t s_row[BN];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
-  if (tid < BN) {
-    const int r = min(tid, td.nrows - 1);
-    s_row[tid] = a.sorted_row_idx[td.row_start + r] / a.k;     // token of the routed row
-  }
-  __syncthreads();
-  const int nchunks = a.H / kChunk;
-  const int RG = 2 * a.I / 16;
-  const int G0 = blockIdx.x * 8 + 2 * w;
-  const int64_t slot = static_cast<int64_t>(e) * RG + G0;     // first of the wave's 2 groups
-  f32x4 acc[2][BN / 16];
+    for (int off = 32; off > 0; off >>= 1) wave_amax = fmaxf(wave_amax, __shfl_xor(wave_amax, off));
+    if (lane == 0 && wave_amax > 0.0f)
+      atomicMax(reinterpret_cast<unsigned int*>(a.a_amax + e), __float_as_uint(wave_amax));
+  } else {
+    const float al = a.alpha2[e];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < BN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ncb = (td.nrows + 15) / 16;
-  mainloop<BN>(reinterpret_cast<const uint4*>(a.w13_codes),
-               reinterpret_cast<const uint32_t*>(a.w13_scales), slot, nchunks, a.x_codes,
-               a.x_scales, a.H / 2, a.H / 16, a.H / 2, a.H / 16, s_row, s_codes, s_scales, ncb,
-               acc);
-  // Epilogue: lane holds rows 4g..4g+3 of each group = (gate i, up i, gate i+1, up i+1).
-  const float al = a.alpha1[e];
-  const float qa = a.qa[e];
-  const float beta = a.beta ? a.beta[e] : 4.0f;
-  const float lam = a.lam ? a.lam[e] : 25.0f;
-  const float ib = 1.0f / beta, il = 1.0f / lam;
-  const int blk = G0 >> 1;                       // NVFP4 group of 16 intermediates
-  float wave_amax = 0.0f;
-#pragma unroll
-  for (int cb = 0; cb < BN / 16; ++cb) {
-    if (cb >= ncb) break;
-    const int n = cb * 16 + (lane & 15);
-    const bool valid = n < td.nrows;
-    float av[4];
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      const f32x4 h = acc[rg][cb];
-      av[2 * rg] = situ(h[0] * al, h[1] * al, beta, ib, lam, il);
-      av[2 * rg + 1] = situ(h[2] * al, h[3] * al, beta, ib, lam, il);
-    }
-    float m = fmaxf(fmaxf(fabsf(av[0]), fabsf(av[1])), fmaxf(fabsf(av[2]), fabsf(av[3])));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (valid) wave_amax = fmaxf(wave_amax, m);
-    float enc;
-    const uint32_t sb = nvfp4_block_scale(m, qa, &enc);
-    const uint32_t b0 = e2m1_encode(av[0] * enc) | (e2m1_encode(av[1] * enc) << 4);
-    const uint32_t b1 = e2m1_encode(av[2] * enc) | (e2m1_encode(av[3] * enc) << 4);
-    if (valid) {
+    for (int cb = 0; cb < NCBA; ++cb) {
+      const int n = cb * 16 + (lane & 15);
+      if (n >= td.nrows) continue;
       const int64_t row = td.row_start + n;
-      uint8_t* ac = a.a_codes + row * (a.I / 2) + 8 * blk;
-      ac[g] = static_cast<uint8_t>(b0);
-      ac[4 + g] = static_cast<uint8_t>(b1);
-      if (g == 0) a.a_scales[row * (a.I / 16) + blk] = static_cast<uint8_t>(sb);
+#pragma unroll
+      for (int r = 0; r < WRG; ++r) {
+        const f32x4 o = acc[r][cb];
+        const int h0 = 16 * (G0 + r) + 4 * g;
+        uint2 v;
+        v.x = static_cast<uint32_t>(f32_to_bf16_rne(o[0] * al)) |
+              (static_cast<uint32_t>(f32_to_bf16_rne(o[1] * al)) << 16);
+        v.y = static_cast<uint32_t>(f32_to_bf16_rne(o[2] * al)) |
+              (static_cast<uint32_t>(f32_to_bf16_rne(o[3] * al)) << 16);
+        *reinterpret_cast<uint2*>(a.o_rows + row * a.H + h0) = v;
+      }
     }
   }
-  for (int off = 32; off > 0; off >>= 1) wave_amax = fmaxf(wave_amax, __shfl_xor(wave_amax, off));
-  if (lane == 0 && wave_amax > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(a.a_amax + e), __float_as_uint(wave_amax));
 }
 
-template <int BN>
-__global__ __launch_bounds__(256) void fc2_kernel(LayerArgs a) {
-  const int tt = blockIdx.y;
-  if (tt >= *a.num_tiles) return;
-  const TileDesc td = a.tiles[tt];
-  const int e = td.expert;
-  __shared__ uint32_t s_codes[BN * kLdsStride];
-  __shared__ uint32_t s_scales[BN * 2];
+template <int MODE, int NW, int WRG, int BN, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void grouped_gemm_kernel(LayerArgs a, int big) {
+  using C = GemmCfg<MODE, NW, WRG, BN>;
+  __shared__ _Float16 s_tok[2][BN * C::kLdsRow];
   __shared__ int64_t s_row[BN];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
-  if (tid < BN) s_row[tid] = td.row_start + min(tid, td.nrows - 1);
+
+  const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
+  const int ntiles = a.num_tiles[big];
+  const int rows_total = MODE == 0 ? 2 * a.I : a.H;
+  const int n_wt = rows_total / C::kWgRows;
+  int tt, wt;
+  map_workgroup(blockIdx.x, n_wt, &tt, &wt);
+  if (tt >= ntiles) return;
+  TileCtx t;
+  t.td = tiles[tt];
+  t.e = t.td.expert;
+  t.tid = threadIdx.x; t.lane = t.tid & 63; t.w = t.tid >> 6; t.g = t.lane >> 4;
+  if (t.tid < BN) {
+    const int r = t.td.row_start + min(t.tid, t.td.nrows - 1);
+    s_row[t.tid] = MODE == 0 ? static_cast<int64_t>(a.sorted_row_idx[r] / a.k) : r;
+  }
   __syncthreads();
-  const int nchunks = a.Ip / kChunk;
-  const int RG = a.H / 16;
-  const int G0 = blockIdx.x * 8 + 2 * w;
-  const int64_t slot = static_cast<int64_t>(e) * RG + G0;     // first of the wave's 2 groups
-  f32x4 acc[2][BN / 16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < BN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ncb = (td.nrows + 15) / 16;
-  mainloop<BN>(reinterpret_cast<const uint4*>(a.w2_codes),
-               reinterpret_cast<const uint32_t*>(a.w2_scales), slot, nchunks, a.a_codes,
-               a.a_scales, a.I / 2, a.I / 16, a.I / 2, a.I / 16, s_row, s_codes, s_scales, ncb,
-               acc);
-  const float al = a.alpha2[e];
-#pragma unroll
-  for (int cb = 0; cb < BN / 16; ++cb) {
-    if (cb >= ncb) break;
-    const int n = cb * 16 + (lane & 15);
-    if (n >= td.nrows) continue;
-    const int64_t row = td.row_start + n;
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      const f32x4 o = acc[rg][cb];
-      const int h0 = 16 * (G0 + rg) + 4 * g;
-      uint2 v;
-      v.x = static_cast<uint32_t>(f32_to_bf16_rne(o[0] * al)) |
-            (static_cast<uint32_t>(f32_to_bf16_rne(o[1] * al)) << 16);
-      v.y = static_cast<uint32_t>(f32_to_bf16_rne(o[2] * al)) |
-            (static_cast<uint32_t>(f32_to_bf16_rne(o[3] * al)) << 16);
-      *reinterpret_cast<uint2*>(a.o_rows + row * a.H + h0) = v;
+  const int K = MODE == 0 ? a.H : a.Ip;
+  t.nchunks = K / kChunk;
+  const int RG = rows_total / 16;
+  t.G0 = wt * (C::kWgRows / 16) + t.w * WRG;
+  t.slot0 = static_cast<int64_t>(t.e) * RG + t.G0;
+  t.wcodes = reinterpret_cast<const uint4*>(MODE == 0 ? a.w13_codes : a.w2_codes);
+  t.wscales = reinterpret_cast<const uint32_t*>(MODE == 0 ? a.w13_scales : a.w2_scales);
+  t.trow = t.tid / C::kThreadsPerRow;
+  t.tpart = t.tid % C::kThreadsPerRow;
+  const int64_t srow = s_row[t.trow];
+  t.trow_codes = (MODE == 0 ? a.x_codes : a.a_codes) + srow * (MODE == 0 ? a.H / 2 : a.I / 2);
+  t.trow_scales = (MODE == 0 ? a.x_scales : a.a_scales) + srow * (MODE == 0 ? a.H / 16 : a.I / 16);
+  t.valid_code_bytes = MODE == 0 ? a.H / 2 : a.I / 2;
+
+  // one instantiation per number of active 16-token column blocks, so the MFMA loops
+  // have compile-time trip counts (uniform branch per workgroup)
+  const int ncb = (t.td.nrows + 15) / 16;
+  if constexpr (BN == 32) {
+    if (ncb == 1) tile_body<MODE, NW, WRG, BN, 1>(a, t, s_tok);
+    else tile_body<MODE, NW, WRG, BN, 2>(a, t, s_tok);
+  } else {
+    switch (ncb) {
+      case 1: tile_body<MODE, NW, WRG, BN, 1>(a, t, s_tok); break;
+      case 2: tile_body<MODE, NW, WRG, BN, 2>(a, t, s_tok); break;
+      case 3: tile_body<MODE, NW, WRG, BN, 3>(a, t, s_tok); break;
+      case 4: tile_body<MODE, NW, WRG, BN, 4>(a, t, s_tok); break;
+      case 5: tile_body<MODE, NW, WRG, BN, 5>(a, t, s_tok); break;
+      case 6: tile_body<MODE, NW, WRG, BN, 6>(a, t, s_tok); break;
+      case 7: tile_body<MODE, NW, WRG, BN, 7>(a, t, s_tok); break;
+      default: tile_body<MODE, NW, WRG, BN, 8>(a, t, s_tok); break;
     }
   }
 }
@@ -241,17 +395,36 @@ __global__ __launch_bounds__(256) void finalize_kernel(LayerArgs a) {
   reinterpret_cast<uint4*>(a.out + t * a.H)[v] = o;
 }
 
-hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream) {
-  dim3 grid(2 * a.I / kWRows, static_cast<unsigned>(a.max_tiles));
-  fc1_kernel<kTokTile><<<grid, dim3(256), 0, stream>>>(a);
+
+// Variants: small tiles (up to 32 tokens) run 4 waves x 2 groups (128-row slabs); big
+// tiles (up to kBigRows tokens) run kBigNW waves x kBigWRG groups when the slab divides
+// the rows, else the 128-row slab.
+constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
+
+template <int MODE, int NW, int WRG, int BN, int WPE>
+static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipStream_t stream) {
+  using C = GemmCfg<MODE, NW, WRG, BN>;
+  const int rows_total = MODE == 0 ? 2 * a.I : a.H;
+  const int64_t grid = round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows),
+                                kXcds * kXcdRun);
+  if (grid > 0)
+    grouped_gemm_kernel<MODE, NW, WRG, BN, WPE>
+        <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
+}
+
+template <int MODE>
+static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
+  const int rows_total = MODE == 0 ? 2 * a.I : a.H;
+  launch_variant<MODE, 4, 2, kSmallRows, 1>(a, a.max_small, 0, stream);
+  if (rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
+    launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE>(a, a.max_big, 1, stream);
+  else
+    launch_variant<MODE, 4, 2, kBigRows, 1>(a, a.max_big, 1, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
-  dim3 grid(a.H / kWRows, static_cast<unsigned>(a.max_tiles));
-  fc2_kernel<kTokTile><<<grid, dim3(256), 0, stream>>>(a);
-  return hipGetLastError();
-}
+hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream) { return launch_gemm<0>(a, stream); }
+hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) { return launch_gemm<1>(a, stream); }
 
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(a.T) * (a.H / 8);

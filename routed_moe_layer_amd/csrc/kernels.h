@@ -20,16 +20,20 @@ struct TileDesc {
 // Router geometry: flat ids are processed in tiles of kRouteTile by workgroups of 256.
 constexpr int kRouteTile = 1024;
 constexpr int kRouteThreads = 256;
-// Tokens per grouped-GEMM tile (the N side of both FC kernels).
-constexpr int kTokTile = 64;
-// Weight rows per grouped-GEMM workgroup (the M side): 4 waves x 32 rows.
-constexpr int kWRows = 128;
+// Grouped-GEMM token tiles (the N side of both FC kernels).  An expert with at most
+// kSmallRows routed rows gets one "small" tile; a larger expert is split into
+// nb = ceil(cnt / kBigRows) "big" tiles of near-equal size (a multiple of 16 rows, the last
+// one shorter).  The two lists feed two variants of the GEMM kernels.
+constexpr int kSmallRows = 32;
+constexpr int kBigRows = 128;
 
 inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
 inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
-// Upper bound of the number of kTokTile tiles over all experts for R routed rows.
-inline int64_t max_token_tiles(int64_t R, int E) {
-  return R / kTokTile + (R < E ? R : E);
+// Upper bounds of the list lengths for R routed rows over E experts.
+inline int64_t max_small_tiles(int64_t R, int E) { return R < E ? R : E; }
+inline int64_t max_big_tiles(int64_t R, int E) {
+  const int64_t big_experts = R / (kSmallRows + 1);
+  return R / kBigRows + (big_experts < E ? big_experts : E);
 }
 
 hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
@@ -45,8 +49,9 @@ struct RouteBuffers {
   int32_t* sorted_ids;       // [n] (may be null)
   int32_t* sorted_row_idx;   // [n] (may be null)
   int32_t* expanded_row_idx; // [n]
-  TileDesc* tiles;           // [max_token_tiles] or null
-  int32_t* num_tiles;        // [1] or null
+  TileDesc* tiles_small;     // [max_small_tiles] or null
+  TileDesc* tiles_big;       // [max_big_tiles] or null
+  int32_t* num_tiles;        // [2]: small, big; or null
   float* amax_reset;         // [E] zeroed by the scan kernel, or null
 };
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
@@ -66,9 +71,10 @@ struct LayerArgs {
   const uint8_t* x_scales;     // [T, H/16]
   const int32_t* sorted_row_idx;
   const int32_t* expanded_row_idx;
-  const TileDesc* tiles;
-  const int32_t* num_tiles;
-  int64_t max_tiles;
+  const TileDesc* tiles_small;
+  const TileDesc* tiles_big;
+  const int32_t* num_tiles;    // [2]
+  int64_t max_small, max_big;
   const uint8_t* w13_codes;    // prepared
   const uint8_t* w13_scales;
   const uint8_t* w2_codes;

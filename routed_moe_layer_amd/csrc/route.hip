@@ -9,8 +9,8 @@
 // part in host dispatch):
 //   hist    : one workgroup per tile of 1024 flat ids; LDS histogram -> tile_hist[tile][e].
 //   scan    : one workgroup; per expert, exclusive scan of tile_hist over tiles (in place),
-//             counts, exclusive/inclusive expert offsets; optionally the grouped-GEMM work
-//             list (tiles of kTokTile rows per expert) and a reset of the SiTU amax stats.
+//             counts, exclusive/inclusive expert offsets; optionally the two grouped-GEMM
+//             work lists (small and big token tiles) and a reset of the SiTU amax stats.
 //   scatter : one workgroup per tile; each wave ranks its 256 ids stably with ballot-based
 //             key matching (one ballot per key bit), waves are ordered through an LDS
 //             per-wave histogram, and every id lands at
@@ -67,14 +67,27 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return wave_excl + incl - v;
 }
 
+// Token tiles of one expert with `cnt` rows: (number of tiles, rows per tile but the last).
+__device__ __forceinline__ void expert_tiles(int cnt, int* n_small, int* n_big, int* base) {
+  *n_small = 0; *n_big = 0; *base = 0;
+  if (cnt <= 0) return;
+  if (cnt <= kSmallRows) { *n_small = 1; *base = cnt; return; }
+  const int nb = (cnt + kBigRows - 1) / kBigRows;
+  const int b = min(kBigRows, ((cnt + nb - 1) / nb + 15) / 16 * 16);
+  *base = b;
+  *n_big = (cnt + b - 1) / b;
+}
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ tile_hist, int ntiles, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum, TileDesc* __restrict__ tiles,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum,
+    TileDesc* __restrict__ tiles_small, TileDesc* __restrict__ tiles_big,
     int32_t* __restrict__ num_tiles, float* __restrict__ amax_reset) {
   __shared__ int sh[16];
-  __shared__ int carry[2];
-  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; }
+  __shared__ int carry[3];
+  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
   __syncthreads();
+  const bool lists = tiles_small != nullptr;
   // Experts are handled in rounds of 1024 (E <= 4096).
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x;
@@ -89,34 +102,27 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
       counts[e] = cnt;
       if (amax_reset) amax_reset[e] = 0.0f;
     }
-    int total;
-    int excl = block_excl_scan(cnt, sh, &total);
-    int ntile_e = (cnt + kTokTile - 1) / kTokTile;
-    int ttotal;
-    int texcl = block_excl_scan(tiles ? ntile_e : 0, sh, &ttotal);
+    int n_small, n_big, base;
+    expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
+    int total, stotal, btotal;
+    const int excl = block_excl_scan(cnt, sh, &total);
+    const int sexcl = block_excl_scan(n_small, sh, &stotal);
+    const int bexcl = block_excl_scan(n_big, sh, &btotal);
     const int off = carry[0] + excl;
-    const int toff = carry[1] + texcl;
     if (e < E) {
       offsets[e] = off;
       if (cumsum) cumsum[e] = off + cnt;
-      if (tiles) {
-        for (int j = 0; j < ntile_e; ++j) {
-          TileDesc d;
-          d.expert = e;
-          d.row_start = off + j * kTokTile;
-          d.nrows = min(kTokTile, cnt - j * kTokTile);
-          d.pad = 0;
-          tiles[toff + j] = d;
-        }
-      }
+      if (n_small) tiles_small[carry[1] + sexcl] = TileDesc{e, off, cnt, 0};
+      for (int j = 0; j < n_big; ++j)
+        tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
     }
     __syncthreads();
-    if (threadIdx.x == 0) { carry[0] += total; carry[1] += ttotal; }
+    if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
     offsets[E] = carry[0];
-    if (num_tiles) *num_tiles = carry[1];
+    if (num_tiles) { num_tiles[0] = carry[1]; num_tiles[1] = carry[2]; }
   }
 }
 
@@ -184,7 +190,8 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
   route_hist_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
       ids, n, E, b.tile_hist);
   route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(
-      b.tile_hist, nt, E, b.counts, b.offsets, b.cumsum, b.tiles, b.num_tiles, b.amax_reset);
+      b.tile_hist, nt, E, b.counts, b.offsets, b.cumsum, b.tiles_small, b.tiles_big, b.num_tiles,
+      b.amax_reset);
   route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
                          (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
       ids, n, E, bits_for(E), b.tile_hist, b.offsets, b.sorted_ids, b.sorted_row_idx,

@@ -55,6 +55,26 @@ def test_quantize_nvfp4_bit_exact(groups, rows, K):
     assert np.array_equal(host(codes), oracle.pack_nibbles(want_c))
 
 
+def test_quantize_nvfp4_ties_and_neighbours_bit_exact():
+    """Blocks whose amax is 6 with q within 2^-20 of 1 get the scale 1.0 and an encode
+    factor equal to q, so v*enc lands exactly on every E2M1 tie (q = 1) or one to a few
+    fp32 ulps on either side of it."""
+    _say("quantize ties")
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0],
+                    np.float32)
+    row = np.concatenate([[6.0], ties, [0.0]]).astype(np.float32)
+    rows = np.stack([row, -row, row[::-1].copy()])
+    qs = np.array([1.0, 1 + 2 ** -20, 1 - 2 ** -20, 1 + 2 ** -23, 1 - 2 ** -24, 1 + 3 * 2 ** -23],
+                  np.float32)
+    bits = np.tile(f32_to_bf16_bits(rows), (len(qs), 1))
+    codes, scales = quantize_on_gpu(dev(bits), len(qs), rows.shape[0], 16, dev(qs))
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.quantize_nvfp4(oracle.bf16_bits_to_f32(bits), np.repeat(qs, 3))
+    assert np.all(want_s == 0x38)
+    assert np.array_equal(host(scales), want_s)
+    assert np.array_equal(host(codes), oracle.pack_nibbles(want_c))
+
+
 def _route_on_gpu(ids, E):
     n, K = ids.shape
     H = 8
