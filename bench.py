@@ -33,7 +33,7 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16/bf16 MFMA
 FC1_BYTES_PER_EXPERT = 768 * 1792 + 768 * 224          # codes + E4M3 scales
 FC2_BYTES_PER_EXPERT = 3584 * 192 + 3584 * 24
 STAGES = ("quantize_x", "route", "fc1_situ_requant", "fc2", "finalize")
-KERNEL_SOURCES = ("common.h", "kernels.h", "gemm.hip", "quant.hip", "route.hip", "api.hip")
+CSRC = os.path.join(ROOT, "routed_moe_layer_amd", "csrc")
 
 
 def log(msg):
@@ -72,9 +72,11 @@ class HipEvents:
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "routed_moe_layer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -27,6 +27,7 @@
 // row groups hold the gate/up pairs of 16 intermediate channels = one NVFP4 group) and the
 // per-expert amax statistic; the FC2 epilogue applies alpha2 and stores BF16 rows.
 #include "common.h"
+#include "gemm_util.h"
 #include "kernels.h"
 
 namespace rmoe {
@@ -63,77 +64,6 @@ struct GemmCfg {
   static constexpr int kDwPerThread = 16 / kThreadsPerRow;   // code dwords (of 16 per row)
   static_assert(kThreads % BN == 0 && 16 % kThreadsPerRow == 0, "token decode split");
 };
-
-// Loads, for chunk c, the code dwords and scale bytes one thread decodes.  Columns past
-// the row's real length read as zero codes with a zero scale.
-template <int NDW>
-__device__ __forceinline__ void load_token_chunk(const uint8_t* __restrict__ codes_row,
-                                                 const uint8_t* __restrict__ scales_row,
-                                                 int c, int part, int valid_code_bytes,
-                                                 uint32_t (&w)[NDW], uint32_t& sc) {
-  static_assert(NDW <= 2 || NDW % 4 == 0, "a thread decodes 1, 2 or a multiple of 4 dwords");
-  const int byte0 = c * 64 + part * NDW * 4;           // first code byte of this thread
-  if constexpr (NDW == 1) {
-    w[0] = byte0 < valid_code_bytes ? *reinterpret_cast<const uint32_t*>(codes_row + byte0) : 0u;
-  } else if constexpr (NDW == 2) {
-    if (byte0 < valid_code_bytes) {
-      const uint2 v = *reinterpret_cast<const uint2*>(codes_row + byte0);
-      w[0] = v.x; w[1] = v.y;
-    } else {
-      w[0] = 0; w[1] = 0;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NDW; i += 4) {
-      if (byte0 + 4 * i < valid_code_bytes) {
-        const uint4 v = *reinterpret_cast<const uint4*>(codes_row + byte0 + 4 * i);
-        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
-      } else {
-        w[i] = 0; w[i + 1] = 0; w[i + 2] = 0; w[i + 3] = 0;
-      }
-    }
-  }
-  // NDW dwords = 8*NDW codes = NDW/2 blocks; scale bytes of this thread
-  const int sbyte0 = byte0 / 8;
-  sc = 0;
-  if (byte0 < valid_code_bytes) {
-    if constexpr (NDW >= 8) {
-      sc = *reinterpret_cast<const uint32_t*>(scales_row + sbyte0);
-    } else {
-#pragma unroll
-      for (int b = 0; b < (NDW + 1) / 2; ++b)
-        sc |= static_cast<uint32_t>(scales_row[sbyte0 + b]) << (8 * b);
-    }
-  }
-}
-
-template <int NDW>
-__device__ __forceinline__ void store_token_chunk(_Float16* __restrict__ dst,
-                                                  const uint32_t (&w)[NDW], uint32_t sc) {
-#pragma unroll
-  for (int i = 0; i < NDW; ++i) {
-    const f16x8 v = decode8(w[i], scale_f16x2((sc >> (8 * (i >> 1))) & 0xFFu));
-    *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
-  }
-}
-
-// Workgroup -> (token tile, weight slab).  Workgroups are dealt to the 8 XCDs round-robin
-// by id; kXcdRun consecutive logical ids are kept on one XCD (and in flight together),
-// and logical ids run over kTileGroup consecutive token tiles of one slab before moving to
-// the next slab.  The token tiles of an expert are adjacent in the work list, so the
-// workgroups that read the same weight slab share that XCD's L2, and a group of token
-// tiles is reread across slabs while it is still cached.
-constexpr int kXcds = 8, kXcdRun = 4, kTileGroup = 4;
-
-__device__ __forceinline__ void map_workgroup(int b, int n_wt, int* tt, int* wt) {
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int L = ((slot / kXcdRun) * kXcds + xcd) * kXcdRun + slot % kXcdRun;
-  const int per_group = n_wt * kTileGroup;
-  *tt = (L / per_group) * kTileGroup + L % kTileGroup;
-  *wt = (L / kTileGroup) % n_wt;
-}
-
-inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Everything a workgroup needs once its tile is known.
 struct TileCtx {
@@ -367,24 +297,39 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 }
 
 // out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[expanded_row_idx[t*k + j], 8v..8v+7]), j in
-// order, fp32 fused multiply-add.  One thread per 8 outputs; 16-byte loads and stores.
-__global__ __launch_bounds__(256) void finalize_kernel(LayerArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int nv = a.H / 8;
-  if (idx >= static_cast<int64_t>(a.T) * nv) return;
-  const int64_t t = idx / nv;
-  const int v = static_cast<int>(idx % nv);
+// order, fp32 fused multiply-add.  A workgroup covers 8*kFinThreads columns of one token
+// (the token's row indices and weights are the same for the whole wave); each thread owns
+// 8 columns and issues the 16-byte loads of up to kFinBatch routed rows before it
+// accumulates them, so a wave keeps that many row reads in flight.
+constexpr int kFinThreads = 256, kFinBatch = 8;
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
+  const int64_t t = blockIdx.x / col_blocks;
+  const int v = (blockIdx.x % col_blocks) * kFinThreads + threadIdx.x;
+  if (v >= a.H / 8) return;
+  const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
+  const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) {
-    const float wt = bf16_to_f32(a.route_weights[t * a.k + j]);
-    const int64_t pos = a.expanded_row_idx[t * a.k + j];
-    if (pos < 0) continue;                      // dropped (expert id out of range)
-    const uint4 d = reinterpret_cast<const uint4*>(a.o_rows + pos * a.H)[v];
-    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
+    uint4 d[kFinBatch];
+    bool ok[kFinBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wt, __uint_as_float(dw[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wt, __uint_as_float(dw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    for (int u = 0; u < kFinBatch; ++u) {
+      const int j = j0 + u;
+      const int64_t pos = j < a.k ? pos_t[j] : -1;
+      ok[u] = pos >= 0;                         // < 0: dropped (expert id out of range)
+      d[u] = ok[u] ? reinterpret_cast<const uint4*>(a.o_rows + pos * a.H)[v] : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u) {
+      if (!ok[u]) continue;
+      const float wt = bf16_to_f32(w_t[j0 + u]);
+      const uint32_t dw[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wt, __uint_as_float(dw[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wt, __uint_as_float(dw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+      }
     }
   }
   uint4 o;
@@ -424,11 +369,26 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream) { return launch_gemm<0>(a, stream); }
-hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) { return launch_gemm<1>(a, stream); }
+constexpr int64_t kFc2ResidentBigMinRows = 2 * 256 * kBigRows;
+
+hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
+  if (!fc2_resident_fits(a)) return launch_gemm<1>(a, stream);
+  launch_fc2_resident_small(a, stream);
+  // The resident kernel gives each big tile one workgroup; below about two big tiles per
+  // CU that leaves the chip idle, and the grouped kernel (tiles x row slabs) is faster.
+  if (static_cast<int64_t>(a.T) * a.k >= kFc2ResidentBigMinRows) launch_fc2_resident_big(a, stream);
+  else if (a.H % GemmCfg<1, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
+    launch_variant<1, kBigNW, kBigWRG, kBigRows, kBigWPE>(a, a.max_big, 1, stream);
+  else
+    launch_variant<1, 4, 2, kBigRows, 1>(a, a.max_big, 1, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
-  const int64_t n = static_cast<int64_t>(a.T) * (a.H / 8);
-  finalize_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(a);
+  const int col_blocks = (a.H / 8 + kFinThreads - 1) / kFinThreads;
+  const int64_t grid = static_cast<int64_t>(a.T) * col_blocks;
+  if (grid > 0)
+    finalize_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kFinThreads), 0, stream>>>(a, col_blocks);
   return hipGetLastError();
 }
 

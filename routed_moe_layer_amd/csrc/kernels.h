@@ -93,6 +93,10 @@ struct LayerArgs {
 };
 hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream);
+// FC2 with the whole token tile resident in LDS (when the padded I fits; fc2.hip).
+bool fc2_resident_fits(const LayerArgs& a);
+void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream);
+void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream);
 
 // Prepared-weight layout (private).  For a matrix of R rows (multiple of 16) and K columns
