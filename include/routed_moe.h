@@ -76,6 +76,8 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  * intermediates that call leaves behind (for inspection and testing; the contents are
  * valid after the call completes and until the workspace is reused):
  *   x_codes   u8  [T, H/2]    NVFP4 codes of x           x_scales  u8  [T, H/16] E4M3
+ *   x_dec     f16 [T, H]      x's NVFP4 values before the global scale (code times block
+ *                             scale, exact in f16): the FC1 operand
  *   sorted_ids      i32 [T*k] expert of each sorted row  (keyValueSort keys)
  *   sorted_row_idx  i32 [T*k] flat id t*k+j of each sorted row
  *   expanded_row_idx i32 [T*k] gather map: sorted position of flat id f
@@ -86,7 +88,7 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
  *                             (0 for an expert with no rows; a calibration statistic) */
 typedef struct {
-  size_t x_codes, x_scales;
+  size_t x_codes, x_scales, x_dec;
   size_t sorted_ids, sorted_row_idx, expanded_row_idx;
   size_t expert_counts, expert_cumsum;
   size_t a_codes, a_scales;

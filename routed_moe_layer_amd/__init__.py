@@ -49,7 +49,7 @@ class MoeDims(ctypes.Structure):
 
 class _Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "x_codes", "x_scales", "sorted_ids", "sorted_row_idx", "expanded_row_idx",
+        "x_codes", "x_scales", "x_dec", "sorted_ids", "sorted_row_idx", "expanded_row_idx",
         "expert_counts", "expert_cumsum", "a_codes", "a_scales", "o_rows", "a_amax", "total")]
 
 

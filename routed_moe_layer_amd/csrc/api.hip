@@ -47,6 +47,7 @@ Layout make_layout(const moe_dims_t& d, int64_t T) {
   Layout L{};
   L.pub.x_codes = c.take(T * H / 2);
   L.pub.x_scales = c.take(T * H / 16);
+  L.pub.x_dec = c.take(T * H * 2);
   L.pub.sorted_ids = c.take(R * 4);
   L.pub.sorted_row_idx = c.take(R * 4);
   L.pub.expanded_row_idx = c.take(R * 4);
@@ -136,7 +137,7 @@ moe_status_t moe_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t row
   if (groups < 1 || rows_per_group < 1 || K < 16 || K % 16 || K > 65536)
     return MOE_ERR_INVALID_ARG;
   if (!aligned(src, 16) || !aligned(codes, 8) || !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_quantize_nvfp4(src, groups, rows_per_group, K, q, codes, scales,
+  return hip_status(launch_quantize_nvfp4(src, groups, rows_per_group, K, q, codes, scales, nullptr,
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -218,6 +219,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   a.H = H; a.I = I; a.Ip = padded_inter(I); a.E = E; a.k = k; a.T = T;
   a.x_codes = ws + L.pub.x_codes;
   a.x_scales = ws + L.pub.x_scales;
+  a.x_dec = reinterpret_cast<const uint16_t*>(ws + L.pub.x_dec);
   int32_t* sorted_ids = reinterpret_cast<int32_t*>(ws + L.pub.sorted_ids);
   int32_t* sorted_row_idx = reinterpret_cast<int32_t*>(ws + L.pub.sorted_row_idx);
   int32_t* expanded_row_idx = reinterpret_cast<int32_t*>(ws + L.pub.expanded_row_idx);
@@ -247,7 +249,8 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
            hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  hipError_t e = launch_quantize_nvfp4(x, 1, T, H, qx, ws + L.pub.x_codes, ws + L.pub.x_scales, s);
+  hipError_t e = launch_quantize_nvfp4(x, 1, T, H, qx, ws + L.pub.x_codes, ws + L.pub.x_scales,
+                                     reinterpret_cast<uint16_t*>(ws + L.pub.x_dec), s);
   if (e != hipSuccess || !mark(1)) return MOE_ERR_HIP;
   RouteBuffers b{};
   b.tile_hist = reinterpret_cast<int32_t*>(ws + L.tile_hist);

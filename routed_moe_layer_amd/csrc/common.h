@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kGroup = 16;          // NVFP4 block length
@@ -31,6 +32,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as packed BF16 (lo in bits 0..15), rounded to nearest even by the
+// hardware conversion (same result as f32_to_bf16_rne for finite values).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // E4M3 byte of a non-negative finite fp32 scale: clamp to 448, then round to nearest even.

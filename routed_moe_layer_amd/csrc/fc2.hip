@@ -10,6 +10,8 @@
 // weight slabs over it: no further barriers, the weight fragments of the next (slab,
 // chunk) stream into registers two steps ahead, and each slab's BF16 rows are stored as
 // soon as its K loop ends.  Each wave owns WRG 16-row MFMA groups of every slab.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_util.h"
 #include "kernels.h"
@@ -25,41 +27,40 @@ struct W2Regs {
   uint32_t s[WRG];
 };
 
-template <int NW, int WRG, int BN, int NCBA>
-__device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
-                                         int nslabs, const _Float16* __restrict__ s_tok) {
-  constexpr int kSlabGroups = NW * WRG;         // 16-row groups per slab
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
-  const int e = td.expert;
-  const int nchunks = a.Ip / kChunk;
-  const int RG = a.H / 16;
-  const int total = nslabs * nchunks;
+// A wave's weight fragments of (slab j, chunk c): WRG 16-row groups x 16 code bytes and
+// one scale dword per lane.
+template <int NW, int WRG>
+__device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int lane, int j,
+                                         int c, int nchunks, W2Regs<WRG>& dst) {
+  constexpr int kSlabGroups = NW * WRG;
   const uint4* __restrict__ wcodes = reinterpret_cast<const uint4*>(a.w2_codes);
   const uint32_t* __restrict__ wscales = reinterpret_cast<const uint32_t*>(a.w2_scales);
-
-  auto load = [&](int q, W2Regs<WRG>& dst) {
-    const int j = slab0 + q / nchunks, c = q % nchunks;
-    const int64_t slot = static_cast<int64_t>(e) * RG + j * kSlabGroups + w * WRG;
+  const int64_t slot = static_cast<int64_t>(e) * (a.H / 16) + j * kSlabGroups + w * WRG;
 #pragma unroll
-    for (int r = 0; r < WRG; ++r) {
-      dst.c[r] = wcodes[((slot + r) * nchunks + c) * 64 + lane];
-      dst.s[r] = wscales[prepared_scale_index(slot + r, nchunks, c, lane)];
-    }
-  };
+  for (int r = 0; r < WRG; ++r) {
+    dst.c[r] = wcodes[((slot + r) * nchunks + c) * 64 + lane];
+    dst.s[r] = wscales[prepared_scale_index(slot + r, nchunks, c, lane)];
+  }
+}
 
-  f32x4 acc[WRG][NCBA];
-#pragma unroll
-  for (int i = 0; i < WRG; ++i)
-#pragma unroll
-    for (int j = 0; j < NCBA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // One (slab, chunk) step q: decode the fragments in `cur` (freeing it), reload `cur`
-  // with step q + 2, run the MFMAs, and store the slab's rows after its last chunk.
-  // Two register sets alternate by the parity of q, so every load lands in the set that
-  // is decoded two steps later (no register copies of in-flight loads).
+// The slabs [slab0, slab0 + nslabs) of one token tile; NCH = Ip/128 chunks per slab.
+// Steps q = (slab, chunk) run in order; step q decodes its register set, refills it with
+// step q+2 (two sets alternate, so no register copies of in-flight loads), runs the MFMAs
+// over the LDS-resident token tile and, after a slab's last chunk, stores the slab's BF16
+// rows.  Two slabs per loop trip keep the chunk index, the register set and the epilogue
+// compile-time; a slab's first K-step starts from a zero accumulator.
+template <int NW, int WRG, int BN, int NCBA, int NCH>
+__device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
+                                         int nslabs, const _Float16* __restrict__ s_tok) {
+  constexpr int kSlabGroups = NW * WRG;                 // 16-row groups per slab
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+  const int e = td.expert;
+  const int last = slab0 + nslabs - 1;
   const float al = a.alpha2[e];
-  auto step = [&](int q, W2Regs<WRG>& cur) {
-    const int c = q % nchunks;
+  const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
+  f32x4 acc[WRG][NCBA];
+
+  auto step = [&](const int j, const int c, W2Regs<WRG>& cur) {
     f16x8 wf[4][WRG];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -68,35 +69,36 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
         const uint32_t cw = s == 0 ? cur.c[r].x : s == 1 ? cur.c[r].y : s == 2 ? cur.c[r].z : cur.c[r].w;
         wf[s][r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
       }
-    if (q + 2 < total) load(q + 2, cur);
+    // refill with step q+2 (slab clamped: surplus loads past the last slab are unused and
+    // unconditional, so the compiler's load counters stay exact)
+    fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const f16x8 xf = *reinterpret_cast<const f16x8*>(
-            s_tok + (cb * 16 + (lane & 15)) * kFc2LdsRow + c * kChunk + 32 * s + 8 * g);
+        const f16x8 xf =
+            *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(wf[s][r], xf, acc[r][cb]);
+        for (int r = 0; r < WRG; ++r)
+          acc[r][cb] = mfma16x16x32(wf[s][r], xf,
+                                    (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
       }
-    if (c == nchunks - 1) {
-      const int j = slab0 + q / nchunks;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c == NCH - 1) {
       const int G0 = j * kSlabGroups + w * WRG;
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
         const int n = cb * 16 + (lane & 15);
-        const int64_t row = td.row_start + n;
+        if (n < td.nrows) {
+          uint16_t* orow = a.o_rows + (td.row_start + n) * a.H + 4 * g;
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) {
-          const f32x4 o = acc[r][cb];
-          acc[r][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (n < td.nrows) {
-            const int h0 = 16 * (G0 + r) + 4 * g;
+          for (int r = 0; r < WRG; ++r) {
+            const f32x4 o = acc[r][cb];
             uint2 v;
-            v.x = static_cast<uint32_t>(f32_to_bf16_rne(o[0] * al)) |
-                  (static_cast<uint32_t>(f32_to_bf16_rne(o[1] * al)) << 16);
-            v.y = static_cast<uint32_t>(f32_to_bf16_rne(o[2] * al)) |
-                  (static_cast<uint32_t>(f32_to_bf16_rne(o[3] * al)) << 16);
-            *reinterpret_cast<uint2*>(a.o_rows + row * a.H + h0) = v;
+            v.x = pack_bf16x2(o[0] * al, o[1] * al);
+            v.y = pack_bf16x2(o[2] * al, o[3] * al);
+            *reinterpret_cast<uint2*>(orow + 16 * (G0 + r)) = v;
           }
         }
       }
@@ -104,14 +106,17 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   };
 
   W2Regs<WRG> setA, setB;
-  load(0, setA);
-  if (total > 1) load(1, setB);
-  int q = 0;
-  for (; q + 1 < total; q += 2) {
-    step(q, setA);
-    step(q + 1, setB);
+  fc2_load<NW, WRG>(a, e, w, lane, slab0, 0, NCH, setA);
+  fc2_load<NW, WRG>(a, e, w, lane, min(slab0 + 1 / NCH, last), 1 % NCH, NCH, setB);
+  int j = slab0;
+  for (; j + 1 <= last; j += 2) {
+#pragma unroll
+    for (int q = 0; q < 2 * NCH; ++q) step(j + q / NCH, q % NCH, (q & 1) ? setB : setA);
   }
-  if (q < total) step(q, setA);
+  if (j == last) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) step(j, q, (q & 1) ? setB : setA);
+  }
 }
 
 // grid: (token tile, slab group) pairs; slab group = SPW consecutive slabs.
@@ -146,19 +151,29 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   __syncthreads();
   const int slab0 = grp * SPW;
   const int nslabs = min(SPW, n_slabs - slab0);
+  // compile-time token blocks (uniform branch per workgroup) and chunks per slab
+  auto run = [&](auto ncba) {
+    constexpr int NCBA = decltype(ncba)::value;
+    switch (a.Ip / kChunk) {
+      case 1: fc2_tile<NW, WRG, BN, NCBA, 1>(a, td, slab0, nslabs, s_tok); break;
+      case 2: fc2_tile<NW, WRG, BN, NCBA, 2>(a, td, slab0, nslabs, s_tok); break;
+      default: fc2_tile<NW, WRG, BN, NCBA, 3>(a, td, slab0, nslabs, s_tok); break;
+    }
+  };
+  using std::integral_constant;
   if constexpr (BN == 32) {
-    if (ncb == 1) fc2_tile<NW, WRG, BN, 1>(a, td, slab0, nslabs, s_tok);
-    else fc2_tile<NW, WRG, BN, 2>(a, td, slab0, nslabs, s_tok);
+    if (ncb == 1) run(integral_constant<int, 1>{});
+    else run(integral_constant<int, 2>{});
   } else {
     switch (ncb) {
-      case 1: fc2_tile<NW, WRG, BN, 1>(a, td, slab0, nslabs, s_tok); break;
-      case 2: fc2_tile<NW, WRG, BN, 2>(a, td, slab0, nslabs, s_tok); break;
-      case 3: fc2_tile<NW, WRG, BN, 3>(a, td, slab0, nslabs, s_tok); break;
-      case 4: fc2_tile<NW, WRG, BN, 4>(a, td, slab0, nslabs, s_tok); break;
-      case 5: fc2_tile<NW, WRG, BN, 5>(a, td, slab0, nslabs, s_tok); break;
-      case 6: fc2_tile<NW, WRG, BN, 6>(a, td, slab0, nslabs, s_tok); break;
-      case 7: fc2_tile<NW, WRG, BN, 7>(a, td, slab0, nslabs, s_tok); break;
-      default: fc2_tile<NW, WRG, BN, 8>(a, td, slab0, nslabs, s_tok); break;
+      case 1: run(integral_constant<int, 1>{}); break;
+      case 2: run(integral_constant<int, 2>{}); break;
+      case 3: run(integral_constant<int, 3>{}); break;
+      case 4: run(integral_constant<int, 4>{}); break;
+      case 5: run(integral_constant<int, 5>{}); break;
+      case 6: run(integral_constant<int, 6>{}); break;
+      case 7: run(integral_constant<int, 7>{}); break;
+      default: run(integral_constant<int, 8>{}); break;
     }
   }
 }

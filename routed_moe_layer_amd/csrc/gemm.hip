@@ -26,6 +26,8 @@
 // The FC1 epilogue fuses alpha1, SiTU, the group-16 requantization (two consecutive MFMA
 // row groups hold the gate/up pairs of 16 intermediate channels = one NVFP4 group) and the
 // per-expert amax statistic; the FC2 epilogue applies alpha2 and stores BF16 rows.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_util.h"
 #include "kernels.h"
@@ -59,23 +61,17 @@ struct GemmCfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int kNcb = BN / 16;                 // 16-token MFMA column blocks
   static constexpr int kWgRows = NW * WRG * 16;        // weight rows per workgroup
-  static constexpr int kLdsRow = kChunk + 8;           // f16 per staged token row (+16 B pad)
-  static constexpr int kThreadsPerRow = kThreads / BN; // token-decode threads per row
-  static constexpr int kDwPerThread = 16 / kThreadsPerRow;   // code dwords (of 16 per row)
-  static_assert(kThreads % BN == 0 && 16 % kThreadsPerRow == 0, "token decode split");
 };
 
-// Everything a workgroup needs once its tile is known.
+// Everything a workgroup needs once its tile is known.  The expert's prepared codes and
+// scales are addressed through buffer resources: a load's offset is a wave-uniform part
+// (row group, chunk) in a scalar register plus a fixed per-lane part.
 struct TileCtx {
   TileDesc td;
   int e, tid, lane, w, g;
   int nchunks, G0;
-  int64_t slot0;
-  const uint4* wcodes;
-  const uint32_t* wscales;
-  const uint8_t* trow_codes;
-  const uint8_t* trow_scales;
-  int trow, tpart, valid_code_bytes;
+  __amdgpu_buffer_rsrc_t wcodes, wscales;   // this expert's prepared codes / scales
+  uint32_t lane_code_off, lane_scale_off;
 };
 
 template <int WRG>
@@ -83,67 +79,225 @@ __device__ __forceinline__ void load_weights(const TileCtx& t, int c, uint4 (&wc
                                              uint32_t (&ws)[WRG]) {
 #pragma unroll
   for (int r = 0; r < WRG; ++r) {
-    wc[r] = t.wcodes[((t.slot0 + r) * t.nchunks + c) * 64 + t.lane];
-    ws[r] = t.wscales[prepared_scale_index(t.slot0 + r, t.nchunks, c, t.lane)];
+    const uint32_t chunk = static_cast<uint32_t>((t.G0 + r) * t.nchunks + c);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(t.wcodes, t.lane_code_off,
+                                                          chunk * 1024u, 0);
+    wc[r] = uint4{v[0], v[1], v[2], v[3]};
+    ws[r] = __builtin_amdgcn_raw_buffer_load_b32(t.wscales, t.lane_scale_off, chunk * 128u, 0);
   }
 }
 
-// Raw token codes and scale bytes of one chunk for one decoding thread.
-template <int NDW>
-struct TokRegs {
-  uint32_t w[NDW];
-  uint32_t sc;
+// ---------------------------------------------------------------------------------------
+// Token-tile staging: how a 128-column chunk of the tile's token rows gets from memory
+// into an LDS buffer of f16 MFMA operands.  `load` fills registers (issued two chunks
+// ahead), `store` writes them into a buffer, `frag` addresses a lane's operand: the 8
+// values k = 32s + 8(lane/16) .. +7 of tile row 16cb + lane%16.  Only the first ROWS
+// rows (a multiple of 16) are staged.
+
+// FC1: the rows of x_dec (x's NVFP4 values in f16, written by the quantizer), moved as
+// 16-byte pieces.  One load instruction of a wave covers 4 rows x 256 bytes (lane:
+// row r0 + lane/16, piece lane%16), so each row is read as one contiguous 256-byte
+// segment.  LDS rows are 128 f16 without padding; piece j of row r sits in slot
+// j ^ (r % 16), so the 16 rows of an operand read hit 16 different slots.
+template <int NW, int BN>
+struct RowStage {
+  static constexpr int kPieces = BN / (4 * NW);        // 16-byte pieces per thread
+  static constexpr int kLdsRow = kChunk;
+  static_assert(BN % (4 * NW) == 0, "row staging split");
+  struct Regs { u32x4 v[kPieces]; };
+  const uint16_t* src;
+  int32_t off[kPieces];                                // element offset in chunk 0
+  int lds0, w;
+
+  __device__ __forceinline__ void init(const LayerArgs& a, const int64_t* s_row, int wave,
+                                       int lane) {
+    src = a.x_dec;
+    w = wave;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int r = (i * NW + wave) * 4 + (lane >> 4);
+      const int j = (lane & 15) ^ (r & 15);
+      off[i] = static_cast<int32_t>(s_row[r] * a.H) + 8 * j;
+    }
+    lds0 = (wave * 4 + (lane >> 4)) * kLdsRow + 8 * (lane & 15);
+  }
+  // piece i of this wave lies in the first ROWS rows (decided at compile time unless the
+  // staged rows end inside piece i's group of NW waves)
+  template <int ROWS>
+  __device__ __forceinline__ bool covers(int i) const {
+    return (i + 1) * NW * 4 <= ROWS || (i * NW * 4 < ROWS && (i * NW + w) * 4 < ROWS);
+  }
+  template <int ROWS>
+  __device__ __forceinline__ void load(int c, Regs& R) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      if (covers<ROWS>(i))
+        R.v[i] = *reinterpret_cast<const u32x4*>(src + off[i] + c * kChunk);
+  }
+  template <int ROWS>
+  __device__ __forceinline__ void store(_Float16* buf, const Regs& R) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      if (covers<ROWS>(i))
+        *reinterpret_cast<u32x4*>(buf + lds0 + i * NW * 4 * kLdsRow) = R.v[i];
+  }
+  static __device__ __forceinline__ const _Float16* frag(const _Float16* buf, int cb, int s,
+                                                         int lane) {
+    return buf + (cb * 16 + (lane & 15)) * kLdsRow + 8 * ((4 * s + (lane >> 4)) ^ (lane & 15));
+  }
 };
 
-// One 128-column chunk c.  Register pipelines run two chunks ahead: on entry `wc/ws` hold
-// chunk c's raw weights and `tnext` chunk c+1's raw token codes; `tfree` is free.
+// NVFP4 codes (x for FC1, the requantized SiTU rows for FC2), decoded to f16 on the way
+// into LDS.  Each row's 64 code bytes per chunk are split over NW*64/BN threads (kNdw
+// dwords each, read through buffer resources); columns past the row's real length (FC2's
+// padded I) read as zero codes with a zero scale.  LDS rows are padded by 16 bytes.
+template <int MODE, int NW, int BN>
+struct CodeStage {
+  static constexpr int kThreadsPerRow = NW * 64 / BN;
+  static constexpr int kNdw = 16 / kThreadsPerRow;     // code dwords (of 16 per row)
+  static constexpr int kLdsRow = kChunk + 8;
+  static_assert((NW * 64) % BN == 0 && 16 % kThreadsPerRow == 0, "code staging split");
+  static_assert(kNdw == 2 || kNdw == 4 || kNdw == 8, "code staging width");
+  struct Regs { uint32_t w[kNdw]; uint32_t sc; };
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t code_off, scale_off;                        // this thread's bytes in chunk 0
+  int trow, part_byte, valid_code_bytes;
+
+  __device__ __forceinline__ void init(const LayerArgs& a, const int64_t* s_row, int wave,
+                                       int lane) {
+    const int tid = wave * 64 + lane;
+    trow = tid / kThreadsPerRow;
+    part_byte = (tid % kThreadsPerRow) * kNdw * 4;
+    const int K = MODE == 0 ? a.H : a.I;
+    const int64_t nrows = MODE == 0 ? a.T : static_cast<int64_t>(a.T) * a.k;
+    codes = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(MODE == 0 ? a.x_codes : a.a_codes), 0,
+        static_cast<int>(nrows * (K / 2)), kBufferFlags);
+    scales = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(MODE == 0 ? a.x_scales : a.a_scales), 0,
+        static_cast<int>(nrows * (K / 16)), kBufferFlags);
+    code_off = static_cast<uint32_t>(s_row[trow] * (K / 2) + part_byte);
+    scale_off = static_cast<uint32_t>(s_row[trow] * (K / 16) + part_byte / 8);
+    valid_code_bytes = K / 2;
+  }
+  template <int ROWS>
+  __device__ __forceinline__ void load(int c, Regs& R) const {
+    if (trow >= ROWS) return;
+    if (c * 64 + part_byte < valid_code_bytes) {
+      const uint32_t co = code_off + 64u * c, so = scale_off + 8u * c;
+#pragma unroll
+      for (int i = 0; i < kNdw; i += (kNdw >= 4 ? 4 : 2)) {
+        if constexpr (kNdw >= 4) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(codes, co + 4 * i, 0, 0);
+          R.w[i] = v[0]; R.w[i + 1] = v[1]; R.w[i + 2] = v[2]; R.w[i + 3] = v[3];
+        } else {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(codes, co + 4 * i, 0, 0);
+          R.w[i] = v[0]; R.w[i + 1] = v[1];
+        }
+      }
+      // kNdw dwords = kNdw/2 blocks = kNdw/2 scale bytes
+      if constexpr (kNdw == 8) R.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, so, 0, 0);
+      else if constexpr (kNdw == 4) R.sc = __builtin_amdgcn_raw_buffer_load_b16(scales, so, 0, 0);
+      else R.sc = __builtin_amdgcn_raw_buffer_load_b8(scales, so, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kNdw; ++i) R.w[i] = 0;
+      R.sc = 0;
+    }
+  }
+  template <int ROWS>
+  __device__ __forceinline__ void store(_Float16* buf, const Regs& R) const {
+    if (trow >= ROWS) return;
+    _Float16* dst = buf + trow * kLdsRow + part_byte * 2;
+#pragma unroll
+    for (int i = 0; i < kNdw; ++i) {
+      const f16x8 v = decode8(R.w[i], scale_f16x2((R.sc >> (8 * (i >> 1))) & 0xFFu));
+      *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
+    }
+  }
+  static __device__ __forceinline__ const _Float16* frag(const _Float16* buf, int cb, int s,
+                                                         int lane) {
+    return buf + (cb * 16 + (lane & 15)) * kLdsRow + 32 * s + 8 * (lane >> 4);
+  }
+};
+
+// Staging of a variant: f16 rows (ROWS true, FC1 only) or NVFP4 codes.
+template <int MODE, int NW, int BN, bool ROWS>
+using StageOf = typename std::conditional<ROWS, RowStage<NW, BN>, CodeStage<MODE, NW, BN>>::type;
+
+// One 128-column chunk c.  Weights run two chunks ahead in registers (on entry `wc/ws`
+// hold chunk c's raw weights), tokens one chunk ahead through `tr`:
 //   1. decode chunk c's weight fragments (frees wc/ws),
-//   2. issue the loads of chunk c+2 (weights into wc/ws, token codes into tfree),
+//   2. issue the loads of chunk c+2's weights (into wc/ws) and chunk c+1's tokens (tr),
 //   3. wait for the LDS buffer of chunk c,
 //   4. run the MFMAs,
-//   5. decode chunk c+1's token codes into the other LDS buffer.
-template <int WRG, int NCBA, int NDW, int LROW>
-__device__ __forceinline__ void chunk_step(const TileCtx& t, int c, uint4 (&wc)[WRG],
-                                           uint32_t (&ws)[WRG], TokRegs<NDW>& tfree,
-                                           const TokRegs<NDW>& tnext, const _Float16* tb_cur,
+//   5. store chunk c+1's tokens into the other LDS buffer.
+//
+// With WRG == 4 the weight fragments are decoded one 32-column K-step at a time (16
+// instead of 64 registers of decoded operands), and the weight loads of chunk c+2 are
+// issued after the last step's decode.
+template <int WRG, int NCBA, class Stage>
+__device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, int c,
+                                           uint4 (&wc)[WRG], uint32_t (&ws)[WRG],
+                                           typename Stage::Regs& tr, const _Float16* tb_cur,
                                            _Float16* tb_next, f32x4 (&acc)[WRG][NCBA]) {
-  const bool tactive = t.trow < 16 * NCBA;
-  f16x8 wf[4][WRG];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
+  constexpr bool kPerStep = WRG >= 4;
+  auto decode_step = [&](int s, f16x8 (&dst)[WRG]) {
 #pragma unroll
     for (int r = 0; r < WRG; ++r) {
       const uint32_t cw = s == 0 ? wc[r].x : s == 1 ? wc[r].y : s == 2 ? wc[r].z : wc[r].w;
-      wf[s][r] = decode8(cw, scale_f16x2((ws[r] >> (8 * s)) & 0xFFu));
+      dst[r] = decode8(cw, scale_f16x2((ws[r] >> (8 * s)) & 0xFFu));
     }
-  if (c + 2 < t.nchunks) {
-    load_weights<WRG>(t, c + 2, wc, ws);
-    if (tactive)
-      load_token_chunk<NDW>(t.trow_codes, t.trow_scales, c + 2, t.tpart, t.valid_code_bytes,
-                            tfree.w, tfree.sc);
+  };
+  if constexpr (kPerStep) {
+    const bool more = c + 1 < t.nchunks;
+    st.template load<16 * NCBA>(min(c + 1, t.nchunks - 1), tr);
+    __syncthreads();                                    // LDS buffer of chunk c complete
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 wf[WRG];
+      decode_step(s, wf);
+      if (s == 3) load_weights<WRG>(t, min(c + 2, t.nchunks - 1), wc, ws);
+#pragma unroll
+      for (int cb = 0; cb < NCBA; ++cb) {
+        const f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, cb, s, t.lane));
+#pragma unroll
+        for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(wf[r], xf, acc[r][cb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) st.template store<16 * NCBA>(tb_next, tr);
+    return;
   }
+  f16x8 wf[4][WRG];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) decode_step(s, wf[s]);
+  // Token loads first, so the wait before their LDS store (end of this step) leaves the
+  // younger weight loads in flight.  Both are issued unconditionally (chunk index clamped,
+  // the surplus loads are never used): with no branch around them the compiler's wait
+  // counts stay exact instead of draining every outstanding load.
+  const bool more = c + 1 < t.nchunks;
+  st.template load<16 * NCBA>(min(c + 1, t.nchunks - 1), tr);
+  load_weights<WRG>(t, min(c + 2, t.nchunks - 1), wc, ws);
   __syncthreads();                                      // LDS buffer of chunk c complete
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int cb = 0; cb < NCBA; ++cb) {
-      const f16x8 xf = *reinterpret_cast<const f16x8*>(
-          tb_cur + (cb * 16 + (t.lane & 15)) * LROW + 32 * s + 8 * t.g);
+      const f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, cb, s, t.lane));
 #pragma unroll
       for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(wf[s][r], xf, acc[r][cb]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (c + 1 < t.nchunks && tactive)
-    store_token_chunk<NDW>(tb_next + t.trow * LROW + t.tpart * NDW * 8, tnext.w, tnext.sc);
+  if (more) st.template store<16 * NCBA>(tb_next, tr);
 }
 
-template <int MODE, int NW, int WRG, int BN, int NCBA>
+template <int MODE, int NW, int WRG, int BN, bool ROWS, int NCBA>
 __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
-                                          _Float16 (*s_tok)[BN * GemmCfg<MODE, NW, WRG, BN>::kLdsRow]) {
-  using C = GemmCfg<MODE, NW, WRG, BN>;
-  constexpr int NDW = C::kDwPerThread;
-  constexpr int LROW = C::kLdsRow;
+                                          const StageOf<MODE, NW, BN, ROWS>& st,
+                                          _Float16 (*s_tok)[BN * StageOf<MODE, NW, BN, ROWS>::kLdsRow]) {
+  using Stage = StageOf<MODE, NW, BN, ROWS>;
   f32x4 acc[WRG][NCBA];
 #pragma unroll
   for (int i = 0; i < WRG; ++i)
@@ -152,25 +306,20 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
 
   uint4 wcA[WRG], wcB[WRG];
   uint32_t wsA[WRG], wsB[WRG];
-  TokRegs<NDW> tA, tB;
-  const bool tactive = t.trow < 16 * NCBA;
+  typename Stage::Regs tr;
   load_weights<WRG>(t, 0, wcA, wsA);
   if (t.nchunks > 1) load_weights<WRG>(t, 1, wcB, wsB);
-  if (tactive) {
-    load_token_chunk<NDW>(t.trow_codes, t.trow_scales, 0, t.tpart, t.valid_code_bytes, tA.w, tA.sc);
-    store_token_chunk<NDW>(s_tok[0] + t.trow * LROW + t.tpart * NDW * 8, tA.w, tA.sc);
-    if (t.nchunks > 1)
-      load_token_chunk<NDW>(t.trow_codes, t.trow_scales, 1, t.tpart, t.valid_code_bytes, tB.w, tB.sc);
-  }
+  st.template load<16 * NCBA>(0, tr);
+  st.template store<16 * NCBA>(s_tok[0], tr);
   // two chunks per trip so register sets and LDS buffers are named statically; an odd
   // last chunk is peeled after the loop (no conditional MFMA block inside the loop)
   int c = 0;
   for (; c + 1 < t.nchunks; c += 2) {
-    chunk_step<WRG, NCBA, NDW, LROW>(t, c, wcA, wsA, tA, tB, s_tok[0], s_tok[1], acc);
-    chunk_step<WRG, NCBA, NDW, LROW>(t, c + 1, wcB, wsB, tB, tA, s_tok[1], s_tok[0], acc);
+    chunk_step<WRG, NCBA>(t, st, c, wcA, wsA, tr, s_tok[0], s_tok[1], acc);
+    chunk_step<WRG, NCBA>(t, st, c + 1, wcB, wsB, tr, s_tok[1], s_tok[0], acc);
   }
   if (c < t.nchunks)
-    chunk_step<WRG, NCBA, NDW, LROW>(t, c, wcA, wsA, tA, tB, s_tok[0], s_tok[1], acc);
+    chunk_step<WRG, NCBA>(t, st, c, wcA, wsA, tr, s_tok[0], s_tok[1], acc);
 
   const TileDesc td = t.td;
   const int e = t.e, lane = t.lane, g = t.g, G0 = t.G0;
@@ -229,21 +378,20 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
         const f32x4 o = acc[r][cb];
         const int h0 = 16 * (G0 + r) + 4 * g;
         uint2 v;
-        v.x = static_cast<uint32_t>(f32_to_bf16_rne(o[0] * al)) |
-              (static_cast<uint32_t>(f32_to_bf16_rne(o[1] * al)) << 16);
-        v.y = static_cast<uint32_t>(f32_to_bf16_rne(o[2] * al)) |
-              (static_cast<uint32_t>(f32_to_bf16_rne(o[3] * al)) << 16);
+        v.x = pack_bf16x2(o[0] * al, o[1] * al);
+        v.y = pack_bf16x2(o[2] * al, o[3] * al);
         *reinterpret_cast<uint2*>(a.o_rows + row * a.H + h0) = v;
       }
     }
   }
 }
 
-template <int MODE, int NW, int WRG, int BN, int WPE>
+template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void grouped_gemm_kernel(LayerArgs a, int big) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
-  __shared__ _Float16 s_tok[2][BN * C::kLdsRow];
+  using Stage = StageOf<MODE, NW, BN, ROWS>;
+  __shared__ _Float16 s_tok[2][BN * Stage::kLdsRow];
   __shared__ int64_t s_row[BN];
 
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
@@ -265,33 +413,39 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   const int K = MODE == 0 ? a.H : a.Ip;
   t.nchunks = K / kChunk;
   const int RG = rows_total / 16;
-  t.G0 = wt * (C::kWgRows / 16) + t.w * WRG;
-  t.slot0 = static_cast<int64_t>(t.e) * RG + t.G0;
-  t.wcodes = reinterpret_cast<const uint4*>(MODE == 0 ? a.w13_codes : a.w2_codes);
-  t.wscales = reinterpret_cast<const uint32_t*>(MODE == 0 ? a.w13_scales : a.w2_scales);
-  t.trow = t.tid / C::kThreadsPerRow;
-  t.tpart = t.tid % C::kThreadsPerRow;
-  const int64_t srow = s_row[t.trow];
-  t.trow_codes = (MODE == 0 ? a.x_codes : a.a_codes) + srow * (MODE == 0 ? a.H / 2 : a.I / 2);
-  t.trow_scales = (MODE == 0 ? a.x_scales : a.a_scales) + srow * (MODE == 0 ? a.H / 16 : a.I / 16);
-  t.valid_code_bytes = MODE == 0 ? a.H / 2 : a.I / 2;
+  t.G0 = wt * (C::kWgRows / 16) + __builtin_amdgcn_readfirstlane(t.w) * WRG;
+  {
+    // prepared layout: row group G, chunk c -> 64 lanes x 16 code bytes at (G*nchunks + c)
+    // * 1024, and 128 scale bytes at (G*nchunks + c) * 128 (prepared_scale_index)
+    const int64_t expert_chunks = static_cast<int64_t>(RG) * t.nchunks;
+    const uint8_t* wc = (MODE == 0 ? a.w13_codes : a.w2_codes) + t.e * expert_chunks * 1024;
+    const uint8_t* wsc = (MODE == 0 ? a.w13_scales : a.w2_scales) + t.e * expert_chunks * 128;
+    t.wcodes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wc), 0,
+                                                 static_cast<int>(expert_chunks * 1024), kBufferFlags);
+    t.wscales = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wsc), 0,
+                                                  static_cast<int>(expert_chunks * 128), kBufferFlags);
+    t.lane_code_off = 16u * t.lane;
+    t.lane_scale_off = 4u * static_cast<uint32_t>(prepared_scale_index(0, 1, 0, t.lane));
+  }
+  Stage st;
+  st.init(a, s_row, t.w, t.lane);
 
   // one instantiation per number of active 16-token column blocks, so the MFMA loops
   // have compile-time trip counts (uniform branch per workgroup)
   const int ncb = (t.td.nrows + 15) / 16;
   if constexpr (BN == 32) {
-    if (ncb == 1) tile_body<MODE, NW, WRG, BN, 1>(a, t, s_tok);
-    else tile_body<MODE, NW, WRG, BN, 2>(a, t, s_tok);
+    if (ncb == 1) tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok);
+    else tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok);
   } else {
     switch (ncb) {
-      case 1: tile_body<MODE, NW, WRG, BN, 1>(a, t, s_tok); break;
-      case 2: tile_body<MODE, NW, WRG, BN, 2>(a, t, s_tok); break;
-      case 3: tile_body<MODE, NW, WRG, BN, 3>(a, t, s_tok); break;
-      case 4: tile_body<MODE, NW, WRG, BN, 4>(a, t, s_tok); break;
-      case 5: tile_body<MODE, NW, WRG, BN, 5>(a, t, s_tok); break;
-      case 6: tile_body<MODE, NW, WRG, BN, 6>(a, t, s_tok); break;
-      case 7: tile_body<MODE, NW, WRG, BN, 7>(a, t, s_tok); break;
-      default: tile_body<MODE, NW, WRG, BN, 8>(a, t, s_tok); break;
+      case 1: tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok); break;
+      case 2: tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok); break;
+      case 3: tile_body<MODE, NW, WRG, BN, ROWS, 3>(a, t, st, s_tok); break;
+      case 4: tile_body<MODE, NW, WRG, BN, ROWS, 4>(a, t, st, s_tok); break;
+      case 5: tile_body<MODE, NW, WRG, BN, ROWS, 5>(a, t, st, s_tok); break;
+      case 6: tile_body<MODE, NW, WRG, BN, ROWS, 6>(a, t, st, s_tok); break;
+      case 7: tile_body<MODE, NW, WRG, BN, ROWS, 7>(a, t, st, s_tok); break;
+      default: tile_body<MODE, NW, WRG, BN, ROWS, 8>(a, t, st, s_tok); break;
     }
   }
 }
@@ -333,54 +487,65 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
     }
   }
   uint4 o;
-  o.x = f32_to_bf16_rne(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[1])) << 16);
-  o.y = f32_to_bf16_rne(acc[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[3])) << 16);
-  o.z = f32_to_bf16_rne(acc[4]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[5])) << 16);
-  o.w = f32_to_bf16_rne(acc[6]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[7])) << 16);
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
   reinterpret_cast<uint4*>(a.out + t * a.H)[v] = o;
 }
 
 
-// Variants: small tiles (up to 32 tokens) run 4 waves x 2 groups (128-row slabs); big
-// tiles (up to kBigRows tokens) run kBigNW waves x kBigWRG groups when the slab divides
-// the rows, else the 128-row slab.
+// Variants: small tiles (up to 32 tokens) run 4 waves x 2 groups (128-row slabs) and
+// stage FC1's tokens as f16 rows.  Big tiles (up to kBigRows tokens) run 4 waves x 2
+// groups, FC1 with f16 rows; with at least kManyRows routed rows (about two big tiles
+// per CU) FC1's big tiles run 4 waves x 4 groups instead (half the LDS operand reads per
+// MFMA; the f16 rows no longer fit in registers, so the tokens are staged as codes).
+// A slab that does not divide the rows falls back to 128-row slabs.
 constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
+constexpr int kFc1WideWRG = 4;
+constexpr int64_t kManyRows = 2 * 256 * kBigRows;
 
-template <int MODE, int NW, int WRG, int BN, int WPE>
+template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
 static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipStream_t stream) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const int64_t grid = round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows),
                                 kXcds * kXcdRun);
   if (grid > 0)
-    grouped_gemm_kernel<MODE, NW, WRG, BN, WPE>
+    grouped_gemm_kernel<MODE, NW, WRG, BN, WPE, ROWS>
         <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
 }
 
 template <int MODE>
 static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
+  constexpr bool kRows = MODE == 0;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
-  launch_variant<MODE, 4, 2, kSmallRows, 1>(a, a.max_small, 0, stream);
+  const bool many = static_cast<int64_t>(a.T) * a.k >= kManyRows;
+  launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
+  if constexpr (MODE == 0) {
+    if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
+      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
+      return hipGetLastError();
+    }
+  }
   if (rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
-    launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE>(a, a.max_big, 1, stream);
+    launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE, kRows>(a, a.max_big, 1, stream);
   else
-    launch_variant<MODE, 4, 2, kBigRows, 1>(a, a.max_big, 1, stream);
+    launch_variant<MODE, 4, 2, kBigRows, 1, kRows>(a, a.max_big, 1, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream) { return launch_gemm<0>(a, stream); }
-constexpr int64_t kFc2ResidentBigMinRows = 2 * 256 * kBigRows;
-
 hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
   if (!fc2_resident_fits(a)) return launch_gemm<1>(a, stream);
   launch_fc2_resident_small(a, stream);
   // The resident kernel gives each big tile one workgroup; below about two big tiles per
   // CU that leaves the chip idle, and the grouped kernel (tiles x row slabs) is faster.
-  if (static_cast<int64_t>(a.T) * a.k >= kFc2ResidentBigMinRows) launch_fc2_resident_big(a, stream);
+  if (static_cast<int64_t>(a.T) * a.k >= kManyRows) launch_fc2_resident_big(a, stream);
   else if (a.H % GemmCfg<1, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
-    launch_variant<1, kBigNW, kBigWRG, kBigRows, kBigWPE>(a, a.max_big, 1, stream);
+    launch_variant<1, kBigNW, kBigWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
   else
-    launch_variant<1, 4, 2, kBigRows, 1>(a, a.max_big, 1, stream);
+    launch_variant<1, 4, 2, kBigRows, 1, false>(a, a.max_big, 1, stream);
   return hipGetLastError();
 }
 

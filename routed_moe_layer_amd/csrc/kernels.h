@@ -38,7 +38,7 @@ inline int64_t max_big_tiles(int64_t R, int E) {
 
 hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
                                  int K, const float* q, uint8_t* codes, uint8_t* scales,
-                                 hipStream_t stream);
+                                 uint16_t* decoded, hipStream_t stream);
 
 // Routing: histogram, scan (+ optional GEMM tile list and stats reset), stable scatter.
 struct RouteBuffers {
@@ -69,6 +69,7 @@ struct LayerArgs {
   int H, I, Ip, E, k, T;
   const uint8_t* x_codes;      // [T, H/2]
   const uint8_t* x_scales;     // [T, H/16]
+  const uint16_t* x_dec;       // [T, H] f16: code times block scale
   const int32_t* sorted_row_idx;
   const int32_t* expanded_row_idx;
   const TileDesc* tiles_small;

@@ -2,8 +2,9 @@
 //
 //  * quantize_nvfp4_kernel: group-16 NVFP4 quantization of BF16 rows ("Cake SiTU
 //    backend", intro: group-16 NVFP4 input quantization with the fp32 scale qX).  One
-//    thread per 16-value block: a 32-byte load, 8 bytes of codes and 1 scale byte out.
-//    HBM-bound (41 bytes per 16 values moved).
+//    thread per 16-value block: a 32-byte load, 8 bytes of codes and 1 scale byte out,
+//    and optionally the block's decoded values (code times block scale, exact in f16;
+//    32 bytes), which FC1 stages as its operand.  HBM-bound (41 or 73 bytes per block).
 //  * route_permute_kernel: the token movement of "torch_npu.npu_moe_init_routing_v2"
 //    (section 计算公式, steps 4-5): per-row dynamic int8 quantization (or a BF16 copy),
 //    each token row written to its K expert-sorted positions through the gather map.
@@ -16,7 +17,7 @@ namespace rmoe {
 __global__ __launch_bounds__(256) void quantize_nvfp4_kernel(
     const uint16_t* __restrict__ src, int64_t nblocks, int blocks_per_row,
     int64_t rows_per_group, const float* __restrict__ q, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, uint16_t* __restrict__ decoded) {
   int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
   int64_t row = b / blocks_per_row;
@@ -39,16 +40,22 @@ __global__ __launch_bounds__(256) void quantize_nvfp4_kernel(
   out.y = pack8_codes(v + 8, enc);
   reinterpret_cast<uint2*>(codes)[b] = out;
   scales[b] = static_cast<uint8_t>(sb);
+  if (decoded) {
+    const f16x2 sc = scale_f16x2(sb);
+    f16x8* d = reinterpret_cast<f16x8*>(decoded + b * kGroup);
+    d[0] = decode8(out.x, sc);
+    d[1] = decode8(out.y, sc);
+  }
 }
 
 hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
                                  int K, const float* q, uint8_t* codes, uint8_t* scales,
-                                 hipStream_t stream) {
+                                 uint16_t* decoded, hipStream_t stream) {
   int64_t nblocks = groups * rows_per_group * (K / kGroup);
   if (nblocks == 0) return hipSuccess;
   int64_t grid = (nblocks + 255) / 256;
   quantize_nvfp4_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream>>>(
-      src, nblocks, K / kGroup, rows_per_group, q, codes, scales);
+      src, nblocks, K / kGroup, rows_per_group, q, codes, scales, decoded);
   return hipGetLastError();
 }
 

@@ -83,6 +83,9 @@ def check_layer(p, gpu_out, inter, ref):
     # bit-exact: x codes and scales, routing
     assert np.array_equal(inter["x_scales"], ref["x_scales"])
     assert np.array_equal(inter["x_codes"], oracle.pack_nibbles(ref["x_codes"]))
+    # FC1's f16 operand: the exact values of x's NVFP4 blocks
+    assert np.array_equal(inter["x_dec"].astype(np.float64),
+                          oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
     for key in ("sorted_ids", "sorted_row_idx", "expanded_row_idx", "counts", "cumsum"):
         assert np.array_equal(inter[key], ref[key]), key
     # intermediate codes

@@ -117,6 +117,7 @@ class DeviceLayer:
         return {
             "x_codes": take("x_codes", T * cfg.H // 2, np.uint8, (T, cfg.H // 2)),
             "x_scales": take("x_scales", T * cfg.H // 16, np.uint8, (T, cfg.H // 16)),
+            "x_dec": take("x_dec", T * cfg.H, np.float16, (T, cfg.H)),
             "sorted_ids": take("sorted_ids", R, np.int32, (R,)),
             "sorted_row_idx": take("sorted_row_idx", R, np.int32, (R,)),
             "expanded_row_idx": take("expanded_row_idx", R, np.int32, (R,)),

@@ -208,6 +208,11 @@ EDGE = [
     ("outliers", _edge("edge_out", T=32, E=16, k=4, outlier_frac=0.05, outlier_mult=30.0,
                        seed_index=37), None),
     ("wide_H", _edge("edge_wideH", T=8, H=1024, I=192, E=16, k=6, seed_index=38), None),
+    # several 100-row big tiles per expert through the 64-row-per-wave FC1 (2I % 256 == 0)
+    ("big_tiles", _edge("edge_big", T=200, E=4, k=4, H=256, I=128, seed_index=39), None),
+    # T*k = 65536 routed rows: FC2 big tiles take the LDS-resident kernel
+    ("resident_fc2", _edge("edge_res", T=16384, E=16, k=4, H=256, I=128, seed_index=40),
+     None),
 ]
 
 
