@@ -260,6 +260,155 @@ def traffic_from_profile(kernel):
         return None
 
 
+# ---------------------------------------------------------------------------------------
+# Profile summaries: turn the CSV output of the rocprofv3 runs (kernel trace per workload,
+# FETCH_SIZE / WRITE_SIZE counters, and the plain-copy calibration) into the text
+# summaries under profiles/ and the traffic table the roofline line reads.
+PROFILE_WORKLOADS = {"prefill": "PREFILL_16K", "decode": "DECODE_16", "mid": "MID_1024"}
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _one(pattern):
+    import glob
+    hits = sorted(glob.glob(pattern))
+    return hits[0] if hits else None
+
+
+def _bench_line(log_path):
+    """The JSON line a profiled bench.py run printed (None if absent)."""
+    if not log_path or not os.path.exists(log_path):
+        return None
+    for ln in open(log_path, errors="replace"):
+        ln = ln.strip()
+        if ln.startswith("{") and '"metric"' in ln:
+            return json.loads(ln)
+    return None
+
+
+def _short(name):
+    n = name.replace("void ", "").replace("rmoe::", "")
+    if n.startswith(("grouped_gemm_kernel", "fc2_kernel", "finalize", "quantize", "route",
+                     "prepare")):
+        return n.split("(")[0]
+    return n if len(n) <= 72 else n[:72] + "..."
+
+
+def _role(name):
+    n = _short(name)
+    if n.startswith("grouped_gemm_kernel<0"):
+        return "fc1_kernel"
+    if n.startswith("grouped_gemm_kernel<1") or n.startswith("fc2_kernel"):
+        return "fc2_kernel"
+    if n.startswith("finalize_kernel"):
+        return "finalize_kernel"
+    return None
+
+
+def summarize_profiles(src, out_dir):
+    import moe_inputs
+    os.makedirs(out_dir, exist_ok=True)
+    cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{w} -o {w} "
+                 "-- python3 <repo>/bench.py --workloads {w} --cpu-tokens 0 --steps 20 --warmup 5")
+    cmd_pmc = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_{w}_{c} -o {w} -- python3 "
+               "<repo>/bench.py --workloads {w} --cpu-tokens 0 --steps 3 --warmup 1")
+    cmd_copy = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_copy_{c} -o copy -- python3 "
+                "<repo>/bench.py --copy-calibration")
+    # copy calibration: counter KiB per byte actually moved by a plain device copy
+    factors = {}
+    for c, key in (("FETCH_SIZE", "copy_bytes_read"), ("WRITE_SIZE", "copy_bytes_written")):
+        f = _one(os.path.join(src, f"pmc_copy_{c}", "*counter_collection.csv"))
+        if f is None:
+            continue
+        rows = [r for r in _read_csv(f) if "copy" in r["Kernel_Name"].lower()
+                or "elementwise" in r["Kernel_Name"]]
+        big = max(rows, key=lambda r: float(r["Counter_Value"]))
+        kib = float(big["Counter_Value"])
+        factors[c] = (1 << 30) / (kib * 1024.0)          # bytes moved per counted byte
+    traffic = {"_copy_calibration": {
+        "fetch_factor": factors.get("FETCH_SIZE"), "write_factor": factors.get("WRITE_SIZE"),
+        "note": "bytes moved per counter byte, from a 1 GiB device-to-device copy"}}
+    for w, cname in PROFILE_WORKLOADS.items():
+        cfg = getattr(moe_inputs, cname)
+        stats = _one(os.path.join(src, f"trace_{w}", "*kernel_stats.csv"))
+        if stats is None:
+            continue
+        line = _bench_line(os.path.join(src, f"trace_{w}.log"))
+        rows = _read_csv(stats)
+        md = [f"# Kernel trace: routed-MoE layer, {cfg.name}", "",
+              "Command (from the repository root on the GPU box, after "
+              "`cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd_trace.format(w=w), "```", "",
+              "Per-kernel statistics (`*_kernel_stats.csv`; all calls of the run: weight "
+              "preparation, calibration, warmup and timed steps; `at::` kernels are the "
+              "benchmark's own input setup):", "",
+              "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+        for r in rows[:14]:
+            md.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                      f"{float(r['Percentage']):.1f} |")
+        if line:
+            wl = line["workloads"][w]
+            md += ["", "Stage times the same run measured with HIP events on the launch stream "
+                   "(mean over the timed steps, ms): "
+                   + ", ".join(f"{k} {v:.4f}" for k, v in wl["stage_ms"].items())
+                   + f"; {wl['ms_per_step']:.3f} ms per step, {wl['tokens_per_s']:.0f} tokens/s. "
+                   f"Kernel sources: `{line['kernel_source_hash']}`."]
+        with open(os.path.join(out_dir, f"kernel_trace_T{cfg.T}.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+        # HBM bytes per launch from the counters, scaled by the copy calibration
+        per = {}
+        src_hash = None
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            f = _one(os.path.join(src, f"pmc_{w}_{c}", "*counter_collection.csv"))
+            if f is None or c not in factors:
+                continue
+            pl = _bench_line(os.path.join(src, f"pmc_{w}_{c}.log"))
+            if pl:
+                src_hash = pl["kernel_source_hash"]
+            for r in _read_csv(f):
+                role = _role(r["Kernel_Name"])
+                if role is None:
+                    continue
+                per.setdefault((role, _short(r["Kernel_Name"])), {}).setdefault(c, []).append(
+                    float(r["Counter_Value"]) * 1024.0 * factors[c])
+        if not per:
+            continue
+        md = [f"# HBM traffic per launch: {cfg.name}", "",
+              "Commands (each counter in a run of its own; the copy calibration divides a "
+              "1 GiB device copy's counter reading into the bytes it moved):", "", "```"]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            md.append(cmd_pmc.format(w=w, c=c))
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            md.append(cmd_copy.format(c=c))
+        md += ["```", "",
+               f"Calibration: fetch factor {factors.get('FETCH_SIZE'):.4f}, write factor "
+               f"{factors.get('WRITE_SIZE'):.4f} (bytes per counted byte).", "",
+               "| kernel | launches | read MB/launch | written MB/launch |", "|---|---|---|---|"]
+        best = {}
+        for (role, kname), cs in sorted(per.items()):
+            fr = cs.get("FETCH_SIZE", [0.0])
+            wr = cs.get("WRITE_SIZE", [0.0])
+            fb, wb = sum(fr) / len(fr), sum(wr) / len(wr)
+            md.append(f"| `{kname}` | {len(fr)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+            if role not in best or fb + wb > best[role]["bytes_per_launch"]:
+                best[role] = {"kernel": kname, "fetch_bytes_per_launch": fb,
+                              "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+                              "source_hash": src_hash}
+        for role, ent in best.items():
+            traffic[f"{role}:{cfg.name}"] = ent
+        md.append("")
+        md.append(f"Kernel sources: `{src_hash}`.")
+        with open(os.path.join(out_dir, f"hbm_traffic_T{cfg.T}.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
+        fh.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,7 +419,12 @@ def main():
                     help="tokens of the oracle's bounded CPU sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 output under DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
               "not part of this build (the layer is one TP rank's work; see the design notes "
