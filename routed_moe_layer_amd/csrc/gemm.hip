@@ -236,7 +236,7 @@ using StageOf = typename std::conditional<ROWS, RowStage<NW, BN>, CodeStage<MODE
 // With WRG == 4 the weight fragments are decoded one 32-column K-step at a time (16
 // instead of 64 registers of decoded operands), and the weight loads of chunk c+2 are
 // issued after the last step's decode.
-template <int WRG, int NCBA, class Stage>
+template <int WRG, int NCBA, int DEPTH, class Stage>
 __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, int c,
                                            uint4 (&wc)[WRG], uint32_t (&ws)[WRG],
                                            typename Stage::Regs& tr, const _Float16* tb_cur,
@@ -257,7 +257,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
     for (int s = 0; s < 4; ++s) {
       f16x8 wf[WRG];
       decode_step(s, wf);
-      if (s == 3) load_weights<WRG>(t, min(c + 2, t.nchunks - 1), wc, ws);
+      if (s == 3) load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
         const f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, cb, s, t.lane));
@@ -278,7 +278,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
   // counts stay exact instead of draining every outstanding load.
   const bool more = c + 1 < t.nchunks;
   st.template load<16 * NCBA>(min(c + 1, t.nchunks - 1), tr);
-  load_weights<WRG>(t, min(c + 2, t.nchunks - 1), wc, ws);
+  load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
   __syncthreads();                                      // LDS buffer of chunk c complete
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -304,22 +304,29 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
 #pragma unroll
     for (int j = 0; j < NCBA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wcA[WRG], wcB[WRG];
-  uint32_t wsA[WRG], wsB[WRG];
+  // DEPTH register sets of raw weights: set i holds chunk c+i on entry to chunk c's step
+  constexpr int DEPTH = BN <= kSmallRows ? 4 : 2;
+  uint4 wc[DEPTH][WRG];
+  uint32_t ws[DEPTH][WRG];
   typename Stage::Regs tr;
-  load_weights<WRG>(t, 0, wcA, wsA);
-  if (t.nchunks > 1) load_weights<WRG>(t, 1, wcB, wsB);
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) load_weights<WRG>(t, min(i, t.nchunks - 1), wc[i], ws[i]);
   st.template load<16 * NCBA>(0, tr);
   st.template store<16 * NCBA>(s_tok[0], tr);
-  // two chunks per trip so register sets and LDS buffers are named statically; an odd
-  // last chunk is peeled after the loop (no conditional MFMA block inside the loop)
+  // DEPTH chunks per trip so register sets and LDS buffers are named statically; the
+  // remaining chunks are peeled after the loop
   int c = 0;
-  for (; c + 1 < t.nchunks; c += 2) {
-    chunk_step<WRG, NCBA>(t, st, c, wcA, wsA, tr, s_tok[0], s_tok[1], acc);
-    chunk_step<WRG, NCBA>(t, st, c + 1, wcB, wsB, tr, s_tok[1], s_tok[0], acc);
+  for (; c + DEPTH <= t.nchunks; c += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+      chunk_step<WRG, NCBA, DEPTH>(t, st, c + i, wc[i], ws[i], tr, s_tok[i & 1],
+                                   s_tok[(i + 1) & 1], acc);
   }
-  if (c < t.nchunks)
-    chunk_step<WRG, NCBA>(t, st, c, wcA, wsA, tr, s_tok[0], s_tok[1], acc);
+#pragma unroll
+  for (int i = 0; i + 1 < DEPTH; ++i)
+    if (c + i < t.nchunks)
+      chunk_step<WRG, NCBA, DEPTH>(t, st, c + i, wc[i], ws[i], tr, s_tok[i & 1],
+                                   s_tok[(i + 1) & 1], acc);
 
   const TileDesc td = t.td;
   const int e = t.e, lane = t.lane, g = t.g, G0 = t.G0;

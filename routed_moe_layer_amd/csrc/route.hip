@@ -5,7 +5,7 @@
 // per-expert histogram as an inclusive prefix sum.  The sort must be stable (equal experts
 // keep increasing f) so that the result is unique.
 //
-// Three launches, no host readback ("Cake SiTU backend", intro: routing values never take
+// Three launches (one for at most kRouteTile ids, see route_small_kernel), no host readback ("Cake SiTU backend", intro: routing values never take
 // part in host dispatch):
 //   hist    : one workgroup per tile of 1024 flat ids; LDS histogram -> tile_hist[tile][e].
 //   scan    : one workgroup; per expert, exclusive scan of tile_hist over tiles (in place),
@@ -21,6 +21,8 @@
 namespace rmoe {
 
 constexpr int kIdsPerThread = kRouteTile / kRouteThreads;   // 4
+constexpr int kScanBatch = 16;
+constexpr size_t kRouteSmallMaxLds = 64 * 1024;   // dynamic LDS of the fused small kernel
 
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ tile_hist) {
@@ -40,29 +42,41 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads); returns the exclusive
-// prefix and writes the total to *total.
-__device__ int block_excl_scan(int v, int* sh, int* total) {
+// The three per-expert quantities the expert scans need (rows, small tiles, big tiles),
+// packed into 21-bit fields of one 64-bit value so that one block scan serves all three
+// (every field's total stays below 2^21: at most MOE_MAX_TOKENS * 64 = 2^20 rows per call,
+// at most 4096 small and 2^13 + 4096 big tiles).
+__device__ __forceinline__ uint64_t pack_counts(int cnt, int n_small, int n_big) {
+  return static_cast<uint64_t>(cnt) | (static_cast<uint64_t>(n_small) << 21) |
+         (static_cast<uint64_t>(n_big) << 42);
+}
+__device__ __forceinline__ int field(uint64_t v, int i) {
+  return static_cast<int>((v >> (21 * i)) & ((1u << 21) - 1));
+}
+
+// Block-wide exclusive scan of one uint64 per thread (any multiple of 64 threads up to
+// 1024); returns the exclusive prefix and writes the total to *total.
+__device__ uint64_t block_excl_scan64(uint64_t v, uint64_t* sh, uint64_t* total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int incl = v;
+  const int nw = blockDim.x / kWave;
+  uint64_t incl = v;
   for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(incl, off);
+    const uint64_t o = __shfl_up(incl, off);
     if (lane >= off) incl += o;
   }
   if (lane == kWave - 1) sh[w] = incl;
   __syncthreads();
   if (w == 0) {
-    int nw = blockDim.x / kWave;
-    int s = lane < nw ? sh[lane] : 0;
+    uint64_t x = lane < nw ? sh[lane] : 0;
     for (int off = 1; off < kWave; off <<= 1) {
-      int o = __shfl_up(s, off);
-      if (lane >= off) s += o;
+      const uint64_t o = __shfl_up(x, off);
+      if (lane >= off) x += o;
     }
-    if (lane < nw) sh[lane] = s;     // inclusive over waves
+    if (lane < nw) sh[lane] = x;                  // inclusive over waves
   }
   __syncthreads();
-  int wave_excl = w == 0 ? 0 : sh[w - 1];
-  *total = sh[blockDim.x / kWave - 1];
+  const uint64_t wave_excl = w == 0 ? 0 : sh[w - 1];
+  *total = sh[nw - 1];
   __syncthreads();
   return wave_excl + incl - v;
 }
@@ -83,7 +97,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum,
     TileDesc* __restrict__ tiles_small, TileDesc* __restrict__ tiles_big,
     int32_t* __restrict__ num_tiles, float* __restrict__ amax_reset) {
-  __shared__ int sh[16];
+  __shared__ uint64_t sh[16];
   __shared__ int carry[3];
   if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
   __syncthreads();
@@ -93,22 +107,28 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int e = e0 + threadIdx.x;
     int cnt = 0;
     if (e < E) {
-      for (int t = 0; t < ntiles; ++t) {
-        int32_t* p = tile_hist + static_cast<int64_t>(t) * E + e;
-        int v = *p;
-        *p = cnt;                       // exclusive over tiles
-        cnt += v;
+      // exclusive over tiles, in place; kScanBatch independent loads in flight per step
+      for (int t0 = 0; t0 < ntiles; t0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i)
+          v[i] = t0 + i < ntiles ? tile_hist[static_cast<int64_t>(t0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+          if (t0 + i < ntiles) tile_hist[static_cast<int64_t>(t0 + i) * E + e] = cnt;
+          cnt += v[i];
+        }
       }
       counts[e] = cnt;
       if (amax_reset) amax_reset[e] = 0.0f;
     }
     int n_small, n_big, base;
     expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
-    int total, stotal, btotal;
-    const int excl = block_excl_scan(cnt, sh, &total);
-    const int sexcl = block_excl_scan(n_small, sh, &stotal);
-    const int bexcl = block_excl_scan(n_big, sh, &btotal);
-    const int off = carry[0] + excl;
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
+    const int total = field(tot, 0), stotal = field(tot, 1), btotal = field(tot, 2);
+    const int sexcl = field(ex, 1), bexcl = field(ex, 2);
+    const int off = carry[0] + field(ex, 0);
     if (e < E) {
       offsets[e] = off;
       if (cumsum) cumsum[e] = off + cnt;
@@ -126,22 +146,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nbits,
-    const int32_t* __restrict__ tile_hist, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_row_idx,
-    int32_t* __restrict__ expanded_row_idx) {
-  extern __shared__ int32_t wave_hist[];           // [4][E]
-  const int nw = kRouteThreads / kWave;
-  for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int64_t wave_base = static_cast<int64_t>(blockIdx.x) * kRouteTile + w * (kRouteTile / nw);
-  int key[kIdsPerThread];
-  int rank[kIdsPerThread];
-  int32_t* my_hist = wave_hist + w * E;
-  // Rounds of 64 consecutive ids, in order: rank within the round among equal keys plus
-  // the count of equal keys in earlier rounds of this wave.
+// Stable ranking of one wave's kIdsPerThread*64 consecutive flat ids (from wave_base):
+// in rounds of 64, an id's rank is the number of equal keys in earlier rounds of this
+// wave (my_hist, the wave's running per-expert count in LDS) plus the equal keys on
+// lower lanes of its round (ballot-based key matching).  key[r] is the expert (-1 for no
+// id) and rank[r] the rank of round r's id.
+__device__ __forceinline__ void rank_wave_ids(const int32_t* __restrict__ ids, int64_t n, int E,
+                                              int nbits, int64_t wave_base, int lane,
+                                              int32_t* my_hist, int32_t* expanded_row_idx,
+                                              int (&key)[kIdsPerThread],
+                                              int (&rank)[kIdsPerThread]) {
   for (int r = 0; r < kIdsPerThread; ++r) {
     int64_t f = wave_base + r * kWave + lane;
     int e = f < n ? ids[f] : -1;
@@ -160,6 +174,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     rank[r] = rk;
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits,
+    const int32_t* __restrict__ tile_hist, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_row_idx,
+    int32_t* __restrict__ expanded_row_idx) {
+  extern __shared__ int32_t wave_hist[];           // [4][E]
+  const int nw = kRouteThreads / kWave;
+  for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t wave_base = static_cast<int64_t>(blockIdx.x) * kRouteTile + w * (kRouteTile / nw);
+  int key[kIdsPerThread];
+  int rank[kIdsPerThread];
+  int32_t* my_hist = wave_hist + w * E;
+  rank_wave_ids(ids, n, E, nbits, wave_base, lane, my_hist, expanded_row_idx, key, rank);
   __syncthreads();
   // Exclusive scan over the waves, per expert.
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -183,10 +214,96 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
   }
 }
 
+// At most kRouteTile flat ids: the three passes fused in one workgroup of 1024 threads (no
+// tile histograms, no handoff between launches).  The first four waves rank the ids (256
+// each, as in the scatter kernel); all sixteen scan the experts.  LDS: the per-wave
+// histograms [4][E] (after the ranking, exclusive over waves) and the expert offsets [E].
+constexpr int kRouteSmallThreads = 1024;
+
+__global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum,
+    TileDesc* __restrict__ tiles_small, TileDesc* __restrict__ tiles_big,
+    int32_t* __restrict__ num_tiles, float* __restrict__ amax_reset,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_row_idx,
+    int32_t* __restrict__ expanded_row_idx) {
+  extern __shared__ int32_t lds[];
+  __shared__ uint64_t sh[16];
+  __shared__ int carry[3];
+  constexpr int nw = kRouteThreads / kWave;            // ranking waves
+  int32_t* wave_hist = lds;
+  int32_t* off_sh = lds + nw * E;
+  for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
+  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t wave_base = static_cast<int64_t>(w) * (kRouteTile / nw);
+  int key[kIdsPerThread];
+  int rank[kIdsPerThread];
+  if (w < nw)
+    rank_wave_ids(ids, n, E, nbits, wave_base, lane, wave_hist + w * E, expanded_row_idx, key,
+                  rank);
+  __syncthreads();
+  const bool lists = tiles_small != nullptr;
+  for (int e0 = 0; e0 < E; e0 += blockDim.x) {
+    const int e = e0 + threadIdx.x;
+    int cnt = 0;
+    if (e < E) {
+      for (int ww = 0; ww < nw; ++ww) {
+        const int v = wave_hist[ww * E + e];
+        wave_hist[ww * E + e] = cnt;                   // exclusive over waves
+        cnt += v;
+      }
+      counts[e] = cnt;
+      if (amax_reset) amax_reset[e] = 0.0f;
+    }
+    int n_small, n_big, base;
+    expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
+    const int total = field(tot, 0), stotal = field(tot, 1), btotal = field(tot, 2);
+    const int sexcl = field(ex, 1), bexcl = field(ex, 2);
+    const int off = carry[0] + field(ex, 0);
+    if (e < E) {
+      offsets[e] = off;
+      off_sh[e] = off;
+      if (cumsum) cumsum[e] = off + cnt;
+      if (n_small) tiles_small[carry[1] + sexcl] = TileDesc{e, off, cnt, 0};
+      for (int j = 0; j < n_big; ++j)
+        tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = carry[0];
+    if (num_tiles) { num_tiles[0] = carry[1]; num_tiles[1] = carry[2]; }
+  }
+  __syncthreads();                                      // off_sh complete
+  if (w >= nw) return;
+  for (int r = 0; r < kIdsPerThread; ++r) {
+    const int e = key[r];
+    if (e < 0) continue;
+    const int64_t f = wave_base + r * kWave + lane;
+    const int pos = off_sh[e] + wave_hist[w * E + e] + rank[r];
+    if (sorted_ids) sorted_ids[pos] = e;
+    if (sorted_row_idx) sorted_row_idx[pos] = static_cast<int32_t>(f);
+    expanded_row_idx[f] = pos;
+  }
+}
+
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
                         hipStream_t stream) {
   const int nt = route_tiles(n);
   if (nt == 0) return hipSuccess;
+  const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
+  if (nt == 1 && small_lds <= kRouteSmallMaxLds) {
+    route_small_kernel<<<dim3(1), dim3(kRouteSmallThreads), small_lds, stream>>>(
+        ids, n, E, bits_for(E), b.counts, b.offsets, b.cumsum, b.tiles_small, b.tiles_big,
+        b.num_tiles, b.amax_reset, b.sorted_ids, b.sorted_row_idx, b.expanded_row_idx);
+    return hipGetLastError();
+  }
   route_hist_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
       ids, n, E, b.tile_hist);
   route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(

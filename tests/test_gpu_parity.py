@@ -103,6 +103,10 @@ ROUTE_CASES = [
     ("T16384_k16_E896", 16384, 16, 896, 0.0),
     ("T700_k1_E1", 700, 1, 1, 0.0),
     ("T300_k64_E4096", 300, 64, 4096, 0.5),
+    # boundary of the single-workgroup router (at most 1024 ids) and just past it
+    ("T64_k16_E896", 64, 16, 896, 0.8),
+    ("T65_k16_E896", 65, 16, 896, 0.8),
+    ("T16_k64_E3000", 16, 64, 3000, 0.3),
 ]
 
 
@@ -126,6 +130,30 @@ def test_route_with_duplicates_and_one_hot_expert():
     for key in want:
         if key in got:
             assert np.array_equal(got[key], want[key]), key
+
+
+@pytest.mark.parametrize("T", [20, 300], ids=["one_workgroup", "tiled"])
+def test_route_drops_out_of_range_ids(T):
+    """Ids outside [0, E) break the caller's contract; the library documents that they
+    are dropped (gather-map entry -1) and the valid ids are sorted stably among
+    themselves.  Expected values: a stable argsort of the valid subset."""
+    _say(f"route out-of-range ids T={T}")
+    E, K = 40, 16
+    rng = np.random.default_rng(77 + T)
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    bad = rng.random((T, K)) < 0.1
+    ids[bad] = rng.choice(np.array([-1, E, E + 7, -100], np.int32), size=int(bad.sum()))
+    got = _route_on_gpu(ids, E)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    order = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    nv = order.size
+    assert np.array_equal(got["sorted_row_idx"][:nv], order)
+    assert np.array_equal(got["sorted_ids"][:nv], flat[order])
+    want = np.full(flat.size, -1, np.int64)
+    want[order] = np.arange(nv)
+    assert np.array_equal(got["expanded_row_idx"], want)
+    assert np.array_equal(got["cumsum"], np.cumsum(np.bincount(flat[valid], minlength=E)))
 
 
 def test_route_int8_full_size_bit_exact():
