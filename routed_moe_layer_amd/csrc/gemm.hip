@@ -305,7 +305,9 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
     for (int j = 0; j < NCBA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // DEPTH register sets of raw weights: set i holds chunk c+i on entry to chunk c's step
-  constexpr int DEPTH = BN <= kSmallRows ? 4 : 2;
+  // (deeper prefetch measured no faster: the small tiles lose occupancy, the big ones
+  // have no registers left)
+  constexpr int DEPTH = 2;
   uint4 wc[DEPTH][WRG];
   uint32_t ws[DEPTH][WRG];
   typename Stage::Regs tr;
