@@ -35,11 +35,11 @@ __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int l
   constexpr int kSlabGroups = NW * WRG;
   const uint4* __restrict__ wcodes = reinterpret_cast<const uint4*>(a.w2_codes);
   const uint32_t* __restrict__ wscales = reinterpret_cast<const uint32_t*>(a.w2_scales);
-  const int64_t slot = static_cast<int64_t>(e) * (a.H / 16) + j * kSlabGroups + w * WRG;
+  const int64_t chunk0 = prepared_chunk(e, c, j * kSlabGroups + w * WRG, nchunks, a.H / 16);
 #pragma unroll
   for (int r = 0; r < WRG; ++r) {
-    dst.c[r] = wcodes[((slot + r) * nchunks + c) * 64 + lane];
-    dst.s[r] = wscales[prepared_scale_index(slot + r, nchunks, c, lane)];
+    dst.c[r] = wcodes[(chunk0 + r) * 64 + lane];
+    dst.s[r] = wscales[prepared_scale_index(chunk0 + r, lane)];
   }
 }
 

@@ -69,7 +69,7 @@ struct GemmCfg {
 struct TileCtx {
   TileDesc td;
   int e, tid, lane, w, g;
-  int nchunks, G0;
+  int nchunks, groups, G0;
   __amdgpu_buffer_rsrc_t wcodes, wscales;   // this expert's prepared codes / scales
   uint32_t lane_code_off, lane_scale_off;
 };
@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_weights(const TileCtx& t, int c, uint4 (&wc
                                              uint32_t (&ws)[WRG]) {
 #pragma unroll
   for (int r = 0; r < WRG; ++r) {
-    const uint32_t chunk = static_cast<uint32_t>((t.G0 + r) * t.nchunks + c);
+    const uint32_t chunk = static_cast<uint32_t>(c * t.groups + t.G0 + r);
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(t.wcodes, t.lane_code_off,
                                                           chunk * 1024u, 0);
     wc[r] = uint4{v[0], v[1], v[2], v[3]};
@@ -424,8 +424,9 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   const int RG = rows_total / 16;
   t.G0 = wt * (C::kWgRows / 16) + __builtin_amdgcn_readfirstlane(t.w) * WRG;
   {
-    // prepared layout: row group G, chunk c -> 64 lanes x 16 code bytes at (G*nchunks + c)
-    // * 1024, and 128 scale bytes at (G*nchunks + c) * 128 (prepared_scale_index)
+    // this expert's chunks (prepared_chunk): (chunk c, row group G) -> 64 lanes x 16 code
+    // bytes at (c*groups + G) * 1024 and 128 scale bytes at (c*groups + G) * 128
+    t.groups = RG;
     const int64_t expert_chunks = static_cast<int64_t>(RG) * t.nchunks;
     const uint8_t* wc = (MODE == 0 ? a.w13_codes : a.w2_codes) + t.e * expert_chunks * 1024;
     const uint8_t* wsc = (MODE == 0 ? a.w13_scales : a.w2_scales) + t.e * expert_chunks * 128;
@@ -434,7 +435,7 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
     t.wscales = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wsc), 0,
                                                   static_cast<int>(expert_chunks * 128), kBufferFlags);
     t.lane_code_off = 16u * t.lane;
-    t.lane_scale_off = 4u * static_cast<uint32_t>(prepared_scale_index(0, 1, 0, t.lane));
+    t.lane_scale_off = 4u * static_cast<uint32_t>(prepared_scale_index(0, t.lane));
   }
   Stage st;
   st.init(a, s_row, t.w, t.lane);

@@ -101,8 +101,10 @@ void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream);
 
 // Prepared-weight layout (private).  For a matrix of R rows (multiple of 16) and K columns
-// padded to Kp (multiple of 128): codes [R/16][Kp/128][64 lanes][16 B] and scales
-// [R/16][Kp/128][2][16][4 B].  Lane l of row group G, chunk c holds row 16G + l%16,
+// padded to Kp (multiple of 128), per expert: codes [Kp/128][R/16][64 lanes][16 B] and
+// scales [Kp/128][R/16][2][16][4 B] -- chunk-major, so the row groups a workgroup reads
+// for one 128-column chunk are one contiguous run.  Lane l of row group G, chunk c holds
+// row 16G + l%16,
 // and its dword s (s = 0..3) holds the 8 codes k = 128c + 32s + 8(l/16) + [0..7]
 // (the f16 16x16x32 MFMA operand for K-step s).  Those 8 codes lie in block
 // 8c + 2s + (l/16)/2, so lanes l and l+16 share a block: the scale dword of lane l is
@@ -112,11 +114,16 @@ hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream);
 // row 8G+j: each lane then holds g and u of the same intermediate channels.
 inline size_t prepared_codes_bytes(int R, int Kp) { return static_cast<size_t>(R) * Kp / 2; }
 inline size_t prepared_scales_bytes(int R, int Kp) { return static_cast<size_t>(R) * Kp / 16; }
-// Index of lane `lane`'s scale dword for (row group G, chunk c) of matrix slot `slot`
-// (= expert * R/16 + G), in uint32 units.
-__host__ __device__ inline int64_t prepared_scale_index(int64_t slot, int nchunks, int c,
-                                                         int lane) {
-  return (slot * nchunks + c) * 32 + (lane >> 5) * 16 + (lane & 15);
+// Index of the 16-row x 128-column chunk (expert e, chunk c, row group G) among a
+// matrix's chunks (groups = R/16 row groups, nchunks = Kp/128 chunks per expert): its
+// codes are the 1024 bytes at 1024 * index, its scales the 32 dwords at 32 * index.
+__host__ __device__ inline int64_t prepared_chunk(int64_t e, int c, int G, int nchunks,
+                                                  int groups) {
+  return (e * nchunks + c) * groups + G;
+}
+// Index of lane `lane`'s scale dword of chunk `chunk`, in uint32 units.
+__host__ __device__ inline int64_t prepared_scale_index(int64_t chunk, int lane) {
+  return chunk * 32 + (lane >> 5) * 16 + (lane & 15);
 }
 
 }  // namespace rmoe

@@ -17,14 +17,15 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     uint8_t* __restrict__ out_scales) {
   int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
+  // idx = 64 * prepared_chunk(e, c, G) + lane
   const int lane = static_cast<int>(idx & 63);
   int64_t rest = idx >> 6;
   const int nchunks = Kp / kChunk;
-  const int c = static_cast<int>(rest % nchunks);
-  rest /= nchunks;
   const int groups = R / 16;
   const int G = static_cast<int>(rest % groups);
-  const int64_t e = rest / groups;
+  rest /= groups;
+  const int c = static_cast<int>(rest % nchunks);
+  const int64_t e = rest / nchunks;
   const int pr = 16 * G + (lane & 15);
   int row = pr;
   if (fc1) {
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   reinterpret_cast<uint4*>(out_codes)[idx] = make_uint4(w[0], w[1], w[2], w[3]);
   // lanes l and l+16 carry the same block scales; the even lane-group stores them
   if ((g & 1) == 0)
-    reinterpret_cast<uint32_t*>(out_scales)[prepared_scale_index(e * groups + G, nchunks, c, lane)] = sc;
+    reinterpret_cast<uint32_t*>(out_scales)[prepared_scale_index(idx >> 6, lane)] = sc;
 }
 
 hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
