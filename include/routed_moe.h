@@ -84,7 +84,8 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   expert_counts   i32 [E]   rows per expert;  expert_cumsum i32 [E] inclusive prefix sum
  *   a_codes   u8  [T*k, I/2]  requantized SiTU output, sorted row order
  *   a_scales  u8  [T*k, I/16]
- *   o_rows    bf16 [T*k, H]   FC2 output per sorted row, alpha2 applied
+ *   o_rows    bf16 [T*k, H]   FC2 output of routed row (t, j) at row t*k + j, alpha2
+ *                             applied (rows of dropped ids are not written)
  *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
  *                             (0 for an expert with no rows; a calibration statistic) */
 typedef struct {

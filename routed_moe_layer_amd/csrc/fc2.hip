@@ -58,29 +58,38 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   const int last = slab0 + nslabs - 1;
   const float al = a.alpha2[e];
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
+  // FC2 rows are stored at their flat id t*k + j, so that the finalization reads each
+  // token's k rows as one contiguous run
+  uint16_t* orow_cb[NCBA];
+#pragma unroll
+  for (int cb = 0; cb < NCBA; ++cb) {
+    const int n = min(cb * 16 + (lane & 15), td.nrows - 1);
+    orow_cb[cb] = a.o_rows + static_cast<int64_t>(a.sorted_row_idx[td.row_start + n]) * a.H + 4 * g;
+  }
   f32x4 acc[WRG][NCBA];
 
   auto step = [&](const int j, const int c, W2Regs<WRG>& cur) {
-    f16x8 wf[4][WRG];
+    // one 32-column K-step at a time: decode its weight fragments, then its MFMAs; after
+    // the last step's decode the set is refilled with step q+2 (slab clamped: surplus
+    // loads past the last slab are unused and unconditional, so the compiler's load
+    // counters stay exact)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s) {
+      f16x8 wf[WRG];
 #pragma unroll
       for (int r = 0; r < WRG; ++r) {
         const uint32_t cw = s == 0 ? cur.c[r].x : s == 1 ? cur.c[r].y : s == 2 ? cur.c[r].z : cur.c[r].w;
-        wf[s][r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
+        wf[r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
       }
-    // refill with step q+2 (slab clamped: surplus loads past the last slab are unused and
-    // unconditional, so the compiler's load counters stay exact)
-    fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      if (s == 3)
+        fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
         const f16x8 xf =
             *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
 #pragma unroll
         for (int r = 0; r < WRG; ++r)
-          acc[r][cb] = mfma16x16x32(wf[s][r], xf,
+          acc[r][cb] = mfma16x16x32(wf[r], xf,
                                     (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -91,7 +100,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
       for (int cb = 0; cb < NCBA; ++cb) {
         const int n = cb * 16 + (lane & 15);
         if (n < td.nrows) {
-          uint16_t* orow = a.o_rows + (td.row_start + n) * a.H + 4 * g;
+          uint16_t* orow = orow_cb[cb];
 #pragma unroll
           for (int r = 0; r < WRG; ++r) {
             const f32x4 o = acc[r][cb];
@@ -102,6 +111,9 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
           }
         }
       }
+      // the next slab's MFMAs (fresh accumulators) stay after these stores, so the two
+      // accumulator sets are never live together
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

@@ -381,7 +381,9 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
     for (int cb = 0; cb < NCBA; ++cb) {
       const int n = cb * 16 + (lane & 15);
       if (n >= td.nrows) continue;
-      const int64_t row = td.row_start + n;
+      // stored at the row's flat id t*k + j (the finalization reads a token's rows as
+      // one contiguous run)
+      const int64_t row = a.sorted_row_idx[td.row_start + n];
 #pragma unroll
       for (int r = 0; r < WRG; ++r) {
         const f32x4 o = acc[r][cb];
@@ -460,11 +462,11 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   }
 }
 
-// out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[expanded_row_idx[t*k + j], 8v..8v+7]), j in
-// order, fp32 fused multiply-add.  A workgroup covers 8*kFinThreads columns of one token
-// (the token's row indices and weights are the same for the whole wave); each thread owns
-// 8 columns and issues the 16-byte loads of up to kFinBatch routed rows before it
-// accumulates them, so a wave keeps that many row reads in flight.
+// out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[t*k + j, 8v..8v+7]), j in order, fp32 fused
+// multiply-add; rows whose id was dropped (gather-map entry < 0) are skipped.  FC2 stored
+// the rows in flat id order, so a token's k rows are one contiguous run.  A workgroup
+// covers 8*kFinThreads columns of one token; each thread owns 8 columns and issues the
+// 16-byte loads of up to kFinBatch rows before it accumulates them.
 constexpr int kFinThreads = 256, kFinBatch = 8;
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
@@ -480,9 +482,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
       const int j = j0 + u;
-      const int64_t pos = j < a.k ? pos_t[j] : -1;
-      ok[u] = pos >= 0;                         // < 0: dropped (expert id out of range)
-      d[u] = ok[u] ? reinterpret_cast<const uint4*>(a.o_rows + pos * a.H)[v] : uint4{0, 0, 0, 0};
+      ok[u] = j < a.k && pos_t[j] >= 0;         // < 0: dropped (expert id out of range)
+      d[u] = ok[u] ? reinterpret_cast<const uint4*>(a.o_rows + (t * a.k + j) * a.H)[v]
+                   : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {

@@ -88,7 +88,7 @@ struct LayerArgs {
   uint8_t* a_codes;            // [T*k, I/2]
   uint8_t* a_scales;           // [T*k, I/16]
   float* a_amax;               // [E]
-  uint16_t* o_rows;            // [T*k, H] bf16
+  uint16_t* o_rows;            // [T*k, H] bf16, row t*k + j (flat id order)
   const uint16_t* route_weights;
   uint16_t* out;               // [T, H]
 };
