@@ -68,29 +68,50 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   }
   f32x4 acc[WRG][NCBA];
 
+  auto decode = [&](const W2Regs<WRG>& cur, const int s, f16x8 (&wf)[WRG]) {
+#pragma unroll
+    for (int r = 0; r < WRG; ++r) {
+      const uint32_t cw = s == 0 ? cur.c[r].x : s == 1 ? cur.c[r].y : s == 2 ? cur.c[r].z : cur.c[r].w;
+      wf[r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
+    }
+  };
   auto step = [&](const int j, const int c, W2Regs<WRG>& cur) {
-    // one 32-column K-step at a time: decode its weight fragments, then its MFMAs; after
-    // the last step's decode the set is refilled with step q+2 (slab clamped: surplus
-    // loads past the last slab are unused and unconditional, so the compiler's load
-    // counters stay exact)
+    // Software pipeline over the four 32-column K-steps: the weight fragments of step s+1
+    // are decoded while the MFMAs of step s run (interleaved: per 16-token block one LDS
+    // operand read, then each MFMA followed by two VALU instructions).  After the last
+    // decode the set is refilled with step q+2 (slab clamped: surplus loads past the last
+    // slab are unused and unconditional, so the compiler's load counters stay exact).
+    f16x8 wf[2][WRG];
+    decode(cur, 0, wf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f16x8 wf[WRG];
-#pragma unroll
-      for (int r = 0; r < WRG; ++r) {
-        const uint32_t cw = s == 0 ? cur.c[r].x : s == 1 ? cur.c[r].y : s == 2 ? cur.c[r].z : cur.c[r].w;
-        wf[r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
-      }
-      if (s == 3)
-        fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
+      if (s < 3) decode(cur, s + 1, wf[(s + 1) & 1]);
+      else fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
+      // token operand of block cb+1 is read while block cb's MFMAs run
+      const _Float16* xs = xrow + c * kChunk + 32 * s;
+      f16x8 xf = *reinterpret_cast<const f16x8*>(xs);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const f16x8 xf =
-            *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
+        const f16x8 xn = cb + 1 < NCBA
+            ? *reinterpret_cast<const f16x8*>(xs + (cb + 1) * 16 * kFc2LdsRow) : xf;
 #pragma unroll
         for (int r = 0; r < WRG; ++r)
-          acc[r][cb] = mfma16x16x32(wf[r], xf,
+          acc[r][cb] = mfma16x16x32(wf[s & 1][r], xf,
                                     (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
+        xf = xn;
+      }
+      if (s < 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read, block 0
+#pragma unroll
+        for (int cb = 0; cb < NCBA; ++cb) {
+          if (cb + 1 < NCBA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // block cb+1
+#pragma unroll
+          for (int r = 0; r < WRG; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU (next decode)
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
