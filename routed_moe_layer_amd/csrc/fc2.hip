@@ -152,8 +152,10 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   }
 }
 
-// grid: (token tile, slab group) pairs; slab group = SPW consecutive slabs.
-template <int NW, int WRG, int BN, int SPW>
+// grid: (token sub-tile, slab group) pairs; slab group = SPW consecutive slabs.  A work
+// list tile of up to kBigRows rows is taken as SPLIT sub-tiles of BN rows (BN < kBigRows
+// keeps the LDS tile small enough for several workgroups per CU).
+template <int NW, int WRG, int BN, int SPW, int SPLIT>
 __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   __shared__ _Float16 s_tok[BN * kFc2LdsRow];
   __shared__ int64_t s_row[BN];
@@ -161,10 +163,14 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   const int ntiles = a.num_tiles[big];
   const int n_slabs = a.H / (NW * WRG * 16);
   const int n_groups = (n_slabs + SPW - 1) / SPW;
-  int tt, grp;
-  map_workgroup(blockIdx.x, n_groups, &tt, &grp);
+  int ts, grp;
+  map_workgroup(blockIdx.x, n_groups, &ts, &grp);
+  const int tt = ts / SPLIT, part = ts % SPLIT;
   if (tt >= ntiles) return;
-  const TileDesc td = tiles[tt];
+  TileDesc td = tiles[tt];
+  td.row_start += part * BN;
+  td.nrows = min(BN, td.nrows - part * BN);
+  if (td.nrows <= 0) return;
   const int tid = threadIdx.x;
   if (tid < BN) s_row[tid] = td.row_start + min(tid, td.nrows - 1);
   __syncthreads();
@@ -197,6 +203,13 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   if constexpr (BN == 32) {
     if (ncb == 1) run(integral_constant<int, 1>{});
     else run(integral_constant<int, 2>{});
+  } else if constexpr (BN == 64) {
+    switch (ncb) {
+      case 1: run(integral_constant<int, 1>{}); break;
+      case 2: run(integral_constant<int, 2>{}); break;
+      case 3: run(integral_constant<int, 3>{}); break;
+      default: run(integral_constant<int, 4>{}); break;
+    }
   } else {
     switch (ncb) {
       case 1: run(integral_constant<int, 1>{}); break;
@@ -211,14 +224,16 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   }
 }
 
-template <int NW, int WRG, int BN, int SPW>
+template <int NW, int WRG, int BN, int SPW, int SPLIT = 1>
 static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
                                hipStream_t stream) {
   const int n_slabs = a.H / (NW * WRG * 16);
   const int n_groups = (n_slabs + SPW - 1) / SPW;
-  const int64_t grid = round_up(round_up(max_tiles, kTileGroup) * n_groups, kXcds * kXcdRun);
+  const int64_t grid =
+      round_up(round_up(max_tiles * SPLIT, kTileGroup) * n_groups, kXcds * kXcdRun);
   if (grid > 0)
-    fc2_kernel<NW, WRG, BN, SPW><<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a, big);
+    fc2_kernel<NW, WRG, BN, SPW, SPLIT>
+        <<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a, big);
 }
 
 // Small tiles: 128-row slabs in groups of 4 (enough workgroups for decode-size batches);
@@ -231,9 +246,9 @@ void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
 
 void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream) {
   if (a.H % 256 == 0)
-    launch_fc2_variant<4, 4, kBigRows, 1 << 20>(a, a.max_big, 1, stream);
+    launch_fc2_variant<4, 4, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
   else
-    launch_fc2_variant<4, 2, kBigRows, 1 << 20>(a, a.max_big, 1, stream);
+    launch_fc2_variant<4, 2, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
 }
 
 }  // namespace rmoe
