@@ -8,10 +8,13 @@ TP8-local shape H=3584, I=384, E=896, top-16, with every input already resident 
 The headline line reports the prefill batch (T=16384, per-expert SiTU parameters, 0.5%
 outlier channels x30): tokens/s, and the roofline of its dominant kernel (the FC1 grouped
 GEMM, bound by the f16 MFMA).  The decode (T=16) and mid (T=1024, Zipf 1.0) batches are
-reported under "workloads" with their HBM rooflines.  Per-stage times come from HIP
-events recorded between the stages on the launch stream (moe_forward_timed).
+reported under "workloads" with their HBM rooflines, and the routing-and-int8-permute
+primitive (moe_route, N=8192, H=7168, E=256, K=8) under "routing_primitive" with its
+routed rows/s and HBM fraction.  Per-stage times come from HIP events recorded between
+the stages on the launch stream (moe_forward_timed).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,decode,mid]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workloads prefill,decode,mid,route] [--summarize DIR]
 """
 
 import argparse
@@ -49,6 +52,7 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -64,6 +68,10 @@ class HipEvents:
         if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def destroy(self, evs):
         for e in evs:
@@ -203,6 +211,51 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     keep = dict(x=x, ids=ids_host[0], rw=rw, qx=qx, alpha1=alpha1, qa=qa, alpha2=alpha2,
                 beta=beta, lam=lam)
     return res, keep
+
+
+def route_workload(cfg, torch, rm, steps, warmup, events):
+    """Time the routing-and-int8-permute primitive (moe_route) on its own workload: the
+    stable sort by expert, the row maps, the per-expert cumsum and the expanded int8 rows
+    with their dynamic scales.  Algorithmic bytes: x read once, ids, the expanded rows and
+    scales and the three index arrays written once."""
+    from moe_inputs import draw_route_inputs
+    N, H, E, K = cfg.N, cfg.H, cfg.E, cfg.K
+    xb, ids_h = draw_route_inputs(cfg)
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    ids = torch.from_numpy(np.ascontiguousarray(ids_h)).cuda()
+    R = N * K
+    ex = torch.empty((R, H), dtype=torch.int8, device="cuda")
+    esc = torch.empty(R, dtype=torch.float32, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    sid = torch.empty(R, dtype=torch.int32, device="cuda")
+    sri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = torch.empty(rm.moe_route_workspace_size(N, K, E), dtype=torch.uint8, device="cuda")
+
+    def call():
+        rm.moe_route(N, H, E, K, x, ids, rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs, sid,
+                     sri, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [events.create(2) for _ in range(steps)]
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    for i in range(steps):
+        events.record(evs[i][0], stream)
+        call()
+        events.record(evs[i][1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = float(np.mean([events.elapsed_ms(e[0], e[1]) for e in evs]))
+    for e in evs:
+        events.destroy(e)
+    nbytes = N * H * 2 + R * 4 + R * H + R * 4 + 3 * R * 4 + E * 4
+    return {"workload": cfg.name, "N": N, "routed_rows_per_s": R / (gpu_ms * 1e-3),
+            "ms_per_call": gpu_ms, "wall_ms_per_call": wall * 1e3 / steps,
+            "algorithmic_bytes": float(nbytes),
+            "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
 
 
 def cpu_baseline(cfg, keep, torch, n_tokens):
@@ -414,7 +467,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="prefill,decode,mid")
+    ap.add_argument("--workloads", default="prefill,decode,mid,route")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens of the oracle's bounded CPU sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -433,7 +486,7 @@ def main():
 
     import torch
     import routed_moe_layer_amd as rm
-    from moe_inputs import DECODE_16, MID_1024, PREFILL_16K
+    from moe_inputs import DECODE_16, MID_1024, PREFILL_16K, ROUTE_8K
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.copy_calibration:
@@ -451,6 +504,13 @@ def main():
     chosen = [w.strip() for w in args.workloads.split(",") if w.strip()]
     cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4)}
     results, keeps = {}, {}
+    route_res = None
+    if "route" in chosen:
+        chosen = [c for c in chosen if c != "route"]
+        log(f"timing {ROUTE_8K.name}: warmup {args.warmup}, steps {args.steps}")
+        route_res = route_workload(ROUTE_8K, torch, rm, args.steps, args.warmup, events)
+        log(f"  {route_res['routed_rows_per_s']:.3e} routed rows/s, {route_res['ms_per_call']:.3f} ms, "
+            f"{100 * route_res['hbm_frac']:.1f}% of HBM peak")
     for name in chosen:
         cfg, rot = cfgs[name]
         log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
@@ -459,6 +519,9 @@ def main():
         r = results[name]
         log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step, stages "
             + ", ".join(f"{k} {v:.3f}" for k, v in r["stage_ms"].items()))
+    if not chosen:                      # routing primitive only
+        print(json.dumps({"routing_primitive": route_res}), flush=True)
+        return
     head = "prefill" if "prefill" in results else chosen[0]
     hr = results[head]
     hcfg = cfgs[head][0]
@@ -483,7 +546,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": hcfg.name, "T": hcfg.T, "H": hcfg.H, "I": hcfg.I, "E": hcfg.E,
                    "top_k": hcfg.k, "parallelism": "single GPU (one TP8 rank's share)"},
-        "roofline": roof, "cpu_baseline": cpu, "workloads": results,
+        "roofline": roof, "cpu_baseline": cpu, "workloads": results, "routing_primitive": route_res,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
