@@ -27,7 +27,7 @@ from .codecs import (E2M1_MAGNITUDES, e2m1_decode, e2m1_encode, e4m3_decode, e4m
 from .nvfp4 import quantize_nvfp4, dequantize_nvfp4, pack_nibbles, unpack_nibbles
 from .calib import (global_scale_from_amax, calibrate_layer, calibrate_tokens,
                     calibrate_weights, quantize_expert_stack)
-from .routing import route, route_int8
+from .routing import route, route_int8, route_v2, int8_static_quant
 from .layer import (situ, fc_exact, layer_forward, layer_forward_dense, token_forward,
                     calibrate_intermediate, intermediate_amax,
                     expert_weights_decoded)
@@ -39,7 +39,7 @@ __all__ = [
     "global_scale_from_amax", "calibrate_layer", "calibrate_tokens", "calibrate_weights",
     "quantize_expert_stack",
     "calibrate_intermediate", "intermediate_amax",
-    "route", "route_int8",
+    "route", "route_int8", "route_v2", "int8_static_quant",
     "situ", "fc_exact", "layer_forward", "layer_forward_dense", "token_forward",
     "expert_weights_decoded",
 ]

@@ -9,7 +9,7 @@ this scale arithmetic during model preparation.  The tensor-to-scale rule amax/(
 description states; it puts the largest element of the tensor at code 6 under a
 block scale of 448.
 
-Reading R8: a tensor whose amax is 0 gets d = q = 1 (any positive value encodes zeros
+Reading taken: a tensor whose amax is 0 gets d = q = 1 (any positive value encodes zeros
 as zeros; 1/0 would make the block-scale arithmetic produce NaN).
 """
 

@@ -6,7 +6,7 @@ The pages name the formats but never spell them out: "Cake SiTU backend", intro 
 section "Prepared weights and scales", say NVFP4 (FP4 values in groups of 16) with
 float8_e4m3fn block scales; "Nvfp4 Tensor" (struct NVFP4Tensor) calls the 4-bit payload
 E2M1 and the scales FP8 E4M3.  The definitions below are the standard ones for those
-names (readings R1-R3 of the design notes):
+names (readings of those names):
 
   * E2M1: bit 3 = sign, bits 2..0 = magnitude index into {0, .5, 1, 1.5, 2, 3, 4, 6};
     no Inf/NaN.
@@ -71,7 +71,7 @@ def e2m1_encode(y):
     """4-bit E2M1 code of float values ``y`` (round to nearest, ties to even, saturate at 6).
 
     The sign bit is the sign bit of ``y``: a negative value that rounds to zero, or -0.0,
-    gives code 0x8 (reading R5: signed zeros are kept).
+    gives code 0x8 (a reading: signed zeros are kept).
     """
     y = np.asarray(y, dtype=np.float64)
     mag_code = _nearest_even(np.abs(y), E2M1_MAGNITUDES)
@@ -89,7 +89,7 @@ def e4m3_decode(codes):
 
 def e4m3_encode(s):
     """E4M3 byte of non-negative float values: clamp to 448 first, then round to nearest,
-    ties to even (reading R4: saturating conversion, never NaN)."""
+    ties to even (a reading: saturating conversion, never NaN)."""
     s = np.asarray(s, dtype=np.float64)
     if np.any(s < 0) or np.any(np.isnan(s)):
         raise ValueError("e4m3_encode is only used on non-negative block scales")

@@ -11,7 +11,7 @@ scales, dA*dW2 [E]; SiTU(g, u) = (4 tanh(g/4) sigmoid(g)) * (25 tanh(u/25)), wit
 optional per-expert float32 situ_beta / situ_linear_beta replacing 4 / 25.
 "Nvfp4 Tensor": the per-expert global scale multiplies after block dequantization.
 
-Readings (R13-R17):
+Readings where the pages are silent:
   * FC1 rows [0, I) are the gate g, rows [I, 2I) the up projection u.
   * An FC dot product is computed exactly (see ``fc_exact``), rounded once to fp32,
     then multiplied by the per-expert alpha in fp32.
@@ -236,7 +236,7 @@ def intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, al
 
 def calibrate_intermediate(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
                            beta=None, lam=None, weight_cache=None):
-    """Reading R18: one shared dA = amax|SiTU output| / 2688 over a calibration set of
+    """Reading taken: one shared dA = amax|SiTU output| / 2688 over a calibration set of
     tokens, expanded to [E] (the page asks for a shared intermediate scale expanded to an
     [E] tensor during model preparation).  Returns (dA [E], qA [E]) float32."""
     E = w13.shape[0]

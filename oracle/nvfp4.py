@@ -8,7 +8,7 @@ activation encoding scale qX = 1/dX, per-expert qA = 1/dA, E4M3 block scales (on
 16 values: FC1 scales are [.., 3584/16], FC2 scales [.., 384/16]).  "Nvfp4 Tensor":
 the global scale multiplies after block dequantization.
 
-The pages do not give the block-scale arithmetic.  Reading R6 (the plainest one that
+The pages do not give the block-scale arithmetic.  The reading taken (the plainest one that
 fits those facts; every step in IEEE fp32, left to right):
 
     amax  = max |v_i|                      over the 16 values of the block
@@ -69,7 +69,7 @@ def dequantize_nvfp4(codes, scales):
 
 def pack_nibbles(codes):
     """Two codes per byte along the last axis: element 2b in the low nibble of byte b
-    (reading R7; "Nvfp4 Tensor" only says eight FP4 values share a 32-bit word)."""
+    (a reading; "Nvfp4 Tensor" only says eight FP4 values share a 32-bit word)."""
     c = np.asarray(codes, dtype=np.uint8) & 0xF
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 

@@ -12,7 +12,7 @@ Follows "torch_npu.npu_moe_init_routing_v2" (Ascend API reference), section ËÆ°Á
   step 5  with the full expert range active, tokens move by the scatter index:
           expandedX[i] = quant[sortedRowIdx[i] // K]
 
-rowIdx is the flat index f = t*K + j of expert_idx[t, j].  Readings (R9-R12):
+rowIdx is the flat index f = t*K + j of expert_idx[t, j].  Readings where the page is silent:
   * keyValueSort is stable: equal experts keep increasing f (the workload asks for a
     stable sort; the page does not say).
   * the histogram output is the inclusive prefix sum with one entry per expert.
@@ -71,3 +71,160 @@ def route_int8(x_f32, expert_ids, num_experts):
     r["expanded_scale"] = scale[src_token]
     r["row_scale"] = scale
     return r
+
+
+# ---------------------------------------------------------------------------------------
+# The options of the same page beyond the defaults (section ËÆ°ÁÆóÂÖ¨Âºè steps 1-6 and the
+# parameter list): scatter index type, count and key_value histograms, an active expert
+# range with availableIdxNum, static int8 quant, drop/pad to an expert capacity, and
+# active_num.  Readings where the page is silent or loose:
+#   * ids outside the active range [start, end) take no part: the sort of step 1 keeps
+#     the in-range ids in their sorted order and they occupy positions 0..avail-1.
+#   * row_idx_type 1: entries past availableIdxNum are left unwritten by the page; here
+#     they are -1 (a defined value is one of the allowed contents).
+#   * histogram mode 1 is the per-expert count and mode 2 the (expert id, count) pairs of
+#     the in-range experts with a nonzero count, in increasing expert id, at the head of
+#     an [expert_num, 2] array whose other rows are 0.  The histogram counts every
+#     in-range id, also ids that drop/pad or active_num later drop.
+#   * static quant: q = round_half_even(fp32(fp32(x * scale) + offset)), saturated to
+#     [-128, 127]; scale and offset are fp32 scalars.
+#   * drop/pad: expert e's routed rows in sorted order take slots e*C + r, r < C; the
+#     gather index of a dropped row is -1; unfilled slots are 0 (scale 0).  Only the
+#     gather index type is defined with drop/pad (the scatter index of [E*C] slots has no
+#     place in an [N*K] output); active_num does not apply to it.
+#   * active_num > 0 keeps expanded rows 0..active_num-1; the index outputs and the
+#     histogram are unaffected.  0 and -1 mean no limit.
+#   * the non-quant mode with a per-row scale [N] moves that scale like the dynamic
+#     quant scale.
+# ---------------------------------------------------------------------------------------
+
+
+def int8_static_quant(x_f32, scale, offset):
+    """Step 4, static mode: round(x*scale + offset) per element, in fp32, to int8."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    y = (x * np.float32(scale)).astype(np.float32)
+    y = (y + np.float32(offset)).astype(np.float32)
+    return np.clip(np.rint(y), -128, 127).astype(np.int8)
+
+
+def route_v2(x_f32, expert_ids, expert_num, *, expert_range=None, row_idx_type=0,
+             tokens_num_type=0, quant_mode=-1, scale=None, offset=None, drop_pad_mode=0,
+             expert_capacity=-1, active_num=-1):
+    """All six steps for x [N, H] (fp32 values of the BF16 input; None when only the
+    index outputs are wanted) and expert_ids [N, K].
+
+    Returns a dict: sorted_row_idx (the in-range part of the stable sort, [avail]),
+    expanded_row_idx [N*K], expert_tokens (mode 0/1: [end-start]; mode 2: [expert_num, 2]),
+    available_idx_num, and with x: expanded_x (rows valid: "valid_rows") and, for the
+    dynamic mode or a per-row scale in mode -1, expanded_scale.
+    """
+    ids = np.asarray(expert_ids)
+    N, K = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    n = flat.size
+    if flat.size and (flat.min() < 0 or flat.max() >= expert_num):
+        raise ValueError("expert id out of range")
+    start, end = (0, expert_num) if expert_range is None else expert_range
+    if not 0 <= start < end <= expert_num:
+        raise ValueError("bad active expert range")
+    if drop_pad_mode and (start, end) != (0, expert_num):
+        raise ValueError("drop/pad needs the full expert range")
+    if drop_pad_mode and row_idx_type != 0:
+        raise ValueError("drop/pad is defined with the gather index only")
+    E_act = end - start
+
+    # step 1: stable key-value sort; the in-range ids stay at the head in sorted order
+    order = np.argsort(flat, kind="stable")
+    keep = (flat[order] >= start) & (flat[order] < end)
+    sorted_row_idx = order[keep]
+    avail = sorted_row_idx.size                                # step 6
+    sorted_ids = flat[sorted_row_idx]
+
+    # step 3: histogram of the in-range sorted experts
+    counts = np.bincount(sorted_ids - start, minlength=E_act).astype(np.int64)
+    if tokens_num_type == 0:
+        expert_tokens = np.cumsum(counts)
+    elif tokens_num_type == 1:
+        expert_tokens = counts.copy()
+    elif tokens_num_type == 2:
+        expert_tokens = np.zeros((expert_num, 2), np.int64)
+        nz = np.nonzero(counts)[0]
+        expert_tokens[:nz.size, 0] = nz + start
+        expert_tokens[:nz.size, 1] = counts[nz]
+    else:
+        raise ValueError("bad tokens_num_type")
+
+    # rank of each sorted position inside its expert (for drop/pad)
+    first = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rank = np.arange(avail) - first[sorted_ids - start]
+
+    # step 2: the position map
+    gather = np.full(n, -1, np.int64)
+    if drop_pad_mode:
+        C = expert_capacity
+        if C < 1:
+            raise ValueError("drop/pad needs expert_capacity >= 1")
+        kept = rank < C
+        gather[sorted_row_idx[kept]] = (sorted_ids[kept] - start) * C + rank[kept]
+    else:
+        gather[sorted_row_idx] = np.arange(avail)
+    if row_idx_type == 1:
+        expanded_row_idx = np.full(n, -1, np.int64)
+        expanded_row_idx[:avail] = sorted_row_idx
+    else:
+        expanded_row_idx = gather
+
+    out = {
+        "sorted_row_idx": sorted_row_idx.astype(np.int32),
+        "expanded_row_idx": expanded_row_idx.astype(np.int32),
+        "expert_tokens": expert_tokens.astype(np.int32),
+        "available_idx_num": int(avail),
+    }
+    if x_f32 is None:
+        return out
+
+    # step 4: quantization of the token rows
+    x = np.asarray(x_f32, dtype=np.float32)
+    H = x.shape[1]
+    row_scale = None
+    if quant_mode == -1:
+        src = x
+        if scale is not None:
+            row_scale = np.asarray(scale, np.float32).reshape(N)
+    elif quant_mode == 0:
+        src = int8_static_quant(x, scale, offset)
+    elif quant_mode == 1:
+        src, row_scale = int8_row_quant(x)
+    else:
+        raise ValueError("bad quant_mode")
+
+    # step 5: token movement
+    if drop_pad_mode:
+        rows = end * expert_capacity
+        valid_rows = rows
+    else:
+        rows = n if active_num <= 0 else min(active_num, n)
+        valid_rows = min(avail, rows)
+    ex = np.zeros((rows, H), src.dtype)
+    es = np.zeros(rows, np.float32) if row_scale is not None else None
+    if (start, end) == (0, expert_num) and not drop_pad_mode:
+        for i in range(valid_rows):                        # by the scatter index
+            ex[i] = src[sorted_row_idx[i] // K]
+            if es is not None:
+                es[i] = row_scale[sorted_row_idx[i] // K]
+    else:
+        for f in range(n):                                 # by the gather index
+            d = gather[f]
+            if 0 <= d < rows:
+                ex[d] = src[f // K]
+                if es is not None:
+                    es[d] = row_scale[f // K]
+    if drop_pad_mode:
+        ex = ex.reshape(end, expert_capacity, H)
+        if es is not None:
+            es = es.reshape(end, expert_capacity)
+    out["expanded_x"] = ex
+    out["valid_rows"] = int(valid_rows)
+    if es is not None:
+        out["expanded_scale"] = es
+    return out
