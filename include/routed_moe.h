@@ -100,7 +100,7 @@ typedef struct {
 
 moe_status_t moe_workspace_layout(moe_dims_t d, int32_t T, moe_workspace_layout_t* out /*host*/);
 
-/* Workspace bytes of moe_route for num_rows tokens, top_k, num_experts. */
+/* Workspace bytes of moe_route and moe_route_v2 for num_rows tokens, top_k, num_experts. */
 moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t num_experts,
                                       size_t* bytes /*host*/);
 
@@ -160,6 +160,57 @@ moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, in
                        int32_t* expert_cumsum, int32_t* sorted_expert_idx,
                        int32_t* sorted_row_idx, void* workspace, size_t workspace_bytes,
                        moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * The routing primitive with the options of the same page ("torch_npu.
+ * npu_moe_init_routing_v2": section 计算公式 steps 1-6 and the parameter list).
+ *
+ *   expert_start, expert_end  active expert range [start, end) (0, 0 = all experts).
+ *        Ids outside it take no part: the in-range ids, stably sorted, occupy positions
+ *        0 .. avail-1, avail = availableIdxNum = the number of in-range ids (step 6).
+ *   row_idx_type  0: expanded_row_idx[f] = position of flat id f (gather index), -1 for
+ *        an out-of-range id;  1: expanded_row_idx[i] = flat id at position i (scatter
+ *        index), -1 for i >= avail (the page leaves those unwritten).
+ *   expert_tokens_num_type  (step 3, over the range, counting every in-range id)
+ *        0: inclusive cumsum [end-start];  1: per-expert count [end-start];
+ *        2: key_value [num_experts, 2] = (expert id, count) of the in-range experts with
+ *        a nonzero count, increasing id, then rows of 0.
+ *   quant_mode  -1: BF16 copy (with a per-row scale [N] given as `scale`, expanded_scale
+ *        [i] = scale[row of i]);  0: static int8, q = clip(round_half_even(fp32(fp32(
+ *        x * scale[0]) + offset[0])), -128, 127), no expanded_scale;  1: dynamic int8
+ *        exactly as moe_route (expanded_scale required).
+ *   drop_pad_mode 1 with expert_capacity C (1 <= C <= N*K; needs the full range, the
+ *        gather index and active_num <= 0): expanded_x is [num_experts, C, H]; expert e's
+ *        rows in sorted order fill slots e*C + r for r < C, later rows are dropped
+ *        (expanded_row_idx -1), empty slots are 0 (expanded_scale 0).
+ *   active_num  > 0: only expanded rows 0 .. active_num-1 exist (expanded_x is
+ *        [min(active_num, N*K), H]); <= 0: no limit.  Index outputs are unaffected.
+ *
+ * Buffers (device): x BF16 [N, H]; expert_idx i32 [N, K] with values in [0, num_experts);
+ * scale, offset f32 as above (else NULL); expanded_x as above (BF16 or int8; rows past
+ * the valid ones are left untouched except drop/pad's zero slots); expanded_row_idx i32
+ * [N*K]; expert_tokens i32 as above or NULL; expanded_scale f32 [rows of expanded_x] or
+ * NULL; available_idx_num i32 [1] or NULL.  workspace: moe_route_workspace_size() bytes.
+ * Limits as moe_route (num_experts <= 4096 where the page allows 10240).  The
+ * smoothing-scale variant of the dynamic mode is not offered.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t expert_start;
+  int32_t expert_end;
+  int32_t row_idx_type;
+  int32_t expert_tokens_num_type;
+  int32_t quant_mode;
+  int32_t drop_pad_mode;
+  int32_t expert_capacity;
+  int32_t active_num;
+} moe_route_options_t;
+
+moe_status_t moe_route_v2(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
+                          const uint16_t* x, const int32_t* expert_idx, const float* scale,
+                          const float* offset, const moe_route_options_t* opts /*host*/,
+                          void* expanded_x, int32_t* expanded_row_idx, int32_t* expert_tokens,
+                          float* expanded_scale, int32_t* available_idx_num, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * The whole layer ("Cake SiTU backend": intro for the stages; section "Prepared weights

@@ -108,7 +108,7 @@ def int8_static_quant(x_f32, scale, offset):
 
 
 def route_v2(x_f32, expert_ids, expert_num, *, expert_range=None, row_idx_type=0,
-             tokens_num_type=0, quant_mode=-1, scale=None, offset=None, drop_pad_mode=0,
+             expert_tokens_num_type=0, quant_mode=-1, scale=None, offset=None, drop_pad_mode=0,
              expert_capacity=-1, active_num=-1):
     """All six steps for x [N, H] (fp32 values of the BF16 input; None when only the
     index outputs are wanted) and expert_ids [N, K].
@@ -142,17 +142,17 @@ def route_v2(x_f32, expert_ids, expert_num, *, expert_range=None, row_idx_type=0
 
     # step 3: histogram of the in-range sorted experts
     counts = np.bincount(sorted_ids - start, minlength=E_act).astype(np.int64)
-    if tokens_num_type == 0:
+    if expert_tokens_num_type == 0:
         expert_tokens = np.cumsum(counts)
-    elif tokens_num_type == 1:
+    elif expert_tokens_num_type == 1:
         expert_tokens = counts.copy()
-    elif tokens_num_type == 2:
+    elif expert_tokens_num_type == 2:
         expert_tokens = np.zeros((expert_num, 2), np.int64)
         nz = np.nonzero(counts)[0]
         expert_tokens[:nz.size, 0] = nz + start
         expert_tokens[:nz.size, 1] = counts[nz]
     else:
-        raise ValueError("bad tokens_num_type")
+        raise ValueError("bad expert_tokens_num_type")
 
     # rank of each sorted position inside its expert (for drop/pad)
     first = np.concatenate([[0], np.cumsum(counts)[:-1]])

@@ -14,8 +14,8 @@ import os
 __all__ = [
     "MoeError", "MoeDims", "library_path", "moe_status_string", "moe_workspace_size",
     "moe_prepared_weights_size", "moe_workspace_layout", "moe_route_workspace_size",
-    "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_forward",
-    "moe_forward_timed", "MOE_FORWARD_STAGES",
+    "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_route_v2",
+    "MoeRouteOptions", "moe_forward", "moe_forward_timed", "MOE_FORWARD_STAGES",
     "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
 ]
 
@@ -30,7 +30,8 @@ MOE_FORWARD_STAGES = 5
 # Every symbol include/routed_moe.h declares.
 EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_size",
             "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
-            "moe_prepare_weights", "moe_route", "moe_forward", "moe_forward_timed")
+            "moe_prepare_weights", "moe_route", "moe_route_v2", "moe_forward",
+            "moe_forward_timed")
 
 
 class MoeError(RuntimeError):
@@ -45,6 +46,19 @@ class MoeDims(ctypes.Structure):
 
     def __init__(self, hidden, inter, num_experts, top_k):
         super().__init__(hidden, inter, num_experts, top_k)
+
+
+class MoeRouteOptions(ctypes.Structure):
+    """moe_route_options_t: the routing primitive's options (defaults: all experts, gather
+    index, cumsum histogram, no quant, dropless, no capacity, no row limit)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "expert_start", "expert_end", "row_idx_type", "expert_tokens_num_type", "quant_mode",
+        "drop_pad_mode", "expert_capacity", "active_num")]
+
+    def __init__(self, expert_start=0, expert_end=0, row_idx_type=0, expert_tokens_num_type=0,
+                 quant_mode=-1, drop_pad_mode=0, expert_capacity=-1, active_num=-1):
+        super().__init__(expert_start, expert_end, row_idx_type, expert_tokens_num_type,
+                         quant_mode, drop_pad_mode, expert_capacity, active_num)
 
 
 class _Layout(ctypes.Structure):
@@ -75,6 +89,8 @@ def _lib():
             "moe_quantize_nvfp4": (st, [P, I64, I64, I32, P, P, P, P]),
             "moe_prepare_weights": (st, [MoeDims, P, P, P, P, P, SZ, P]),
             "moe_route": (st, [I32, I32, I32, I32, P, P, ctypes.c_int, P, P, P, P, P, P, P, SZ, P]),
+            "moe_route_v2": (st, [I32, I32, I32, I32, P, P, P, P,
+                                  ctypes.POINTER(MoeRouteOptions), P, P, P, P, P, P, SZ, P]),
             "moe_forward": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]),
             "moe_forward_timed": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P,
                                        ctypes.POINTER(P)]),
@@ -170,6 +186,18 @@ def moe_route(num_rows, hidden, num_experts, top_k, x, expert_idx, quant, expand
         num_rows, hidden, num_experts, top_k, _ptr(x), _ptr(expert_idx), quant, _ptr(expanded_x),
         _ptr(expanded_scale), _ptr(expanded_row_idx), _ptr(expert_cumsum),
         _ptr(sorted_expert_idx), _ptr(sorted_row_idx), _ptr(workspace), nb, _stream(stream)))
+
+
+def moe_route_v2(num_rows, hidden, num_experts, top_k, x, expert_idx, options, expanded_x,
+                 expanded_row_idx, expert_tokens=None, expanded_scale=None,
+                 available_idx_num=None, scale=None, offset=None, workspace=None,
+                 workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_route_v2", _lib().moe_route_v2(
+        num_rows, hidden, num_experts, top_k, _ptr(x), _ptr(expert_idx), _ptr(scale),
+        _ptr(offset), ctypes.byref(options), _ptr(expanded_x), _ptr(expanded_row_idx),
+        _ptr(expert_tokens), _ptr(expanded_scale), _ptr(available_idx_num), _ptr(workspace),
+        nb, _stream(stream)))
 
 
 def moe_forward(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,

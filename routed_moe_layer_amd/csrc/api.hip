@@ -126,6 +126,7 @@ moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t n
   c.take(static_cast<size_t>(route_tiles(n)) * num_experts * 4);   // tile histograms
   c.take(static_cast<size_t>(num_experts) * 4);                     // counts
   c.take(static_cast<size_t>(num_experts + 1) * 4);                 // offsets
+  c.take(static_cast<size_t>(n) * 4);                               // position map (v2)
   *bytes = c.off;
   return MOE_OK;
 }
@@ -188,7 +189,84 @@ moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, in
   hipError_t e = launch_route(expert_idx, n, num_experts, b, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_route_permute(x, num_rows, hidden, top_k, static_cast<int>(quant), expanded_row_idx,
-                           expanded_x, expanded_scale, s);
+                           INT64_MAX, nullptr, nullptr, nullptr, expanded_x, expanded_scale, s);
+  return hip_status(e);
+}
+
+moe_status_t moe_route_v2(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
+                          const uint16_t* x, const int32_t* expert_idx, const float* scale,
+                          const float* offset, const moe_route_options_t* opts,
+                          void* expanded_x, int32_t* expanded_row_idx, int32_t* expert_tokens,
+                          float* expanded_scale, int32_t* available_idx_num, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream) {
+  size_t need = 0;
+  moe_status_t st = moe_route_workspace_size(num_rows, top_k, num_experts, &need);
+  if (st != MOE_OK) return st;
+  if (!opts) return MOE_ERR_INVALID_ARG;
+  if (hidden < 8 || hidden % 8 || hidden > 65536) return MOE_ERR_UNSUPPORTED;
+  const moe_route_options_t o = *opts;
+  int start = o.expert_start, end = o.expert_end;
+  if (start == 0 && end == 0) end = num_experts;
+  if (start < 0 || end <= start || end > num_experts) return MOE_ERR_INVALID_ARG;
+  if (o.row_idx_type != 0 && o.row_idx_type != 1) return MOE_ERR_INVALID_ARG;
+  if (o.expert_tokens_num_type < 0 || o.expert_tokens_num_type > 2) return MOE_ERR_INVALID_ARG;
+  if (o.quant_mode < -1 || o.quant_mode > 1) return MOE_ERR_INVALID_ARG;
+  if (o.drop_pad_mode != 0 && o.drop_pad_mode != 1) return MOE_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(num_rows) * top_k;
+  const bool drop_pad = o.drop_pad_mode == 1;
+  if (drop_pad) {
+    if (start != 0 || end != num_experts || o.row_idx_type != 0 || o.active_num > 0)
+      return MOE_ERR_INVALID_ARG;
+    if (o.expert_capacity < 1 || o.expert_capacity > n) return MOE_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(num_experts) * o.expert_capacity > INT32_MAX)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (!x || !expert_idx || !expanded_x || !expanded_row_idx || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (o.quant_mode == 0 && (!scale || !offset)) return MOE_ERR_INVALID_ARG;
+  if (o.quant_mode == 1 && !expanded_scale) return MOE_ERR_INVALID_ARG;
+  if (o.quant_mode == -1 && scale && !expanded_scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(expanded_x, 16) || !aligned(workspace, kAlign) ||
+      !aligned(expert_idx, 4) || !aligned(expanded_row_idx, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int E_act = end - start;
+  Carver c;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  RouteBuffers b{};
+  b.tile_hist = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(route_tiles(n)) * num_experts * 4));
+  b.counts = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts) * 4));
+  b.offsets = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts + 1) * 4));
+  int32_t* map = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(n) * 4));
+  b.e_base = start;
+  b.capacity = drop_pad ? o.expert_capacity : 0;
+  b.available = available_idx_num;
+  if (o.row_idx_type == 1) {
+    b.sorted_row_idx = expanded_row_idx;      // the scatter index
+  } else {
+    map = expanded_row_idx;                   // the gather index is the position map
+  }
+  b.expanded_row_idx = map;
+  if (expert_tokens) {
+    if (o.expert_tokens_num_type == 0) b.cumsum = expert_tokens;
+    else if (o.expert_tokens_num_type == 1) b.counts = expert_tokens;
+    else { b.key_value = expert_tokens; b.kv_rows = num_experts; }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_route(expert_idx, n, E_act, b, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int quant = o.quant_mode == -1 ? 0 : (o.quant_mode == 1 ? 1 : 2);
+  const int64_t limit = drop_pad ? static_cast<int64_t>(num_experts) * o.expert_capacity
+                                 : (o.active_num > 0 ? o.active_num : INT64_MAX);
+  e = launch_route_permute(x, num_rows, hidden, top_k, quant, map, limit,
+                           o.quant_mode == -1 ? scale : nullptr, scale, offset, expanded_x,
+                           expanded_scale, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (drop_pad) {
+    const int64_t row_bytes = static_cast<int64_t>(hidden) * (quant == 0 ? 2 : 1);
+    e = launch_route_pad_fill(b.counts, num_experts, o.expert_capacity, row_bytes, expanded_x,
+                              quant == 1 || (quant == 0 && scale) ? expanded_scale : nullptr, s);
+  }
   return hip_status(e);
 }
 

@@ -41,25 +41,44 @@ hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t ro
                                  uint16_t* decoded, hipStream_t stream);
 
 // Routing: histogram, scan (+ optional GEMM tile list and stats reset), stable scatter.
+// The E experts routed are ids e_base .. e_base + E - 1 (an active expert range); other
+// ids take no part.  Positions i of the sort run over the in-range ids only.
 struct RouteBuffers {
   int32_t* tile_hist;        // [route_tiles(n), E]
   int32_t* counts;           // [E]
-  int32_t* offsets;          // [E + 1] exclusive
+  int32_t* offsets;          // [E + 1] exclusive; offsets[E] = number of in-range ids
   int32_t* cumsum;           // [E] inclusive (may be null)
-  int32_t* sorted_ids;       // [n] (may be null)
-  int32_t* sorted_row_idx;   // [n] (may be null)
-  int32_t* expanded_row_idx; // [n]
+  int32_t* sorted_ids;       // [n] absolute expert ids; entries >= offsets[E] are -1 (or null)
+  int32_t* sorted_row_idx;   // [n] flat ids; entries >= offsets[E] are -1 (or null)
+  int32_t* expanded_row_idx; // [n] position map: sorted position of f, -1 out of range
   TileDesc* tiles_small;     // [max_small_tiles] or null
   TileDesc* tiles_big;       // [max_big_tiles] or null
   int32_t* num_tiles;        // [2]: small, big; or null
   float* amax_reset;         // [E] zeroed by the scan kernel, or null
+  int32_t* key_value;        // [kv_rows, 2]: (expert id, count) of the experts with a
+                             // nonzero count in increasing id, then zero rows; or null.
+                             // Never together with the tile lists.
+  int32_t* available;        // [1] number of in-range ids, or null
+  int32_t kv_rows;
+  int32_t e_base;
+  int32_t capacity;          // > 0: the position map holds slot e*capacity + rank within
+                             // the expert, or -1 when rank >= capacity
 };
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
                         hipStream_t stream);
 
+// Token movement of the routing primitive: token row t goes to rows map[t*K + j] (skipped
+// when negative or >= limit).  quant 0: BF16 copy (plus row_scale[t] to expanded_scale
+// when both are given); 1: dynamic int8 with its scale; 2: static int8 with the device
+// scalars *static_scale and *static_offset.
 hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
-                                const int32_t* expanded_row_idx, void* expanded_x,
-                                float* expanded_scale, hipStream_t stream);
+                                const int32_t* map, int64_t limit, const float* row_scale,
+                                const float* static_scale, const float* static_offset,
+                                void* expanded_x, float* expanded_scale, hipStream_t stream);
+// Drop/pad: zero the slots of expert e at and past counts[e] (rows of row_bytes bytes,
+// a multiple of 8; scale 0 when expanded_scale is given), for E experts of C slots each.
+hipError_t launch_route_pad_fill(const int32_t* counts, int E, int C, int64_t row_bytes,
+                                 void* expanded_x, float* expanded_scale, hipStream_t stream);
 
 hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
                                   const uint8_t* w13_sf, const uint8_t* w2,

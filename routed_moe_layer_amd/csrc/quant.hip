@@ -60,9 +60,13 @@ hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t ro
 }
 
 // ---------------------------------------------------------------------------------------
-// Token movement for the routing primitive.  quant == 1: dynamic int8 per row,
-//   scale = fp32(row_max|x| / 127); q = clip(rint(fp32(x / scale)), -127, 127).
-// quant == 0: BF16 copy.  Rows are written to expanded_row_idx[t*K + j], j < K.
+// Token movement for the routing primitive ("torch_npu.npu_moe_init_routing_v2", section
+// 计算公式 steps 4-5).  One workgroup per token row t; the row goes to rows map[t*K + j]
+// (skipped when negative or >= limit).
+//   quant 0: BF16 copy; with row_scale, expanded_scale[row] = row_scale[t].
+//   quant 1: dynamic int8 per row, scale = fp32(row_max|x| / 127),
+//            q = clip(rint(fp32(x / scale)), -127, 127) (0 when scale is 0).
+//   quant 2: static int8, q = clip(rint(fp32(fp32(x * s) + o)), -128, 127).
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -74,16 +78,42 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
+// Static quantization of one value: the product and the sum are rounded to fp32 one at a
+// time (no fused multiply-add), then rounded half to even and saturated.
+__device__ __forceinline__ float static_int8(float x, float s, float o) {
+#pragma clang fp contract(off)
+  const float y = x * s + o;
+  return fminf(fmaxf(rintf(y), -128.0f), 127.0f);
+}
+
+// Eight BF16 values (one 16-byte vector) to eight int8 codes through q().
+template <class Q>
+__device__ __forceinline__ uint2 quant8(uint4 d, Q q) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
+    const float qf = q(__uint_as_float(bits));
+    packed[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+
 __global__ __launch_bounds__(256) void route_permute_kernel(
-    const uint16_t* __restrict__ x, int H, int K, int quant,
-    const int32_t* __restrict__ expanded_row_idx, void* __restrict__ expanded_x,
+    const uint16_t* __restrict__ x, int H, int K, int quant, const int32_t* __restrict__ map,
+    int64_t limit, const float* __restrict__ row_scale, const float* __restrict__ static_scale,
+    const float* __restrict__ static_offset, void* __restrict__ expanded_x,
     float* __restrict__ expanded_scale) {
   __shared__ float red[4];
   __shared__ int32_t dst[64];
   const int64_t t = blockIdx.x;
   const uint16_t* xr = x + t * H;
   const int nvec = H / 8;                   // 16-byte vectors of 8 BF16
-  if (threadIdx.x < K) dst[threadIdx.x] = expanded_row_idx[t * K + threadIdx.x];
+  if (threadIdx.x < K) {
+    const int32_t d = map[t * K + threadIdx.x];
+    dst[threadIdx.x] = (d >= 0 && d < limit) ? d : -1;
+  }
   if (quant == 0) {
     __syncthreads();
     for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
@@ -94,6 +124,23 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
         reinterpret_cast<uint4*>(o)[v] = d;
       }
     }
+    if (row_scale && expanded_scale && threadIdx.x < K && dst[threadIdx.x] >= 0)
+      expanded_scale[dst[threadIdx.x]] = row_scale[t];
+    return;
+  }
+  auto store8 = [&](int v, uint2 pv) {
+    for (int j = 0; j < K; ++j) {
+      if (dst[j] < 0) continue;
+      int8_t* o = static_cast<int8_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
+      reinterpret_cast<uint2*>(o)[v] = pv;
+    }
+  };
+  if (quant == 2) {
+    const float s = static_scale[0], off = static_offset[0];
+    __syncthreads();
+    for (int v = threadIdx.x; v < nvec; v += blockDim.x)
+      store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v],
+                       [=](float xv) { return static_int8(xv, s, off); }));
     return;
   }
   float amax = 0.0f;
@@ -108,35 +155,49 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
   }
   amax = block_max(amax, red);            // includes the __syncthreads for dst[]
   const float scale = amax / 127.0f;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    uint4 d = reinterpret_cast<const uint4*>(xr)[v];
-    uint32_t w[4] = {d.x, d.y, d.z, d.w};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
-      float xv = __uint_as_float(bits);
-      float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
-      qf = fminf(fmaxf(qf, -127.0f), 127.0f);
-      uint32_t qb = static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu;
-      packed[i >> 2] |= qb << (8 * (i & 3));
-    }
-    uint2 pv = make_uint2(packed[0], packed[1]);
-    for (int j = 0; j < K; ++j) {
-      if (dst[j] < 0) continue;
-      int8_t* o = static_cast<int8_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
-      reinterpret_cast<uint2*>(o)[v] = pv;
-    }
-  }
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x)
+    store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v], [=](float xv) {
+             const float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
+             return fminf(fmaxf(qf, -127.0f), 127.0f);
+           }));
   if (threadIdx.x < K && dst[threadIdx.x] >= 0) expanded_scale[dst[threadIdx.x]] = scale;
 }
 
 hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
-                                const int32_t* expanded_row_idx, void* expanded_x,
-                                float* expanded_scale, hipStream_t stream) {
+                                const int32_t* map, int64_t limit, const float* row_scale,
+                                const float* static_scale, const float* static_offset,
+                                void* expanded_x, float* expanded_scale, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   route_permute_kernel<<<dim3(static_cast<unsigned>(N)), dim3(256), 0, stream>>>(
-      x, H, K, quant, expanded_row_idx, expanded_x, expanded_scale);
+      x, H, K, quant, map, limit, row_scale, static_scale, static_offset, expanded_x,
+      expanded_scale);
+  return hipGetLastError();
+}
+
+// Drop/pad ("torch_npu.npu_moe_init_routing_v2", step 5: experts with fewer rows than the
+// capacity are filled with zeros).  Workgroup (x, e) zeroes slots counts[e] + x,
+// counts[e] + x + gridDim.x, ... of expert e.
+__global__ __launch_bounds__(256) void route_pad_fill_kernel(const int32_t* __restrict__ counts,
+                                                             int C, int64_t row_bytes,
+                                                             void* __restrict__ expanded_x,
+                                                             float* __restrict__ expanded_scale) {
+  const int e = blockIdx.y;
+  const int first = min(max(counts[e], 0), C);
+  const int64_t words = row_bytes / 8;
+  for (int s = first + static_cast<int>(blockIdx.x); s < C; s += gridDim.x) {
+    const int64_t slot = static_cast<int64_t>(e) * C + s;
+    uint2* row = reinterpret_cast<uint2*>(static_cast<uint8_t*>(expanded_x) + slot * row_bytes);
+    for (int64_t v = threadIdx.x; v < words; v += blockDim.x) row[v] = make_uint2(0u, 0u);
+    if (expanded_scale && threadIdx.x == 0) expanded_scale[slot] = 0.0f;
+  }
+}
+
+hipError_t launch_route_pad_fill(const int32_t* counts, int E, int C, int64_t row_bytes,
+                                 void* expanded_x, float* expanded_scale, hipStream_t stream) {
+  if (E == 0 || C == 0) return hipSuccess;
+  const unsigned gx = static_cast<unsigned>(C < 64 ? C : 64);
+  route_pad_fill_kernel<<<dim3(gx, static_cast<unsigned>(E)), dim3(256), 0, stream>>>(
+      counts, C, row_bytes, expanded_x, expanded_scale);
   return hipGetLastError();
 }
 

@@ -3,10 +3,13 @@
 // "torch_npu.npu_moe_init_routing_v2" (section 计算公式): step 1 keyValueSort(expertIdx,
 // rowIdx), step 2 the gather map expandedRowIdx[sortedRowIdx[i]] = i, step 3 the
 // per-expert histogram as an inclusive prefix sum.  The sort must be stable (equal experts
-// keep increasing f) so that the result is unique.
+// keep increasing f) so that the result is unique.  The same page's options are handled
+// here too: an active expert range (ids outside it take no part; step 6's
+// availableIdxNum is the in-range count), the count and key_value histogram modes, and
+// drop/pad slots e*capacity + rank (-1 past the capacity).
 //
-// Three launches (one for at most kRouteTile ids, see route_small_kernel), no host readback ("Cake SiTU backend", intro: routing values never take
-// part in host dispatch):
+// Three launches (one for at most kRouteTile ids, see route_small_kernel), no host
+// readback ("Cake SiTU backend", intro: routing values never take part in host dispatch):
 //   hist    : one workgroup per tile of 1024 flat ids; LDS histogram -> tile_hist[tile][e].
 //   scan    : one workgroup; per expert, exclusive scan of tile_hist over tiles (in place),
 //             counts, exclusive/inclusive expert offsets; optionally the two grouped-GEMM
@@ -24,34 +27,46 @@ constexpr int kIdsPerThread = kRouteTile / kRouteThreads;   // 4
 constexpr int kScanBatch = 16;
 constexpr size_t kRouteSmallMaxLds = 64 * 1024;   // dynamic LDS of the fused small kernel
 
+// Key of flat id f: its expert id relative to the first routed expert (unsigned wrap, so
+// ids below the range come out >= E); -1 past the end of the ids.
+__device__ __forceinline__ int route_key(const int32_t* __restrict__ ids, int64_t f, int64_t n,
+                                         int e_base) {
+  return f < n ? static_cast<int>(static_cast<uint32_t>(ids[f]) - static_cast<uint32_t>(e_base))
+               : -1;
+}
+__device__ __forceinline__ bool key_valid(int e, int E) {
+  return static_cast<unsigned>(e) < static_cast<unsigned>(E);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ tile_hist) {
+    const int32_t* __restrict__ ids, int64_t n, int E, int e_base,
+    int32_t* __restrict__ tile_hist) {
   extern __shared__ int32_t hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kRouteTile;
   for (int i = threadIdx.x; i < kRouteTile; i += blockDim.x) {
-    int64_t f = base + i;
-    if (f < n) {
-      const int e = ids[f];
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&hist[e], 1);
-    }
+    const int e = route_key(ids, base + i, n, e_base);
+    if (key_valid(e, E)) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
   int32_t* out = tile_hist + static_cast<int64_t>(blockIdx.x) * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
 }
 
-// The three per-expert quantities the expert scans need (rows, small tiles, big tiles),
-// packed into 21-bit fields of one 64-bit value so that one block scan serves all three
-// (every field's total stays below 2^21: at most MOE_MAX_TOKENS * 64 = 2^20 rows per call,
-// at most 4096 small and 2^13 + 4096 big tiles).
+// The three per-expert quantities the expert scans need, packed into one 64-bit value so
+// that one block scan serves all three: rows (26 bits; at most 2^24 ids per call), small
+// tiles or nonzero experts (19 bits; at most 4096), big tiles (19 bits; at most
+// 2^20 / kBigRows + 4096 for the layer's 2^20 routed rows).
+constexpr int kRowBits = 26, kTileBits = 19;
 __device__ __forceinline__ uint64_t pack_counts(int cnt, int n_small, int n_big) {
-  return static_cast<uint64_t>(cnt) | (static_cast<uint64_t>(n_small) << 21) |
-         (static_cast<uint64_t>(n_big) << 42);
+  return static_cast<uint64_t>(cnt) | (static_cast<uint64_t>(n_small) << kRowBits) |
+         (static_cast<uint64_t>(n_big) << (kRowBits + kTileBits));
 }
 __device__ __forceinline__ int field(uint64_t v, int i) {
-  return static_cast<int>((v >> (21 * i)) & ((1u << 21) - 1));
+  const int shift = i == 0 ? 0 : kRowBits + (i - 1) * kTileBits;
+  const int bits = i == 0 ? kRowBits : kTileBits;
+  return static_cast<int>((v >> shift) & ((uint64_t{1} << bits) - 1));
 }
 
 // Block-wide exclusive scan of one uint64 per thread (any multiple of 64 threads up to
@@ -92,16 +107,64 @@ __device__ __forceinline__ void expert_tiles(int cnt, int* n_small, int* n_big, 
   *n_big = (cnt + b - 1) / b;
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(
-    int32_t* __restrict__ tile_hist, int ntiles, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum,
-    TileDesc* __restrict__ tiles_small, TileDesc* __restrict__ tiles_big,
-    int32_t* __restrict__ num_tiles, float* __restrict__ amax_reset) {
+// One round of the expert scan over experts e0 .. e0 + blockDim.x - 1; thread e - e0 holds
+// expert e's count `cnt` (0 for e >= E).  Writes the expert offsets (also to off_sh when
+// given), the inclusive cumsum, and either the grouped-GEMM tile lists or the key-value
+// pairs.  carry[0..2] are the running totals of rows, small tiles (or nonzero experts)
+// and big tiles; they are updated for the next round.
+__device__ void scan_experts_round(const RouteBuffers& b, int E, int e, int cnt, uint64_t* sh,
+                                   int* carry, int32_t* off_sh) {
+  const bool lists = b.tiles_small != nullptr;
+  int n_small, n_big, base;
+  expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
+  if (b.key_value) n_small = cnt > 0 ? 1 : 0;
+  uint64_t tot;
+  const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
+  const int total = field(tot, 0), stotal = field(tot, 1), btotal = field(tot, 2);
+  const int sexcl = field(ex, 1), bexcl = field(ex, 2);
+  const int off = carry[0] + field(ex, 0);
+  if (e < E) {
+    b.offsets[e] = off;
+    if (off_sh) off_sh[e] = off;
+    if (b.cumsum) b.cumsum[e] = off + cnt;
+    if (n_small) {
+      const int slot = carry[1] + sexcl;
+      if (lists) {
+        b.tiles_small[slot] = TileDesc{e, off, cnt, 0};
+      } else {
+        b.key_value[2 * slot] = e + b.e_base;
+        b.key_value[2 * slot + 1] = cnt;
+      }
+    }
+    for (int j = 0; j < n_big; ++j)
+      b.tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
+  __syncthreads();
+}
+
+// After the last round: the total, the tile counts, and the zero rows of the key-value
+// output past the nonzero experts.
+__device__ void scan_experts_finish(const RouteBuffers& b, int E, const int* carry) {
+  if (threadIdx.x == 0) {
+    b.offsets[E] = carry[0];
+    if (b.available) b.available[0] = carry[0];
+    if (b.num_tiles) { b.num_tiles[0] = carry[1]; b.num_tiles[1] = carry[2]; }
+  }
+  if (b.key_value)
+    for (int i = carry[1] + threadIdx.x; i < b.kv_rows; i += blockDim.x) {
+      b.key_value[2 * i] = 0;
+      b.key_value[2 * i + 1] = 0;
+    }
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int ntiles, int E) {
   __shared__ uint64_t sh[16];
   __shared__ int carry[3];
   if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
   __syncthreads();
-  const bool lists = tiles_small != nullptr;
+  int32_t* __restrict__ tile_hist = b.tile_hist;
   // Experts are handled in rounds of 1024 (E <= 4096).
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x;
@@ -119,55 +182,37 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
           cnt += v[i];
         }
       }
-      counts[e] = cnt;
-      if (amax_reset) amax_reset[e] = 0.0f;
+      b.counts[e] = cnt;
+      if (b.amax_reset) b.amax_reset[e] = 0.0f;
     }
-    int n_small, n_big, base;
-    expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
-    uint64_t tot;
-    const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
-    const int total = field(tot, 0), stotal = field(tot, 1), btotal = field(tot, 2);
-    const int sexcl = field(ex, 1), bexcl = field(ex, 2);
-    const int off = carry[0] + field(ex, 0);
-    if (e < E) {
-      offsets[e] = off;
-      if (cumsum) cumsum[e] = off + cnt;
-      if (n_small) tiles_small[carry[1] + sexcl] = TileDesc{e, off, cnt, 0};
-      for (int j = 0; j < n_big; ++j)
-        tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
-    __syncthreads();
+    scan_experts_round(b, E, e, cnt, sh, carry, nullptr);
   }
-  if (threadIdx.x == 0) {
-    offsets[E] = carry[0];
-    if (num_tiles) { num_tiles[0] = carry[1]; num_tiles[1] = carry[2]; }
-  }
+  scan_experts_finish(b, E, carry);
 }
 
 // Stable ranking of one wave's kIdsPerThread*64 consecutive flat ids (from wave_base):
 // in rounds of 64, an id's rank is the number of equal keys in earlier rounds of this
 // wave (my_hist, the wave's running per-expert count in LDS) plus the equal keys on
-// lower lanes of its round (ballot-based key matching).  key[r] is the expert (-1 for no
-// id) and rank[r] the rank of round r's id.
+// lower lanes of its round (ballot-based key matching).  key[r] is the expert key (-1 for
+// no id) and rank[r] the rank of round r's id.
 __device__ __forceinline__ void rank_wave_ids(const int32_t* __restrict__ ids, int64_t n, int E,
-                                              int nbits, int64_t wave_base, int lane,
-                                              int32_t* my_hist, int32_t* expanded_row_idx,
+                                              int nbits, int e_base, int64_t wave_base,
+                                              int lane, int32_t* my_hist,
+                                              int32_t* expanded_row_idx,
                                               int (&key)[kIdsPerThread],
                                               int (&rank)[kIdsPerThread]) {
   for (int r = 0; r < kIdsPerThread; ++r) {
-    int64_t f = wave_base + r * kWave + lane;
-    int e = f < n ? ids[f] : -1;
-    // An id outside [0, E) breaks the caller's contract; it is dropped (never counted,
-    // never scattered) and its gather-map entry is -1, so no kernel indexes with it.
-    bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    const int64_t f = wave_base + r * kWave + lane;
+    int e = route_key(ids, f, n, e_base);
+    // An id outside the routed range is dropped (never counted, never scattered) and its
+    // position-map entry is -1, so no kernel indexes with it.
+    const bool valid = key_valid(e, E);
     if (f < n && !valid) expanded_row_idx[f] = -1;
     if (!valid) e = 0;
-    uint64_t active = __ballot(valid);
-    uint64_t peers = match_key(static_cast<uint32_t>(e), nbits, active);
-    int before = valid ? my_hist[e] : 0;
-    int rk = before + __popcll(peers & lanemask_lt());
+    const uint64_t active = __ballot(valid);
+    const uint64_t peers = match_key(static_cast<uint32_t>(e), nbits, active);
+    const int before = valid ? my_hist[e] : 0;
+    const int rk = before + __popcll(peers & lanemask_lt());
     // the lowest lane of each group of equal keys bumps the wave histogram
     if (valid && (peers & lanemask_lt()) == 0) my_hist[e] = before + __popcll(peers);
     key[r] = valid ? e : -1;
@@ -176,11 +221,28 @@ __device__ __forceinline__ void rank_wave_ids(const int32_t* __restrict__ ids, i
   }
 }
 
+// Final placement of in-range flat id f of expert key e, rank r_in within its expert and
+// expert offset off.
+__device__ __forceinline__ void place_id(const RouteBuffers& b, int e, int64_t f, int off,
+                                         int r_in) {
+  const int pos = off + r_in;
+  if (b.sorted_ids) b.sorted_ids[pos] = e + b.e_base;
+  if (b.sorted_row_idx) b.sorted_row_idx[pos] = static_cast<int32_t>(f);
+  b.expanded_row_idx[f] =
+      b.capacity > 0 ? (r_in < b.capacity ? e * b.capacity + r_in : -1) : pos;
+}
+
+// Sorted positions at and past the in-range total hold no id: -1.
+__device__ __forceinline__ void fill_tail(const RouteBuffers& b, int64_t f, int64_t n,
+                                          int total) {
+  if (f < n && f >= total) {
+    if (b.sorted_ids) b.sorted_ids[f] = -1;
+    if (b.sorted_row_idx) b.sorted_row_idx[f] = -1;
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nbits,
-    const int32_t* __restrict__ tile_hist, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_row_idx,
-    int32_t* __restrict__ expanded_row_idx) {
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
   extern __shared__ int32_t wave_hist[];           // [4][E]
   const int nw = kRouteThreads / kWave;
   for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
@@ -190,7 +252,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
   int key[kIdsPerThread];
   int rank[kIdsPerThread];
   int32_t* my_hist = wave_hist + w * E;
-  rank_wave_ids(ids, n, E, nbits, wave_base, lane, my_hist, expanded_row_idx, key, rank);
+  rank_wave_ids(ids, n, E, nbits, b.e_base, wave_base, lane, my_hist, b.expanded_row_idx, key,
+                rank);
   __syncthreads();
   // Exclusive scan over the waves, per expert.
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -202,15 +265,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     }
   }
   __syncthreads();
-  const int32_t* th = tile_hist + static_cast<int64_t>(blockIdx.x) * E;
+  const int32_t* th = b.tile_hist + static_cast<int64_t>(blockIdx.x) * E;
+  const int total = b.offsets[E];
   for (int r = 0; r < kIdsPerThread; ++r) {
-    int e = key[r];
+    const int64_t f = wave_base + r * kWave + lane;
+    fill_tail(b, f, n, total);
+    const int e = key[r];
     if (e < 0) continue;
-    int64_t f = wave_base + r * kWave + lane;
-    int pos = offsets[e] + th[e] + my_hist[e] + rank[r];
-    if (sorted_ids) sorted_ids[pos] = e;
-    if (sorted_row_idx) sorted_row_idx[pos] = static_cast<int32_t>(f);
-    expanded_row_idx[f] = pos;
+    place_id(b, e, f, b.offsets[e], th[e] + my_hist[e] + rank[r]);
   }
 }
 
@@ -221,12 +283,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
 constexpr int kRouteSmallThreads = 1024;
 
 __global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ cumsum,
-    TileDesc* __restrict__ tiles_small, TileDesc* __restrict__ tiles_big,
-    int32_t* __restrict__ num_tiles, float* __restrict__ amax_reset,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_row_idx,
-    int32_t* __restrict__ expanded_row_idx) {
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
   extern __shared__ int32_t lds[];
   __shared__ uint64_t sh[16];
   __shared__ int carry[3];
@@ -241,10 +298,9 @@ __global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
   int key[kIdsPerThread];
   int rank[kIdsPerThread];
   if (w < nw)
-    rank_wave_ids(ids, n, E, nbits, wave_base, lane, wave_hist + w * E, expanded_row_idx, key,
-                  rank);
+    rank_wave_ids(ids, n, E, nbits, b.e_base, wave_base, lane, wave_hist + w * E,
+                  b.expanded_row_idx, key, rank);
   __syncthreads();
-  const bool lists = tiles_small != nullptr;
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x;
     int cnt = 0;
@@ -254,42 +310,21 @@ __global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
         wave_hist[ww * E + e] = cnt;                   // exclusive over waves
         cnt += v;
       }
-      counts[e] = cnt;
-      if (amax_reset) amax_reset[e] = 0.0f;
+      b.counts[e] = cnt;
+      if (b.amax_reset) b.amax_reset[e] = 0.0f;
     }
-    int n_small, n_big, base;
-    expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
-    uint64_t tot;
-    const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
-    const int total = field(tot, 0), stotal = field(tot, 1), btotal = field(tot, 2);
-    const int sexcl = field(ex, 1), bexcl = field(ex, 2);
-    const int off = carry[0] + field(ex, 0);
-    if (e < E) {
-      offsets[e] = off;
-      off_sh[e] = off;
-      if (cumsum) cumsum[e] = off + cnt;
-      if (n_small) tiles_small[carry[1] + sexcl] = TileDesc{e, off, cnt, 0};
-      for (int j = 0; j < n_big; ++j)
-        tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
-    __syncthreads();
+    scan_experts_round(b, E, e, cnt, sh, carry, off_sh);
   }
-  if (threadIdx.x == 0) {
-    offsets[E] = carry[0];
-    if (num_tiles) { num_tiles[0] = carry[1]; num_tiles[1] = carry[2]; }
-  }
+  scan_experts_finish(b, E, carry);
   __syncthreads();                                      // off_sh complete
   if (w >= nw) return;
+  const int total = carry[0];
   for (int r = 0; r < kIdsPerThread; ++r) {
+    const int64_t f = wave_base + r * kWave + lane;
+    fill_tail(b, f, n, total);
     const int e = key[r];
     if (e < 0) continue;
-    const int64_t f = wave_base + r * kWave + lane;
-    const int pos = off_sh[e] + wave_hist[w * E + e] + rank[r];
-    if (sorted_ids) sorted_ids[pos] = e;
-    if (sorted_row_idx) sorted_row_idx[pos] = static_cast<int32_t>(f);
-    expanded_row_idx[f] = pos;
+    place_id(b, e, f, off_sh[e], wave_hist[w * E + e] + rank[r]);
   }
 }
 
@@ -300,19 +335,15 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
   const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
   if (nt == 1 && small_lds <= kRouteSmallMaxLds) {
     route_small_kernel<<<dim3(1), dim3(kRouteSmallThreads), small_lds, stream>>>(
-        ids, n, E, bits_for(E), b.counts, b.offsets, b.cumsum, b.tiles_small, b.tiles_big,
-        b.num_tiles, b.amax_reset, b.sorted_ids, b.sorted_row_idx, b.expanded_row_idx);
+        ids, n, E, bits_for(E), b);
     return hipGetLastError();
   }
   route_hist_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
-      ids, n, E, b.tile_hist);
-  route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(
-      b.tile_hist, nt, E, b.counts, b.offsets, b.cumsum, b.tiles_small, b.tiles_big, b.num_tiles,
-      b.amax_reset);
+      ids, n, E, b.e_base, b.tile_hist);
+  route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(b, nt, E);
   route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
                          (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
-      ids, n, E, bits_for(E), b.tile_hist, b.offsets, b.sorted_ids, b.sorted_row_idx,
-      b.expanded_row_idx);
+      ids, n, E, bits_for(E), b);
   return hipGetLastError();
 }
 

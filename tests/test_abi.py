@@ -118,6 +118,48 @@ def test_route_validation():
         assert ei.value.status == code
 
 
+def test_route_v2_validation():
+    ws = rm.moe_route_workspace_size(64, 8, 32)
+    base = dict(num_rows=64, hidden=256, num_experts=32, top_k=8, x=4096, expert_idx=8192,
+                expanded_x=1 << 20, expanded_row_idx=1 << 22, expert_tokens=1 << 23,
+                expanded_scale=1 << 21, available_idx_num=None, scale=None, offset=None,
+                workspace=1 << 24, workspace_bytes=ws, stream=0)
+    O = rm.MoeRouteOptions
+    cases = [
+        (dict(options=O(expert_start=4, expert_end=4)), -1),            # empty range
+        (dict(options=O(expert_start=0, expert_end=33)), -1),           # past num_experts
+        (dict(options=O(expert_start=-1, expert_end=3)), -1),
+        (dict(options=O(row_idx_type=2)), -1),
+        (dict(options=O(expert_tokens_num_type=3)), -1),
+        (dict(options=O(quant_mode=2)), -1),
+        (dict(options=O(quant_mode=0)), -1),                             # static needs scale
+        (dict(options=O(quant_mode=0), scale=256), -1),                 # ... and offset
+        (dict(options=O(quant_mode=1), expanded_scale=None), -1),
+        (dict(options=O(quant_mode=-1), scale=256, expanded_scale=None), -1),
+        (dict(options=O(drop_pad_mode=2)), -1),
+        (dict(options=O(drop_pad_mode=1, expert_capacity=0)), -1),
+        (dict(options=O(drop_pad_mode=1, expert_capacity=513)), -1),    # > N*K
+        (dict(options=O(drop_pad_mode=1, expert_capacity=4, row_idx_type=1)), -1),
+        (dict(options=O(drop_pad_mode=1, expert_capacity=4, expert_start=0, expert_end=16)), -1),
+        (dict(options=O(drop_pad_mode=1, expert_capacity=4, active_num=10)), -1),
+        (dict(options=O(), workspace_bytes=ws - 1), -3),
+        (dict(options=O(), hidden=12), -2),
+        (dict(options=O(), x=4098), -1),
+        (dict(options=O(), expanded_row_idx=None), -1),
+    ]
+    for kw, code in cases:
+        a = dict(base); a.update(kw)
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_route_v2(**a)
+        assert ei.value.status == code, kw
+
+
+def test_route_workspace_holds_the_position_map():
+    # tile histograms + counts + offsets + one int32 per routed row, 256-byte aligned
+    n = 8192 * 8
+    assert rm.moe_route_workspace_size(8192, 8, 256) >= (n // 1024) * 256 * 4 + 257 * 4 + 4 * n
+
+
 def test_quantize_validation():
     for kw in (dict(K=24), dict(src=None), dict(src=4098), dict(groups=0)):
         a = dict(src=4096, groups=1, rows_per_group=4, K=256, q=256, codes=8192, scales=16384,

@@ -150,10 +150,21 @@ def test_route_drops_out_of_range_ids(T):
     nv = order.size
     assert np.array_equal(got["sorted_row_idx"][:nv], order)
     assert np.array_equal(got["sorted_ids"][:nv], flat[order])
+    assert np.all(got["sorted_row_idx"][nv:] == -1) and np.all(got["sorted_ids"][nv:] == -1)
     want = np.full(flat.size, -1, np.int64)
     want[order] = np.arange(nv)
     assert np.array_equal(got["expanded_row_idx"], want)
     assert np.array_equal(got["cumsum"], np.cumsum(np.bincount(flat[valid], minlength=E)))
+
+
+def test_route_more_than_2_21_ids():
+    """2.56 M routed rows: the expert scan's packed row totals need more than 21 bits."""
+    _say("route 40000 x 64 ids")
+    ids = draw_expert_ids(40000, 256, 64, seed_index=1400, zipf_s=1.2)
+    got = _route_on_gpu(ids, 256)
+    want = oracle.route(ids, 256)
+    for key in ("expanded_row_idx", "cumsum", "sorted_ids", "sorted_row_idx"):
+        assert np.array_equal(got[key], want[key]), key
 
 
 def test_route_int8_full_size_bit_exact():

@@ -1,0 +1,204 @@
+"""GPU parity of moe_route_v2 (the routing primitive's options: scatter index, count and
+key_value histograms, active expert range, static int8, drop/pad, active_num, per-row
+scale) against oracle.route_v2, bit for bit, through the C ABI.
+
+Every output buffer starts filled with a sentinel: the defined entries must equal the
+oracle's, and the rows past the valid ones must still hold the sentinel (no stray
+writes)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_moe_layer_amd as rm
+from moe_inputs import ROUTE_8K, draw_expert_ids, draw_route_inputs, draw_tokens, f32_to_bf16_bits
+from tests.gpu_harness import dev, host, empty_bytes
+
+pytestmark = pytest.mark.gpu
+
+SENT_BYTE = 0x5A
+SENT_I32 = 0x5A5A5A5A
+STATIC_SCALE = np.float32(17.3)
+STATIC_OFFSET = np.float32(-0.6)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _rows(N, K, E, opts):
+    if opts.get("drop_pad_mode", 0):
+        return E * opts["expert_capacity"]
+    a = opts.get("active_num", -1)
+    return N * K if a <= 0 else min(a, N * K)
+
+
+def run_v2(x_bits, ids, E, opts, row_scale=None):
+    """One moe_route_v2 call; returns the host copies of every output."""
+    N, K = ids.shape
+    H = x_bits.shape[1]
+    q = opts.get("quant_mode", -1)
+    rows = _rows(N, K, E, opts)
+    elem = 2 if q == -1 else 1
+    ex = torch.full((rows * H * elem,), SENT_BYTE, dtype=torch.uint8, device="cuda")
+    eri = torch.full((N * K,), SENT_I32, dtype=torch.int32, device="cuda")
+    start, end = opts.get("expert_start", 0), opts.get("expert_end", 0)
+    e_act = (end - start) if end else E
+    tok_shape = (E, 2) if opts.get("expert_tokens_num_type", 0) == 2 else (e_act,)
+    tok = torch.full(tok_shape, SENT_I32, dtype=torch.int32, device="cuda")
+    esc = torch.full((max(rows, 1),), SENT_I32, dtype=torch.int32, device="cuda")
+    avail = torch.full((1,), SENT_I32, dtype=torch.int32, device="cuda")
+    scale = offset = None
+    if q == 0:
+        scale = dev(np.array([STATIC_SCALE], np.float32))
+        offset = dev(np.array([STATIC_OFFSET], np.float32))
+    elif q == -1 and row_scale is not None:
+        scale = dev(row_scale)
+    want_scale = q == 1 or (q == -1 and row_scale is not None)
+    ws = empty_bytes(rm.moe_route_workspace_size(N, K, E), fill=0xFF)
+    rm.moe_route_v2(N, H, E, K, dev(x_bits), dev(ids.astype(np.int32)), rm.MoeRouteOptions(**opts),
+                    ex, eri, expert_tokens=tok, expanded_scale=esc if want_scale else None,
+                    available_idx_num=avail, scale=scale, offset=offset, workspace=ws)
+    torch.cuda.synchronize()
+    ex_h = host(ex)
+    ex_h = ex_h.view(np.uint16) if elem == 2 else ex_h.view(np.int8)
+    return {"expanded_x": ex_h.reshape(rows, H), "expanded_row_idx": host(eri),
+            "expert_tokens": host(tok), "expanded_scale": host(esc).view(np.float32)[:rows],
+            "expanded_scale_bits": host(esc)[:rows], "available_idx_num": int(host(avail)[0]),
+            "has_scale": want_scale}
+
+
+def oracle_v2(x_bits, ids, E, opts, row_scale=None):
+    o = dict(opts)
+    start, end = o.pop("expert_start", 0), o.pop("expert_end", 0)
+    rng_ = None if (start, end) == (0, 0) else (start, end)
+    q = o.get("quant_mode", -1)
+    scale = offset = None
+    if q == 0:
+        scale, offset = STATIC_SCALE, STATIC_OFFSET
+    elif row_scale is not None:
+        scale = row_scale
+    return oracle.route_v2(oracle.bf16_bits_to_f32(x_bits), ids, E, expert_range=rng_,
+                           scale=scale, offset=offset, **o)
+
+
+def check_v2(got, want, opts):
+    assert got["available_idx_num"] == want["available_idx_num"]
+    assert np.array_equal(got["expanded_row_idx"], want["expanded_row_idx"])
+    assert np.array_equal(got["expert_tokens"], want["expert_tokens"])
+    q = opts.get("quant_mode", -1)
+    wx = want["expanded_x"]
+    rows = got["expanded_x"].shape[0]
+    wx = wx.reshape(rows, -1)
+    if q == -1:
+        wx = f32_to_bf16_bits(wx)
+    v = want["valid_rows"]
+    gx = got["expanded_x"]
+    bad = np.nonzero(np.any(gx[:v] != wx[:v], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} expanded rows differ, first {bad[:5]}"
+    if v < rows:                                   # rows past the valid ones: untouched
+        assert np.all(gx[v:].view(np.uint8) == SENT_BYTE)
+    if got["has_scale"]:
+        ws_ = want["expanded_scale"].reshape(-1)
+        assert np.array_equal(got["expanded_scale"][:v].view(np.uint32),
+                              ws_[:v].astype(np.float32).view(np.uint32))
+        if v < rows:
+            assert np.all(got["expanded_scale_bits"][v:] == SENT_I32)
+
+
+# name, N, K, E, H, zipf, options, per-row scale
+V2_CASES = [
+    ("scatter_one_workgroup", 16, 16, 896, 64, 0.0, dict(row_idx_type=1), False),
+    ("scatter_tiled_count", 300, 8, 64, 64, 1.1, dict(row_idx_type=1, expert_tokens_num_type=1),
+     False),
+    ("range_gather_count_dynamic", 500, 8, 256, 136, 1.1,
+     dict(expert_start=3, expert_end=40, expert_tokens_num_type=1, quant_mode=1), False),
+    ("range_scatter_kv_static", 500, 8, 256, 136, 0.5,
+     dict(expert_start=100, expert_end=228, row_idx_type=1, expert_tokens_num_type=2,
+          quant_mode=0), False),
+    ("range_one_expert", 200, 4, 16, 64, 0.0, dict(expert_start=15, expert_end=16), False),
+    ("range_one_workgroup_kv", 60, 16, 896, 64, 1.0,
+     dict(expert_start=400, expert_end=896, expert_tokens_num_type=2, quant_mode=1), False),
+    # the page's low-latency case: one token, K=8, 256 experts, dynamic quant, key_value
+    ("one_token_kv_dynamic", 1, 8, 256, 7168, 0.0,
+     dict(expert_start=0, expert_end=256, quant_mode=1, expert_tokens_num_type=2), False),
+    # the page's large-batch case: K=8, 256 experts, a range of 32, no quant, scatter, count
+    ("large_batch_range32", 2048, 8, 256, 7168, 1.1,
+     dict(expert_start=64, expert_end=96, quant_mode=-1, row_idx_type=1,
+          expert_tokens_num_type=1), False),
+    ("droppad_c1_dynamic", 200, 4, 16, 64, 1.3,
+     dict(drop_pad_mode=1, expert_capacity=1, quant_mode=1), False),
+    ("droppad_c37_static_kv", 300, 8, 64, 136, 1.1,
+     dict(drop_pad_mode=1, expert_capacity=37, quant_mode=0, expert_tokens_num_type=2), False),
+    ("droppad_nothing_dropped_bf16", 40, 4, 8, 64, 0.0,
+     dict(drop_pad_mode=1, expert_capacity=160, quant_mode=-1), False),
+    ("droppad_one_workgroup", 16, 16, 896, 64, 0.0,
+     dict(drop_pad_mode=1, expert_capacity=2, quant_mode=1, expert_tokens_num_type=1), False),
+    ("active_num_cut_dynamic", 300, 8, 64, 64, 1.1, dict(active_num=1000, quant_mode=1), False),
+    ("active_num_range_static", 300, 8, 64, 64, 1.1,
+     dict(active_num=50, expert_start=10, expert_end=30, quant_mode=0), False),
+    ("active_num_above_rows", 30, 4, 8, 64, 0.0, dict(active_num=100000, quant_mode=-1), False),
+    ("row_scale_bf16", 300, 8, 64, 72, 0.5, dict(quant_mode=-1), True),
+    ("row_scale_range_scatter", 300, 8, 64, 72, 0.5,
+     dict(quant_mode=-1, expert_start=5, expert_end=50, row_idx_type=1), True),
+    ("row_scale_droppad", 100, 4, 8, 72, 1.0,
+     dict(quant_mode=-1, drop_pad_mode=1, expert_capacity=20), True),
+]
+
+
+@pytest.mark.parametrize("name,N,K,E,H,zipf,opts,rs", V2_CASES, ids=[c[0] for c in V2_CASES])
+def test_route_v2_bit_exact(name, N, K, E, H, zipf, opts, rs):
+    _say(f"route_v2 {name}")
+    seed = 1200 + N + H
+    ids = draw_expert_ids(N, E, K, seed_index=seed, zipf_s=zipf)
+    x = draw_tokens(N, H, seed_index=seed)
+    x = f32_to_bf16_bits(oracle.bf16_bits_to_f32(x) * np.float32(3.0))
+    row_scale = (np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+                 if rs else None)
+    got = run_v2(x, ids, E, opts, row_scale)
+    want = oracle_v2(x, ids, E, opts, row_scale)
+    check_v2(got, want, opts)
+
+
+def test_route_v2_full_size_scatter_kv_dynamic():
+    """The int8 routing workload (N=8192, H=7168, E=256, K=8) through the options path."""
+    cfg = ROUTE_8K
+    _say(f"route_v2 {cfg.name} scatter kv dynamic")
+    x, ids = draw_route_inputs(cfg)
+    opts = dict(row_idx_type=1, expert_tokens_num_type=2, quant_mode=1)
+    got = run_v2(x, ids, cfg.E, opts)
+    want = oracle_v2(x, ids, cfg.E, opts)
+    check_v2(got, want, opts)
+
+
+def test_route_v2_defaults_equal_moe_route():
+    """With default options moe_route_v2 computes what moe_route does."""
+    _say("route_v2 defaults vs moe_route")
+    N, K, E, H = 700, 8, 128, 64
+    ids = draw_expert_ids(N, E, K, seed_index=1300, zipf_s=1.0)
+    x = draw_tokens(N, H, seed_index=1300)
+    got = run_v2(x, ids, E, dict(quant_mode=1))
+    ex = torch.empty((N * K, H), dtype=torch.int8, device="cuda")
+    esc = torch.empty(N * K, dtype=torch.float32, device="cuda")
+    eri = torch.empty(N * K, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
+    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs,
+                 None, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(got["expanded_x"], host(ex))
+    assert np.array_equal(got["expanded_scale"], host(esc))
+    assert np.array_equal(got["expanded_row_idx"], host(eri))
+    assert np.array_equal(got["expert_tokens"], host(cs))

@@ -56,9 +56,9 @@ def test_histogram_modes_match_brute_force(N, K, E, rng_):
     ids = draw_expert_ids(N, E, K, seed_index=400 + N, zipf_s=1.3)
     start, end = (0, E) if rng_ is None else rng_
     _, _, counts, _ = _brute(ids, E, start, end)
-    r1 = oroute.route_v2(None, ids, E, expert_range=rng_, tokens_num_type=1)
+    r1 = oroute.route_v2(None, ids, E, expert_range=rng_, expert_tokens_num_type=1)
     assert r1["expert_tokens"].tolist() == counts
-    r2 = oroute.route_v2(None, ids, E, expert_range=rng_, tokens_num_type=2)
+    r2 = oroute.route_v2(None, ids, E, expert_range=rng_, expert_tokens_num_type=2)
     kv = r2["expert_tokens"]
     assert kv.shape == (E, 2)
     pairs = [[start + i, c] for i, c in enumerate(counts) if c > 0]
@@ -69,7 +69,7 @@ def test_histogram_modes_match_brute_force(N, K, E, rng_):
 def test_key_value_hand_example():
     # experts 1 and 3 used, 0 and 2 empty
     ids = np.array([[3, 1], [3, 3]], np.int32)
-    kv = oroute.route_v2(None, ids, 4, tokens_num_type=2)["expert_tokens"]
+    kv = oroute.route_v2(None, ids, 4, expert_tokens_num_type=2)["expert_tokens"]
     assert kv.tolist() == [[1, 1], [3, 3], [0, 0], [0, 0]]
 
 
