@@ -10,7 +10,8 @@ outlier channels x30): tokens/s, and the roofline of its dominant kernel (the FC
 GEMM, bound by the f16 MFMA).  The decode (T=16) and mid (T=1024, Zipf 1.0) batches are
 reported under "workloads" with their HBM rooflines, and the routing-and-int8-permute
 primitive (moe_route, N=8192, H=7168, E=256, K=8) under "routing_primitive" with its
-routed rows/s and HBM fraction.  Per-stage times come from HIP events recorded between
+routed rows/s and HBM fraction, and two cases of its options (moe_route_v2) under
+"routing_primitive.options".  Per-stage times come from HIP events recorded between
 the stages on the launch stream (moe_forward_timed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -213,6 +214,27 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     return res, keep
 
 
+def _time_calls(call, torch, steps, warmup, events):
+    """Mean HIP-event time (ms) of `call` over `steps` calls after `warmup`, and the wall
+    time per call (ms)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [events.create(2) for _ in range(steps)]
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    for i in range(steps):
+        events.record(evs[i][0], stream)
+        call()
+        events.record(evs[i][1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = float(np.mean([events.elapsed_ms(e[0], e[1]) for e in evs]))
+    for e in evs:
+        events.destroy(e)
+    return gpu_ms, wall * 1e3 / steps
+
+
 def route_workload(cfg, torch, rm, steps, warmup, events):
     """Time the routing-and-int8-permute primitive (moe_route) on its own workload: the
     stable sort by expert, the row maps, the per-expert cumsum and the expanded int8 rows
@@ -236,25 +258,64 @@ def route_workload(cfg, torch, rm, steps, warmup, events):
         rm.moe_route(N, H, E, K, x, ids, rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs, sid,
                      sri, ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [events.create(2) for _ in range(steps)]
-    stream = torch.cuda.current_stream().cuda_stream
-    t0 = time.perf_counter()
-    for i in range(steps):
-        events.record(evs[i][0], stream)
-        call()
-        events.record(evs[i][1], stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = float(np.mean([events.elapsed_ms(e[0], e[1]) for e in evs]))
-    for e in evs:
-        events.destroy(e)
+    gpu_ms, wall_ms = _time_calls(call, torch, steps, warmup, events)
     nbytes = N * H * 2 + R * 4 + R * H + R * 4 + 3 * R * 4 + E * 4
     return {"workload": cfg.name, "N": N, "routed_rows_per_s": R / (gpu_ms * 1e-3),
-            "ms_per_call": gpu_ms, "wall_ms_per_call": wall * 1e3 / steps,
+            "ms_per_call": gpu_ms, "wall_ms_per_call": wall_ms,
             "algorithmic_bytes": float(nbytes),
+            "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
+
+
+# The routing page's two named fast cases, through moe_route_v2 on the routing workload's
+# inputs: a large batch routed to one range of 32 experts (BF16 rows, scatter index,
+# per-expert counts) and a single token (dynamic int8, key_value histogram).
+ROUTE_OPTION_CASES = {
+    "large_batch_range32": dict(N=8192, start=0, end=32,
+                                opts=dict(expert_start=0, expert_end=32, quant_mode=-1,
+                                          row_idx_type=1, expert_tokens_num_type=1)),
+    "one_token_dynamic_kv": dict(N=1, start=0, end=256,
+                                 opts=dict(expert_start=0, expert_end=256, quant_mode=1,
+                                           expert_tokens_num_type=2)),
+}
+
+
+def route_options_workload(case, cfg, torch, rm, steps, warmup, events):
+    """Time one moe_route_v2 case.  Algorithmic bytes: the ids, the x rows of tokens with
+    at least one in-range id (read once), the expanded rows (and scales) of the in-range
+    ids, the index output and the histogram, each once."""
+    from moe_inputs import draw_route_inputs
+    c = ROUTE_OPTION_CASES[case]
+    xb, ids_h = draw_route_inputs(cfg)
+    N, H, E, K = c["N"], cfg.H, cfg.E, cfg.K
+    xb, ids_h = np.ascontiguousarray(xb[:N]), np.ascontiguousarray(ids_h[:N])
+    opts = c["opts"]
+    q = opts["quant_mode"]
+    inr = (ids_h >= c["start"]) & (ids_h < c["end"])
+    avail = int(inr.sum())
+    tok_hit = int(inr.any(axis=1).sum())
+    R = N * K
+    elem = 2 if q == -1 else 1
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    ids = torch.from_numpy(ids_h).cuda()
+    ex = torch.empty((R, H * elem), dtype=torch.uint8, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    kv = opts["expert_tokens_num_type"] == 2
+    tok = torch.empty((E, 2) if kv else (c["end"] - c["start"],), dtype=torch.int32,
+                      device="cuda")
+    esc = torch.empty(R, dtype=torch.float32, device="cuda") if q == 1 else None
+    ws = torch.empty(rm.moe_route_workspace_size(N, K, E), dtype=torch.uint8, device="cuda")
+    o = rm.MoeRouteOptions(**opts)
+
+    def call():
+        rm.moe_route_v2(N, H, E, K, x, ids, o, ex, eri, expert_tokens=tok, expanded_scale=esc,
+                        workspace=ws)
+
+    gpu_ms, wall_ms = _time_calls(call, torch, steps, warmup, events)
+    nbytes = (R * 4 + tok_hit * H * 2 + avail * (H * elem + (4 if q == 1 else 0)) + R * 4
+              + tok.numel() * 4)
+    return {"workload": f"{case}_N{N}_H{H}_E{E}_K{K}_experts{c['start']}-{c['end']}",
+            "routed_rows": avail, "us_per_call": gpu_ms * 1e3, "wall_us_per_call": wall_ms * 1e3,
+            "in_range_rows_per_s": avail / (gpu_ms * 1e-3), "algorithmic_bytes": float(nbytes),
             "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
 
 
@@ -457,9 +518,66 @@ def summarize_profiles(src, out_dir):
         md.append(f"Kernel sources: `{src_hash}`.")
         with open(os.path.join(out_dir, f"hbm_traffic_T{cfg.T}.md"), "w") as fh:
             fh.write("\n".join(md) + "\n")
+    _summarize_routing(src, out_dir, cmd_trace)
     with open(os.path.join(out_dir, "traffic.json"), "w") as fh:
         json.dump(traffic, fh, indent=1)
         fh.write("\n")
+
+
+def _summarize_routing(src, out_dir, cmd_trace):
+    """Kernel trace of the routing-primitive run (moe_route and the moe_route_v2 cases)."""
+    stats = _one(os.path.join(src, "trace_route", "*kernel_stats.csv"))
+    if stats is None:
+        return
+    line = None
+    log_path = os.path.join(src, "trace_route.log")
+    if os.path.exists(log_path):
+        for ln in open(log_path, errors="replace"):
+            if ln.startswith("{") and '"routing_primitive"' in ln:
+                line = json.loads(ln)["routing_primitive"]
+    md = ["# Kernel trace: routing primitive", "",
+          "Command (from the repository root on the GPU box, after "
+          "`cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd_trace.format(w="route"), "```", "",
+          "Per-kernel statistics (all calls of the run: moe_route on "
+          "route_N8192_H7168_E256_K8_zipf1.1_int8, then the moe_route_v2 cases, each with "
+          "its warmup and timed calls; `at::` kernels are the benchmark's own input setup):", "",
+          "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in _read_csv(stats)[:14]:
+        md.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                  f"{float(r['Percentage']):.1f} |")
+    trace = _one(os.path.join(src, "trace_route", "*kernel_trace.csv"))
+    if line and trace:
+        # The cases run one after the other, each with warmup + steps calls: split the
+        # library's kernels in dispatch order.
+        kern = [r for r in _read_csv(trace) if "rmoe::route" in r["Kernel_Name"]]
+        kern.sort(key=lambda r: int(r["Start_Timestamp"]))
+        # one library call starts with the histogram (or the fused small router) launch
+        calls = []
+        for r in kern:
+            if not calls or _short(r["Kernel_Name"]).startswith(("route_hist", "route_small")):
+                calls.append([])
+            calls[-1].append(r)
+        cases = [("moe_route", line)] + [(c, r) for c, r in line.get("options", {}).items()]
+        names = sorted({_short(r["Kernel_Name"]) for r in kern})
+        per_case = len(calls) // len(cases)
+        md += ["", "Per case (kernel average µs over its calls; HIP-event time per call of "
+               "the same run, which includes the gaps between launches):", "",
+               "| case | " + " | ".join(f"`{n}`" for n in names) + " | event µs/call | HBM frac |",
+               "|---|" + "---|" * (len(names) + 2)]
+        for i, (case, r) in enumerate(cases):
+            chunk = [k for c in calls[i * per_case:(i + 1) * per_case] for k in c]
+            cells = []
+            for n in names:
+                d = [(int(c["End_Timestamp"]) - int(c["Start_Timestamp"])) / 1e3 for c in chunk
+                     if _short(c["Kernel_Name"]) == n]
+                cells.append(f"{sum(d) / len(d):.1f}" if d else "—")
+            us = r["ms_per_call"] * 1e3 if case == "moe_route" else r["us_per_call"]
+            label = r["workload"]
+            md.append(f"| {label} | " + " | ".join(cells) + f" | {us:.1f} | "
+                      f"{100 * r['hbm_frac']:.1f}% |")
+    with open(os.path.join(out_dir, "kernel_trace_routing.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
 
 
 def main():
@@ -500,8 +618,9 @@ def main():
         return
     rm._lib()
     events = HipEvents()
-    prepared, d13, d2 = build_weights(DECODE_16, torch, rm)
     chosen = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    if any(c != "route" for c in chosen):
+        prepared, d13, d2 = build_weights(DECODE_16, torch, rm)
     cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4)}
     results, keeps = {}, {}
     route_res = None
@@ -511,6 +630,13 @@ def main():
         route_res = route_workload(ROUTE_8K, torch, rm, args.steps, args.warmup, events)
         log(f"  {route_res['routed_rows_per_s']:.3e} routed rows/s, {route_res['ms_per_call']:.3f} ms, "
             f"{100 * route_res['hbm_frac']:.1f}% of HBM peak")
+        route_res["options"] = {}
+        for case in ROUTE_OPTION_CASES:
+            r = route_options_workload(case, ROUTE_8K, torch, rm, args.steps, args.warmup,
+                                       events)
+            route_res["options"][case] = r
+            log(f"  {r['workload']}: {r['us_per_call']:.1f} us/call, {r['routed_rows']} rows, "
+                f"{100 * r['hbm_frac']:.1f}% of HBM peak")
     for name in chosen:
         cfg, rot = cfgs[name]
         log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")

@@ -114,8 +114,13 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
     const int32_t d = map[t * K + threadIdx.x];
     dst[threadIdx.x] = (d >= 0 && d < limit) ? d : -1;
   }
+  __syncthreads();
+  // A token none of whose ids is moved (out of the expert range, dropped, past the row
+  // limit) is not read at all.  The test is uniform over the workgroup.
+  bool any = false;
+  for (int j = 0; j < K; ++j) any |= dst[j] >= 0;
+  if (!any) return;
   if (quant == 0) {
-    __syncthreads();
     for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
       uint4 d = reinterpret_cast<const uint4*>(xr)[v];
       for (int j = 0; j < K; ++j) {
@@ -137,7 +142,6 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
   };
   if (quant == 2) {
     const float s = static_scale[0], off = static_offset[0];
-    __syncthreads();
     for (int v = threadIdx.x; v < nvec; v += blockDim.x)
       store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v],
                        [=](float xv) { return static_int8(xv, s, off); }));
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256) void route_permute_kernel(
       amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
     }
   }
-  amax = block_max(amax, red);            // includes the __syncthreads for dst[]
+  amax = block_max(amax, red);
   const float scale = amax / 127.0f;
   for (int v = threadIdx.x; v < nvec; v += blockDim.x)
     store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v], [=](float xv) {
