@@ -189,7 +189,8 @@ moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, in
   hipError_t e = launch_route(expert_idx, n, num_experts, b, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_route_permute(x, num_rows, hidden, top_k, static_cast<int>(quant), expanded_row_idx,
-                           INT64_MAX, nullptr, nullptr, nullptr, expanded_x, expanded_scale, s);
+                           INT64_MAX, false, nullptr, nullptr, nullptr, expanded_x,
+                           expanded_scale, s);
   return hip_status(e);
 }
 
@@ -258,7 +259,8 @@ moe_status_t moe_route_v2(int32_t num_rows, int32_t hidden, int32_t num_experts,
   const int quant = o.quant_mode == -1 ? 0 : (o.quant_mode == 1 ? 1 : 2);
   const int64_t limit = drop_pad ? static_cast<int64_t>(num_experts) * o.expert_capacity
                                  : (o.active_num > 0 ? o.active_num : INT64_MAX);
-  e = launch_route_permute(x, num_rows, hidden, top_k, quant, map, limit,
+  const bool may_skip = E_act != num_experts || drop_pad || o.active_num > 0;
+  e = launch_route_permute(x, num_rows, hidden, top_k, quant, map, limit, may_skip,
                            o.quant_mode == -1 ? scale : nullptr, scale, offset, expanded_x,
                            expanded_scale, s);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -68,11 +68,13 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
                         hipStream_t stream);
 
 // Token movement of the routing primitive: token row t goes to rows map[t*K + j] (skipped
-// when negative or >= limit).  quant 0: BF16 copy (plus row_scale[t] to expanded_scale
+// when negative or >= limit).  may_skip: some tokens may have no row to go to (an expert
+// range, capacity or row limit); such tokens are then not read.  quant 0: BF16 copy (plus row_scale[t] to expanded_scale
 // when both are given); 1: dynamic int8 with its scale; 2: static int8 with the device
 // scalars *static_scale and *static_offset.
 hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
-                                const int32_t* map, int64_t limit, const float* row_scale,
+                                const int32_t* map, int64_t limit, bool may_skip,
+                                const float* row_scale,
                                 const float* static_scale, const float* static_offset,
                                 void* expanded_x, float* expanded_scale, hipStream_t stream);
 // Drop/pad: zero the slots of expert e at and past counts[e] (rows of row_bytes bytes,

@@ -100,80 +100,109 @@ __device__ __forceinline__ uint2 quant8(uint4 d, Q q) {
   return make_uint2(packed[0], packed[1]);
 }
 
-__global__ __launch_bounds__(256) void route_permute_kernel(
+// Up to kPermCache 16-byte vectors per thread of the current row chunk are held in
+// registers: all of a chunk's loads are in flight together, and a row of at most
+// kPermThreads * kPermCache vectors (H <= 8192) is read from memory once even in the
+// dynamic mode, whose scale needs the whole row before the first code.
+constexpr int kPermThreads = 256;
+constexpr int kPermCache = 4;
+
+__global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
     const uint16_t* __restrict__ x, int H, int K, int quant, const int32_t* __restrict__ map,
-    int64_t limit, const float* __restrict__ row_scale, const float* __restrict__ static_scale,
-    const float* __restrict__ static_offset, void* __restrict__ expanded_x,
-    float* __restrict__ expanded_scale) {
-  __shared__ float red[4];
+    int64_t limit, bool may_skip, const float* __restrict__ row_scale,
+    const float* __restrict__ static_scale, const float* __restrict__ static_offset,
+    void* __restrict__ expanded_x, float* __restrict__ expanded_scale) {
+  __shared__ float red[kPermThreads / kWave];
   __shared__ int32_t dst[64];
   const int64_t t = blockIdx.x;
-  const uint16_t* xr = x + t * H;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * H);
   const int nvec = H / 8;                   // 16-byte vectors of 8 BF16
+  const int per_chunk = kPermThreads * kPermCache;
+  uint4 r[kPermCache];
+  auto load_chunk = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < kPermCache; ++i) {
+      const int v = base + threadIdx.x + i * kPermThreads;
+      r[i] = v < nvec ? xr[v] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
   if (threadIdx.x < K) {
     const int32_t d = map[t * K + threadIdx.x];
     dst[threadIdx.x] = (d >= 0 && d < limit) ? d : -1;
   }
+  // Without an expert range, capacity or row limit every token is moved: its first
+  // chunk is loaded while the row map arrives.
+  if (!may_skip) load_chunk(0);
   __syncthreads();
-  // A token none of whose ids is moved (out of the expert range, dropped, past the row
-  // limit) is not read at all.  The test is uniform over the workgroup.
-  bool any = false;
-  for (int j = 0; j < K; ++j) any |= dst[j] >= 0;
-  if (!any) return;
-  if (quant == 0) {
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-      uint4 d = reinterpret_cast<const uint4*>(xr)[v];
-      for (int j = 0; j < K; ++j) {
-        if (dst[j] < 0) continue;
-        uint16_t* o = static_cast<uint16_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
-        reinterpret_cast<uint4*>(o)[v] = d;
+  if (may_skip) {
+    // A token none of whose ids is moved is not read at all (uniform over the workgroup).
+    bool any = false;
+    for (int j = 0; j < K; ++j) any |= dst[j] >= 0;
+    if (!any) return;
+    load_chunk(0);
+  }
+  float scale = 0.0f;
+  if (quant == 1) {
+    float amax = 0.0f;
+    for (int base = 0; base < nvec; base += per_chunk) {
+      if (base > 0) load_chunk(base);
+#pragma unroll
+      for (int i = 0; i < kPermCache; ++i) {
+        const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[q] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+        }
       }
     }
-    if (row_scale && expanded_scale && threadIdx.x < K && dst[threadIdx.x] >= 0)
-      expanded_scale[dst[threadIdx.x]] = row_scale[t];
-    return;
+    amax = block_max(amax, red);
+    scale = amax / 127.0f;
+    if (nvec > per_chunk) load_chunk(0);      // the row did not stay in registers
   }
-  auto store8 = [&](int v, uint2 pv) {
-    for (int j = 0; j < K; ++j) {
-      if (dst[j] < 0) continue;
-      int8_t* o = static_cast<int8_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
-      reinterpret_cast<uint2*>(o)[v] = pv;
-    }
-  };
-  if (quant == 2) {
-    const float s = static_scale[0], off = static_offset[0];
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x)
-      store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v],
-                       [=](float xv) { return static_int8(xv, s, off); }));
-    return;
-  }
-  float amax = 0.0f;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    uint4 d = reinterpret_cast<const uint4*>(xr)[v];
-    uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  const float s_st = quant == 2 ? static_scale[0] : 0.0f;
+  const float o_st = quant == 2 ? static_offset[0] : 0.0f;
+  for (int base = 0; base < nvec; base += per_chunk) {
+    if (base > 0) load_chunk(base);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    for (int i = 0; i < kPermCache; ++i) {
+      const int v = base + threadIdx.x + i * kPermThreads;
+      if (v >= nvec) continue;
+      if (quant == 0) {
+        for (int j = 0; j < K; ++j) {
+          if (dst[j] < 0) continue;
+          uint16_t* o = static_cast<uint16_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
+          reinterpret_cast<uint4*>(o)[v] = r[i];
+        }
+        continue;
+      }
+      const uint2 pv =
+          quant == 2 ? quant8(r[i], [=](float xv) { return static_int8(xv, s_st, o_st); })
+                     : quant8(r[i], [=](float xv) {
+                         const float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
+                         return fminf(fmaxf(qf, -127.0f), 127.0f);
+                       });
+      for (int j = 0; j < K; ++j) {
+        if (dst[j] < 0) continue;
+        int8_t* o = static_cast<int8_t*>(expanded_x) + static_cast<int64_t>(dst[j]) * H;
+        reinterpret_cast<uint2*>(o)[v] = pv;
+      }
     }
   }
-  amax = block_max(amax, red);
-  const float scale = amax / 127.0f;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x)
-    store8(v, quant8(reinterpret_cast<const uint4*>(xr)[v], [=](float xv) {
-             const float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
-             return fminf(fmaxf(qf, -127.0f), 127.0f);
-           }));
-  if (threadIdx.x < K && dst[threadIdx.x] >= 0) expanded_scale[dst[threadIdx.x]] = scale;
+  if (threadIdx.x < K && dst[threadIdx.x] >= 0 && expanded_scale) {
+    if (quant == 1) expanded_scale[dst[threadIdx.x]] = scale;
+    else if (quant == 0 && row_scale) expanded_scale[dst[threadIdx.x]] = row_scale[t];
+  }
 }
 
 hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int quant,
-                                const int32_t* map, int64_t limit, const float* row_scale,
+                                const int32_t* map, int64_t limit, bool may_skip,
+                                const float* row_scale,
                                 const float* static_scale, const float* static_offset,
                                 void* expanded_x, float* expanded_scale, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  route_permute_kernel<<<dim3(static_cast<unsigned>(N)), dim3(256), 0, stream>>>(
-      x, H, K, quant, map, limit, row_scale, static_scale, static_offset, expanded_x,
+  route_permute_kernel<<<dim3(static_cast<unsigned>(N)), dim3(kPermThreads), 0, stream>>>(
+      x, H, K, quant, map, limit, may_skip, row_scale, static_scale, static_offset, expanded_x,
       expanded_scale);
   return hipGetLastError();
 }

@@ -155,6 +155,12 @@ V2_CASES = [
      dict(quant_mode=-1, expert_start=5, expert_end=50, row_idx_type=1), True),
     ("row_scale_droppad", 100, 4, 8, 72, 1.0,
      dict(quant_mode=-1, drop_pad_mode=1, expert_capacity=20), True),
+    # rows longer than the permute kernel's register chunk (8192 BF16): several chunks
+    ("dynamic_two_chunks", 50, 4, 16, 8200, 0.5, dict(quant_mode=1), False),
+    ("static_three_chunks_range", 20, 4, 16, 16392, 0.0,
+     dict(quant_mode=0, expert_start=2, expert_end=9), False),
+    ("bf16_two_chunks_droppad", 30, 2, 4, 9000, 0.0,
+     dict(drop_pad_mode=1, expert_capacity=5, quant_mode=-1), False),
 ]
 
 
