@@ -254,6 +254,86 @@ moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
                                size_t workspace_bytes, uint16_t* out, moe_stream_t stream,
                                void* const* events);
 
+/* ------------------------------------------------------------------------------------
+ * Chunk-streamed front end, one rank ("[RFC] Chunk-ready symmetric-buffer protocol for
+ * streaming MegaMoE inputs": sections "Fixed-capacity ring", "Independent readiness
+ * generations", "Memory ordering", "Chunk-aware dispatch scheduling" option 1 --
+ * chunk-local expert pools -- and "Progress and deadlock requirements").
+ *
+ * A caller-owned ring of num_slots slots of tokens_per_slot (C) tokens.  Token chunk n
+ * (tokens n*C .. min((n+1)*C, total) - 1) lives in slot n % num_slots.  Two producers fill
+ * a slot independently, in either order: the ROUTE producer writes expert_ids [C, k] i32
+ * and route_weights [C, k] BF16, the LAYOUT producer writes x [C, H] BF16.  Each producer,
+ * for each chunk, on its own stream:
+ *     moe_ring_acquire(slot, role)   -- waits until the consumer has finished the slot's
+ *                                       previous contents from this producer
+ *     ... write the payload part (kernels or copies on the same stream) ...
+ *     moe_ring_publish(slot, role)   -- publishes the next generation of its part
+ * moe_forward_streamed consumes chunks in order: it waits for both parts of a chunk, runs
+ * the whole layer on that chunk alone (its own routing and expert tiles) into out rows
+ * n*C .., and publishes the slot as consumed.  Generations are per slot and per role and
+ * count uses of the slot; all sequence counters live in the ring, so a launch sequence
+ * captured into a graph stays valid over any number of replays.  Publishes are
+ * system-scope release stores after the payload writes that precede them on the stream;
+ * waits are system-scope acquire loads.
+ *
+ * Progress: every wait is a one-workgroup kernel bounded by timeout_us (0 = 1 s).  When
+ * a wait expires it records MOE_RING_CONSUMER_TIMEOUT or MOE_RING_PRODUCER_TIMEOUT in the
+ * ring's status word (the first failure is kept) and returns; the work after it then runs
+ * on whatever the slot holds, and the ring must be re-initialized.  Serialized execution
+ * is valid whenever every publish a wait needs is enqueued before that wait on the same
+ * stream (for example all chunks produced into a ring of at least as many slots, then
+ * consumed; or produce/consume alternating per chunk).  Producer and consumer on
+ * different streams overlap.
+ * ------------------------------------------------------------------------------------ */
+typedef enum { MOE_RING_ROUTE = 0, MOE_RING_LAYOUT = 1 } moe_ring_role_t;
+
+/* Values of the ring's status word (u32 at moe_ring_layout_t.status). */
+#define MOE_RING_OK 0u
+#define MOE_RING_CONSUMER_TIMEOUT 1u
+#define MOE_RING_PRODUCER_TIMEOUT 2u
+
+typedef struct {
+  void* base;               /* device, 256-byte aligned */
+  size_t bytes;             /* >= moe_ring_layout().total */
+  int32_t num_slots;        /* 1 .. 4096 */
+  int32_t tokens_per_slot;  /* 1 .. MOE_MAX_TOKENS */
+} moe_ring_t;
+
+/* Byte offsets inside the ring (host-only):
+ *   x              BF16 [num_slots, C, H]
+ *   expert_ids     i32  [num_slots, C, k]
+ *   route_weights  BF16 [num_slots, C, k]
+ *   counters       one 64-byte record per slot: u32 route_ready_gen, layout_ready_gen,
+ *                  consumed_gen, then the three owners' private sequences
+ *   status         u32 */
+typedef struct {
+  size_t x, expert_ids, route_weights, counters, status, total;
+} moe_ring_layout_t;
+
+moe_status_t moe_ring_layout(moe_dims_t d, int32_t num_slots, int32_t tokens_per_slot,
+                             moe_ring_layout_t* out /*host*/);
+
+/* Zero the counters and the status word (a kernel on `stream`, no memset). */
+moe_status_t moe_ring_init(moe_dims_t d, const moe_ring_t* ring /*host*/, moe_stream_t stream);
+
+moe_status_t moe_ring_acquire(moe_dims_t d, const moe_ring_t* ring /*host*/, int32_t slot,
+                              moe_ring_role_t role, uint32_t timeout_us, moe_stream_t stream);
+
+moe_status_t moe_ring_publish(moe_dims_t d, const moe_ring_t* ring /*host*/, int32_t slot,
+                              moe_ring_role_t role, moe_stream_t stream);
+
+/* The layer (as moe_forward) over chunks first_chunk .. first_chunk + num_chunks - 1 of a
+ * stream of total_tokens tokens; out is BF16 [total_tokens, H] (device) and receives the
+ * rows of those chunks.  workspace: moe_workspace_size(d, tokens_per_slot) bytes. */
+moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring /*host*/,
+                                  int32_t total_tokens, int32_t first_chunk,
+                                  int32_t num_chunks, const void* prepared, const float* qx,
+                                  const float* alpha1, const float* qa, const float* alpha2,
+                                  const float* situ_beta, const float* situ_linear_beta,
+                                  uint32_t timeout_us, void* workspace, size_t workspace_bytes,
+                                  uint16_t* out, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,9 @@ __all__ = [
     "moe_prepared_weights_size", "moe_workspace_layout", "moe_route_workspace_size",
     "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_route_v2",
     "MoeRouteOptions", "moe_forward", "moe_forward_timed", "MOE_FORWARD_STAGES",
+    "MoeRing", "make_ring", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
+    "moe_ring_publish", "moe_forward_streamed", "MOE_RING_ROUTE", "MOE_RING_LAYOUT",
+    "MOE_RING_OK", "MOE_RING_CONSUMER_TIMEOUT", "MOE_RING_PRODUCER_TIMEOUT",
     "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
 ]
 
@@ -31,7 +34,14 @@ MOE_FORWARD_STAGES = 5
 EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_size",
             "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
             "moe_prepare_weights", "moe_route", "moe_route_v2", "moe_forward",
-            "moe_forward_timed")
+            "moe_forward_timed", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
+            "moe_ring_publish", "moe_forward_streamed")
+
+MOE_RING_ROUTE = 0
+MOE_RING_LAYOUT = 1
+MOE_RING_OK = 0
+MOE_RING_CONSUMER_TIMEOUT = 1
+MOE_RING_PRODUCER_TIMEOUT = 2
 
 
 class MoeError(RuntimeError):
@@ -59,6 +69,17 @@ class MoeRouteOptions(ctypes.Structure):
                  quant_mode=-1, drop_pad_mode=0, expert_capacity=-1, active_num=-1):
         super().__init__(expert_start, expert_end, row_idx_type, expert_tokens_num_type,
                          quant_mode, drop_pad_mode, expert_capacity, active_num)
+
+
+class MoeRing(ctypes.Structure):
+    """moe_ring_t: a caller-owned ring of token slots (device memory at `base`)."""
+    _fields_ = [("base", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
+                ("num_slots", ctypes.c_int32), ("tokens_per_slot", ctypes.c_int32)]
+
+
+class _RingLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "x", "expert_ids", "route_weights", "counters", "status", "total")]
 
 
 class _Layout(ctypes.Structure):
@@ -94,6 +115,13 @@ def _lib():
             "moe_forward": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]),
             "moe_forward_timed": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P,
                                        ctypes.POINTER(P)]),
+            "moe_ring_layout": (st, [MoeDims, I32, I32, ctypes.POINTER(_RingLayout)]),
+            "moe_ring_init": (st, [MoeDims, ctypes.POINTER(MoeRing), P]),
+            "moe_ring_acquire": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, ctypes.c_int,
+                                      ctypes.c_uint32, P]),
+            "moe_ring_publish": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, ctypes.c_int, P]),
+            "moe_forward_streamed": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, I32, I32, P, P,
+                                          P, P, P, P, P, ctypes.c_uint32, P, SZ, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -219,3 +247,43 @@ def moe_forward_timed(dims, T, x, expert_ids, route_weights, prepared, qx, alpha
         dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
         _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
         _ptr(workspace), nb, _ptr(out), _stream(stream), ev))
+
+
+def moe_ring_layout(dims, num_slots, tokens_per_slot):
+    lay = _RingLayout()
+    _check("moe_ring_layout", _lib().moe_ring_layout(dims, num_slots, tokens_per_slot,
+                                                     ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n, _ in _RingLayout._fields_}
+
+
+def make_ring(buffer, num_slots, tokens_per_slot):
+    """A MoeRing over a device byte buffer (a tensor or an int address with its size)."""
+    if isinstance(buffer, tuple):
+        base, nbytes = buffer
+    else:
+        base, nbytes = buffer.data_ptr(), _nbytes(buffer)
+    return MoeRing(base, nbytes, num_slots, tokens_per_slot)
+
+
+def moe_ring_init(dims, ring, stream=None):
+    _check("moe_ring_init", _lib().moe_ring_init(dims, ctypes.byref(ring), _stream(stream)))
+
+
+def moe_ring_acquire(dims, ring, slot, role, timeout_us=0, stream=None):
+    _check("moe_ring_acquire", _lib().moe_ring_acquire(dims, ctypes.byref(ring), slot, role,
+                                                       timeout_us, _stream(stream)))
+
+
+def moe_ring_publish(dims, ring, slot, role, stream=None):
+    _check("moe_ring_publish", _lib().moe_ring_publish(dims, ctypes.byref(ring), slot, role,
+                                                       _stream(stream)))
+
+
+def moe_forward_streamed(dims, ring, total_tokens, first_chunk, num_chunks, prepared, qx,
+                         alpha1, qa, alpha2, situ_beta, situ_linear_beta, workspace, out,
+                         timeout_us=0, workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_forward_streamed", _lib().moe_forward_streamed(
+        dims, ctypes.byref(ring), total_tokens, first_chunk, num_chunks, _ptr(prepared), _ptr(qx),
+        _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
+        timeout_us, _ptr(workspace), nb, _ptr(out), _stream(stream)))

@@ -2,6 +2,8 @@
 // Declarations and the contract of every entry point are in include/routed_moe.h.
 #include "routed_moe.h"
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,6 +37,51 @@ moe_status_t check_dims(const moe_dims_t& d) {
 }
 
 int padded_inter(int I) { return (I + kChunk - 1) / kChunk * kChunk; }
+
+// Streamed front end: ring carving and the device wall-clock rate for wait deadlines.
+moe_status_t ring_layout(const moe_dims_t& d, int32_t S, int32_t C, moe_ring_layout_t* L) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (S < 1 || S > 4096 || C < 1 || C > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  const size_t slot_tokens = static_cast<size_t>(S) * C;
+  Carver c;
+  L->x = c.take(slot_tokens * d.hidden * 2);
+  L->expert_ids = c.take(slot_tokens * d.top_k * 4);
+  L->route_weights = c.take(slot_tokens * d.top_k * 2);
+  L->counters = c.take(static_cast<size_t>(S) * sizeof(RingSlot));
+  L->status = c.take(4);
+  L->total = c.off;
+  return MOE_OK;
+}
+
+moe_status_t check_ring(const moe_dims_t& d, const moe_ring_t* r, moe_ring_layout_t* L) {
+  if (!r || !r->base) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = ring_layout(d, r->num_slots, r->tokens_per_slot, L);
+  if (st != MOE_OK) return st;
+  if (!aligned(r->base, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (r->bytes < L->total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+RingSlot* ring_slots(const moe_ring_t* r, const moe_ring_layout_t& L) {
+  return reinterpret_cast<RingSlot*>(static_cast<uint8_t*>(r->base) + L.counters);
+}
+
+uint32_t* ring_status(const moe_ring_t* r, const moe_ring_layout_t& L) {
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(r->base) + L.status);
+}
+
+// Wall-clock ticks of a timeout (0 = the default), on the current device.
+constexpr uint32_t kDefaultRingTimeoutUs = 1000000;
+bool ring_ticks(uint32_t timeout_us, int64_t* ticks) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    return false;
+  const uint64_t us = timeout_us ? timeout_us : kDefaultRingTimeoutUs;
+  *ticks = static_cast<int64_t>(us * static_cast<uint64_t>(khz) / 1000u);
+  return true;
+}
 
 struct Layout {
   moe_workspace_layout_t pub;
@@ -375,6 +422,99 @@ moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
   return forward_impl(d, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
                       situ_beta, situ_linear_beta, workspace, workspace_bytes, out, stream,
                       events);
+}
+
+moe_status_t moe_ring_layout(moe_dims_t d, int32_t num_slots, int32_t tokens_per_slot,
+                             moe_ring_layout_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  return ring_layout(d, num_slots, tokens_per_slot, out);
+}
+
+moe_status_t moe_ring_init(moe_dims_t d, const moe_ring_t* ring, moe_stream_t stream) {
+  moe_ring_layout_t L;
+  moe_status_t st = check_ring(d, ring, &L);
+  if (st != MOE_OK) return st;
+  // the counter records and the status word are contiguous
+  const int words = static_cast<int>((L.total - L.counters) / 4);
+  return hip_status(launch_ring_init(reinterpret_cast<uint32_t*>(ring_slots(ring, L)), words,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_ring_acquire(moe_dims_t d, const moe_ring_t* ring, int32_t slot,
+                              moe_ring_role_t role, uint32_t timeout_us, moe_stream_t stream) {
+  moe_ring_layout_t L;
+  moe_status_t st = check_ring(d, ring, &L);
+  if (st != MOE_OK) return st;
+  if (slot < 0 || slot >= ring->num_slots) return MOE_ERR_INVALID_ARG;
+  if (role != MOE_RING_ROUTE && role != MOE_RING_LAYOUT) return MOE_ERR_INVALID_ARG;
+  int64_t ticks = 0;
+  if (!ring_ticks(timeout_us, &ticks)) return MOE_ERR_HIP;
+  RingSlot* rs = ring_slots(ring, L) + slot;
+  const uint32_t* seq = role == MOE_RING_ROUTE ? &rs->route_seq : &rs->layout_seq;
+  // free for this producer once the consumer has finished its last publish of the slot
+  return hip_status(launch_ring_wait(&rs->consumed, nullptr, seq, 0u, ticks,
+                                     ring_status(ring, L), MOE_RING_PRODUCER_TIMEOUT,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_ring_publish(moe_dims_t d, const moe_ring_t* ring, int32_t slot,
+                              moe_ring_role_t role, moe_stream_t stream) {
+  moe_ring_layout_t L;
+  moe_status_t st = check_ring(d, ring, &L);
+  if (st != MOE_OK) return st;
+  if (slot < 0 || slot >= ring->num_slots) return MOE_ERR_INVALID_ARG;
+  if (role != MOE_RING_ROUTE && role != MOE_RING_LAYOUT) return MOE_ERR_INVALID_ARG;
+  RingSlot* rs = ring_slots(ring, L) + slot;
+  return hip_status(role == MOE_RING_ROUTE
+                        ? launch_ring_publish(&rs->route_ready, &rs->route_seq,
+                                              reinterpret_cast<hipStream_t>(stream))
+                        : launch_ring_publish(&rs->layout_ready, &rs->layout_seq,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring, int32_t total_tokens,
+                                  int32_t first_chunk, int32_t num_chunks,
+                                  const void* prepared, const float* qx, const float* alpha1,
+                                  const float* qa, const float* alpha2, const float* situ_beta,
+                                  const float* situ_linear_beta, uint32_t timeout_us,
+                                  void* workspace, size_t workspace_bytes, uint16_t* out,
+                                  moe_stream_t stream) {
+  moe_ring_layout_t L;
+  moe_status_t st = check_ring(d, ring, &L);
+  if (st != MOE_OK) return st;
+  const int64_t C = ring->tokens_per_slot, S = ring->num_slots;
+  if (total_tokens < 1 || first_chunk < 0 || num_chunks < 1) return MOE_ERR_INVALID_ARG;
+  const int64_t chunks = (total_tokens + C - 1) / C;
+  if (static_cast<int64_t>(first_chunk) + num_chunks > chunks) return MOE_ERR_INVALID_ARG;
+  if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  size_t need = 0;
+  st = moe_workspace_size(d, static_cast<int32_t>(C), &need);
+  if (st != MOE_OK) return st;
+  if (!workspace || workspace_bytes < need) return workspace ? MOE_ERR_WORKSPACE_TOO_SMALL
+                                                             : MOE_ERR_INVALID_ARG;
+  int64_t ticks = 0;
+  if (!ring_ticks(timeout_us, &ticks)) return MOE_ERR_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ring->base);
+  const int H = d.hidden, k = d.top_k;
+  for (int64_t n = first_chunk; n < first_chunk + num_chunks; ++n) {
+    const int64_t slot = n % S;
+    const int32_t valid = static_cast<int32_t>(std::min<int64_t>(C, total_tokens - n * C));
+    RingSlot* rs = ring_slots(ring, L) + slot;
+    if (launch_ring_wait(&rs->route_ready, &rs->layout_ready, &rs->consumer_seq, 1u, ticks,
+                         ring_status(ring, L), MOE_RING_CONSUMER_TIMEOUT, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(base + L.x) + slot * C * H;
+    const int32_t* ids = reinterpret_cast<const int32_t*>(base + L.expert_ids) + slot * C * k;
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(base + L.route_weights) + slot * C * k;
+    st = forward_impl(d, valid, x, ids, w, prepared, qx, alpha1, qa, alpha2, situ_beta,
+                      situ_linear_beta, workspace, workspace_bytes, out + n * C * H, stream,
+                      nullptr);
+    if (st != MOE_OK) return st;
+    if (launch_ring_publish(&rs->consumed, &rs->consumer_seq, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

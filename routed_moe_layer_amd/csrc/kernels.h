@@ -82,6 +82,23 @@ hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int 
 hipError_t launch_route_pad_fill(const int32_t* counts, int E, int C, int64_t row_bytes,
                                  void* expanded_x, float* expanded_scale, hipStream_t stream);
 
+// Streamed front end (stream.hip): one 64-byte counter record per ring slot.
+struct RingSlot {
+  uint32_t route_ready;    // generation the routing producer last published
+  uint32_t layout_ready;   // generation the layout producer last published
+  uint32_t consumed;       // generation the consumer last finished
+  uint32_t route_seq;      // routing producer's sequence
+  uint32_t layout_seq;     // layout producer's sequence
+  uint32_t consumer_seq;   // consumer's sequence
+  uint32_t pad[10];
+};
+static_assert(sizeof(RingSlot) == 64, "one counter record per 64 bytes");
+hipError_t launch_ring_init(uint32_t* words, int n, hipStream_t stream);
+hipError_t launch_ring_wait(const uint32_t* a, const uint32_t* b, const uint32_t* seq,
+                            uint32_t add, int64_t ticks, uint32_t* status, uint32_t code,
+                            hipStream_t stream);
+hipError_t launch_ring_publish(uint32_t* gen, uint32_t* seq, hipStream_t stream);
+
 hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
                                   const uint8_t* w13_sf, const uint8_t* w2,
                                   const uint8_t* w2_sf, uint8_t* prepared, hipStream_t stream);
