@@ -11,11 +11,12 @@ GEMM, bound by the f16 MFMA).  The decode (T=16) and mid (T=1024, Zipf 1.0) batc
 reported under "workloads" with their HBM rooflines, and the routing-and-int8-permute
 primitive (moe_route, N=8192, H=7168, E=256, K=8) under "routing_primitive" with its
 routed rows/s and HBM fraction, and two cases of its options (moe_route_v2) under
-"routing_primitive.options".  Per-stage times come from HIP events recorded between
+"routing_primitive.options", and the layer through the chunk-streamed front end
+(moe_forward_streamed fed by a producer on a second stream) under "streamed".  Per-stage times come from HIP events recorded between
 the stages on the launch stream (moe_forward_timed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workloads prefill,decode,mid,route] [--summarize DIR]
+                       [--workloads prefill,decode,mid,route,stream] [--summarize DIR]
 """
 
 import argparse
@@ -212,6 +213,57 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     keep = dict(x=x, ids=ids_host[0], rw=rw, qx=qx, alpha1=alpha1, qa=qa, alpha2=alpha2,
                 beta=beta, lam=lam)
     return res, keep
+
+
+# The chunk-streamed front end: (layer workload, tokens per slot, ring slots).
+STREAM_CASES = {"prefill": (4096, 2), "mid": (256, 2)}
+
+
+def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmup, events):
+    """Time the streamed layer on a layer workload's inputs: per step, the consumer
+    (moe_forward_streamed over every chunk) is enqueued on the launch stream and a
+    producer on a second stream fills a `slots`-slot ring chunk by chunk (copies of the
+    resident ids, route weights and x into the slot, each part acquired and published),
+    so production overlaps the layer's work on earlier chunks."""
+    E, H, I, k, T = cfg.E, cfg.H, cfg.I, cfg.k, cfg.T
+    dims = rm.MoeDims(H, I, E, k)
+    x, rw = keep["x"], keep["rw"]
+    ids = torch.from_numpy(np.ascontiguousarray(keep["ids"])).cuda()
+    lay = rm.moe_ring_layout(dims, slots, chunk)
+    buf = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    ring = rm.make_ring(buf, slots, chunk)
+    rx = buf[lay["x"]:].view(torch.int16)[:slots * chunk * H].view(slots, chunk, H)
+    rids = buf[lay["expert_ids"]:].view(torch.int32)[:slots * chunk * k].view(slots, chunk, k)
+    rrw = buf[lay["route_weights"]:].view(torch.int16)[:slots * chunk * k].view(slots, chunk, k)
+    ws = torch.empty(rm.moe_workspace_size(dims, chunk), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    n = (T + chunk - 1) // chunk
+    prod = torch.cuda.Stream()
+    rm.moe_ring_init(dims, ring)
+    torch.cuda.synchronize()
+
+    def step():
+        rm.moe_forward_streamed(dims, ring, T, 0, n, prepared, keep["qx"], keep["alpha1"],
+                                keep["qa"], keep["alpha2"], keep["beta"], keep["lam"], ws, out)
+        with torch.cuda.stream(prod):
+            for i in range(n):
+                sl, lo, hi = i % slots, i * chunk, min(T, (i + 1) * chunk)
+                rm.moe_ring_acquire(dims, ring, sl, rm.MOE_RING_ROUTE, stream=prod)
+                rids[sl, :hi - lo].copy_(ids[lo:hi])
+                rrw[sl, :hi - lo].copy_(rw[lo:hi])
+                rm.moe_ring_publish(dims, ring, sl, rm.MOE_RING_ROUTE, stream=prod)
+                rm.moe_ring_acquire(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
+                rx[sl, :hi - lo].copy_(x[lo:hi])
+                rm.moe_ring_publish(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
+
+    gpu_ms, wall_ms = _time_calls(step, torch, steps, warmup, events)
+    torch.cuda.synchronize()
+    status = int(buf[lay["status"]:lay["status"] + 4].view(torch.int32).item())
+    if status != rm.MOE_RING_OK:
+        raise RuntimeError(f"streamed run ended with ring status {status}")
+    return {"workload": f"{cfg.name}_streamed_C{chunk}_S{slots}", "chunks": n,
+            "tokens_per_s": T / (wall_ms * 1e-3), "ms_per_step": wall_ms,
+            "gpu_ms_per_step": gpu_ms}
 
 
 def _time_calls(call, torch, steps, warmup, events):
@@ -585,7 +637,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="prefill,decode,mid,route")
+    ap.add_argument("--workloads", default="prefill,decode,mid,route,stream")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens of the oracle's bounded CPU sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -618,7 +670,7 @@ def main():
         return
     rm._lib()
     events = HipEvents()
-    chosen = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    chosen = [w.strip() for w in args.workloads.split(",") if w.strip() and w.strip() != "stream"]
     if any(c != "route" for c in chosen):
         prepared, d13, d2 = build_weights(DECODE_16, torch, rm)
     cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4)}
@@ -645,6 +697,19 @@ def main():
         r = results[name]
         log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step, stages "
             + ", ".join(f"{k} {v:.3f}" for k, v in r["stage_ms"].items()))
+    streamed = {}
+    if "stream" in [w.strip() for w in args.workloads.split(",")]:
+        for name, (chunk, slots) in STREAM_CASES.items():
+            if name not in keeps:
+                continue
+            cfg = cfgs[name][0]
+            log(f"timing {cfg.name} streamed in chunks of {chunk} through {slots} slots")
+            r = streamed_workload(cfg, keeps[name], torch, rm, prepared, chunk, slots,
+                                  args.steps, args.warmup, events)
+            r["batch_tokens_per_s"] = results[name]["tokens_per_s"]
+            streamed[name] = r
+            log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step "
+                f"(batch {results[name]['tokens_per_s']:.1f})")
     if not chosen:                      # routing primitive only
         print(json.dumps({"routing_primitive": route_res}), flush=True)
         return
@@ -673,6 +738,7 @@ def main():
         "config": {"workload": hcfg.name, "T": hcfg.T, "H": hcfg.H, "I": hcfg.I, "E": hcfg.E,
                    "top_k": hcfg.k, "parallelism": "single GPU (one TP8 rank's share)"},
         "roofline": roof, "cpu_baseline": cpu, "workloads": results, "routing_primitive": route_res,
+        "streamed": streamed or None,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
