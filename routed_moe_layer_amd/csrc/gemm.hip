@@ -233,36 +233,57 @@ using StageOf = typename std::conditional<ROWS, RowStage<NW, BN>, CodeStage<MODE
 //   4. run the MFMAs,
 //   5. store chunk c+1's tokens into the other LDS buffer.
 //
-// With WRG == 4 the weight fragments are decoded one 32-column K-step at a time (16
-// instead of 64 registers of decoded operands), and the weight loads of chunk c+2 are
-// issued after the last step's decode.
+// With WRG == 4 the weight fragments are decoded one 32-column K-step at a time and
+// software-pipelined: step s+1's fragments are decoded while step s's MFMAs run.  Chunk
+// c+2's weight loads are issued in step 3, after the last decode of chunk c.  The LDS
+// operand of each 16-token block is read one block ahead, across K-steps within the chunk.
 template <int WRG, int NCBA, int DEPTH, class Stage>
 __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, int c,
                                            uint4 (&wc)[WRG], uint32_t (&ws)[WRG],
                                            typename Stage::Regs& tr, const _Float16* tb_cur,
                                            _Float16* tb_next, f32x4 (&acc)[WRG][NCBA]) {
   constexpr bool kPerStep = WRG >= 4;
-  auto decode_step = [&](int s, f16x8 (&dst)[WRG]) {
+  auto decode_from = [&](const uint4 (&rc)[WRG], const uint32_t (&rs)[WRG], int s,
+                         f16x8 (&dst)[WRG]) {
 #pragma unroll
     for (int r = 0; r < WRG; ++r) {
-      const uint32_t cw = s == 0 ? wc[r].x : s == 1 ? wc[r].y : s == 2 ? wc[r].z : wc[r].w;
-      dst[r] = decode8(cw, scale_f16x2((ws[r] >> (8 * s)) & 0xFFu));
+      const uint32_t cw = s == 0 ? rc[r].x : s == 1 ? rc[r].y : s == 2 ? rc[r].z : rc[r].w;
+      dst[r] = decode8(cw, scale_f16x2((rs[r] >> (8 * s)) & 0xFFu));
     }
   };
   if constexpr (kPerStep) {
     const bool more = c + 1 < t.nchunks;
     st.template load<16 * NCBA>(min(c + 1, t.nchunks - 1), tr);
     __syncthreads();                                    // LDS buffer of chunk c complete
+    f16x8 wf0[WRG], wf1[WRG];
+    decode_from(wc, ws, 0, wf0);
+    f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, 0, 0, t.lane));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f16x8 wf[WRG];
-      decode_step(s, wf);
-      if (s == 3) load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
+      f16x8 (&cur)[WRG] = (s & 1) ? wf1 : wf0;
+      f16x8 (&nxt)[WRG] = (s & 1) ? wf0 : wf1;
+      if (s < 3) decode_from(wc, ws, s + 1, nxt);
+      else load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, cb, s, t.lane));
+        const bool ahead = cb + 1 < NCBA || s < 3;
+        const f16x8 xn = ahead
+            ? *reinterpret_cast<const f16x8*>(
+                  Stage::frag(tb_cur, cb + 1 < NCBA ? cb + 1 : 0, cb + 1 < NCBA ? s : s + 1, t.lane))
+            : xf;
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(wf[r], xf, acc[r][cb]);
+        for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(cur[r], xf, acc[r][cb]);
+        xf = xn;
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCBA; ++cb) {
+        if (cb + 1 < NCBA || s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int r = 0; r < WRG; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU (next decode)
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -271,7 +292,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
   }
   f16x8 wf[4][WRG];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) decode_step(s, wf[s]);
+  for (int s = 0; s < 4; ++s) decode_from(wc, ws, s, wf[s]);
   // Token loads first, so the wait before their LDS store (end of this step) leaves the
   // younger weight loads in flight.  Both are issued unconditionally (chunk index clamped,
   // the surplus loads are never used): with no branch around them the compiler's wait
@@ -514,7 +535,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 // MFMA; the f16 rows no longer fit in registers, so the tokens are staged as codes).
 // A slab that does not divide the rows falls back to 128-row slabs.
 constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
-constexpr int kFc1WideWRG = 4;
+constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
 constexpr int64_t kManyRows = 2 * 256 * kBigRows;
 
 template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
@@ -536,7 +557,7 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
   if constexpr (MODE == 0) {
     if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
-      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
+      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);
       return hipGetLastError();
     }
   }
