@@ -488,11 +488,11 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 // the rows in flat id order, so a token's k rows are one contiguous run.  A workgroup
 // covers 8*kFinThreads columns of one token; each thread owns 8 columns and issues the
 // 16-byte loads of up to kFinBatch rows before it accumulates them.
-constexpr int kFinThreads = 256, kFinBatch = 8;
+constexpr int kFinThreads = 512, kFinBatch = 8;
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
   const int64_t t = blockIdx.x / col_blocks;
-  const int v = (blockIdx.x % col_blocks) * kFinThreads + threadIdx.x;
+  const int v = (blockIdx.x % col_blocks) * blockDim.x + threadIdx.x;
   if (v >= a.H / 8) return;
   const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
@@ -583,10 +583,14 @@ hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
-  const int col_blocks = (a.H / 8 + kFinThreads - 1) / kFinThreads;
+  // whole waves covering a token's H/8 vectors in as few workgroups as possible
+  const int vecs = a.H / 8;
+  const int col_blocks = (vecs + kFinThreads - 1) / kFinThreads;
+  const int per_block = (vecs + col_blocks - 1) / col_blocks;
+  const int threads = (per_block + 63) / 64 * 64;
   const int64_t grid = static_cast<int64_t>(a.T) * col_blocks;
   if (grid > 0)
-    finalize_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kFinThreads), 0, stream>>>(a, col_blocks);
+    finalize_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
   return hipGetLastError();
 }
 
