@@ -528,14 +528,18 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 }
 
 
-// Variants: small tiles (up to 32 tokens) run 4 waves x 2 groups (128-row slabs) and
-// stage FC1's tokens as f16 rows.  Big tiles (up to kBigRows tokens) run 4 waves x 2
+// Variants: small tiles (up to 32 tokens) run 4 waves x 4 groups (256-row slabs) in FC1
+// and 4 waves x 2 groups (128-row slabs) in FC2 or when the rows do not divide, and stage
+// FC1's tokens as f16 rows.  Big tiles (up to kBigRows tokens) run 4 waves x 2
 // groups, FC1 with f16 rows; with at least kManyRows routed rows (about two big tiles
 // per CU) FC1's big tiles run 4 waves x 4 groups instead (half the LDS operand reads per
 // MFMA; the f16 rows no longer fit in registers, so the tokens are staged as codes).
 // A slab that does not divide the rows falls back to 128-row slabs.
 constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
 constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
+// FC1 small tiles: 4 row groups per wave (256-row slabs), so that a decode-size batch's
+// workgroups fit the chip in one round instead of 1.3.
+constexpr int kFc1SmallWRG = 4;
 constexpr int64_t kManyRows = 2 * 256 * kBigRows;
 
 template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
@@ -554,7 +558,10 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   constexpr bool kRows = MODE == 0;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const bool many = static_cast<int64_t>(a.T) * a.k >= kManyRows;
-  launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
+  if (MODE == 0 && rows_total % GemmCfg<MODE, 4, kFc1SmallWRG, kSmallRows>::kWgRows == 0)
+    launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, kRows>(a, a.max_small, 0, stream);
+  else
+    launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
   if constexpr (MODE == 0) {
     if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
       launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);
