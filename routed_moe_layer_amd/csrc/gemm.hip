@@ -498,20 +498,22 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
-    uint4 d[kFinBatch];
+    u32x4 d[kFinBatch];
     bool ok[kFinBatch];
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
       const int j = j0 + u;
       ok[u] = j < a.k && pos_t[j] >= 0;         // < 0: dropped (expert id out of range)
-      d[u] = ok[u] ? reinterpret_cast<const uint4*>(a.o_rows + (t * a.k + j) * a.H)[v]
-                   : uint4{0, 0, 0, 0};
+      // read once, never again: nontemporal, so the rows do not displace cached data
+      d[u] = ok[u] ? __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x4*>(a.o_rows + (t * a.k + j) * a.H) + v)
+                   : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
       if (!ok[u]) continue;
       const float wt = bf16_to_f32(w_t[j0 + u]);
-      const uint32_t dw[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
+      const uint32_t dw[4] = {d[u][0], d[u][1], d[u][2], d[u][3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = fmaf(wt, __uint_as_float(dw[i] << 16), acc[2 * i]);
