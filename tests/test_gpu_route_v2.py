@@ -208,3 +208,55 @@ def test_route_v2_defaults_equal_moe_route():
     assert np.array_equal(got["expanded_scale"], host(esc))
     assert np.array_equal(got["expanded_row_idx"], host(eri))
     assert np.array_equal(got["expert_tokens"], host(cs))
+
+
+def _random_case(rng):
+    E = int(rng.choice([1, 3, 16, 64, 256, 897, 4096]))
+    K = int(rng.integers(1, min(E, 16) + 1))
+    N = int(rng.choice([1, 2, 7, 31, 128, 300, 1000]))
+    H = int(rng.choice([8, 64, 136, 2048, 8200]))
+    if N * H > 2_000_000:
+        H = 64
+    opts = {"row_idx_type": int(rng.integers(0, 2)),
+            "expert_tokens_num_type": int(rng.integers(0, 3)),
+            "quant_mode": int(rng.integers(-1, 2))}
+    if rng.random() < 0.3 and opts["row_idx_type"] == 0:
+        opts["drop_pad_mode"] = 1
+        opts["expert_capacity"] = int(rng.integers(1, min(N * K, max(2, N * K // E * 2)) + 1))
+    else:
+        if rng.random() < 0.5:
+            s = int(rng.integers(0, E))
+            opts["expert_start"], opts["expert_end"] = s, int(rng.integers(s + 1, E + 1))
+        if rng.random() < 0.3:
+            opts["active_num"] = int(rng.integers(1, N * K + 5))
+    zipf = float(rng.choice([0.0, 1.0, 1.5]))
+    row_scale = opts["quant_mode"] == -1 and rng.random() < 0.5
+    return N, K, E, H, zipf, opts, row_scale
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_route_v2_random_options_bit_exact(seed):
+    """Seeded random shapes and option combinations (expert range, index type, histogram
+    mode, quant mode, drop/pad capacity, active_num, per-row scale)."""
+    rng = np.random.default_rng(9000 + seed)
+    N, K, E, H, zipf, opts, rs = _random_case(rng)
+    _say(f"route_v2 random {seed}: N={N} K={K} E={E} H={H} zipf={zipf} {opts} row_scale={rs}")
+    ids = draw_expert_ids(N, E, K, seed_index=2000 + seed, zipf_s=zipf)
+    x = draw_tokens(N, H, seed_index=2000 + seed)
+    row_scale = rng.standard_normal(N).astype(np.float32) if rs else None
+    got = run_v2(x, ids, E, opts, row_scale)
+    want = oracle_v2(x, ids, E, opts, row_scale)
+    check_v2(got, want, opts)
+
+
+def test_route_v2_drop_pad_kv_many_ids():
+    """Drop/pad with key_value counts past 2^21 routed rows (several router tiles and the
+    26-bit row fields of the expert scan)."""
+    _say("route_v2 drop/pad, 2.4 M ids")
+    N, K, E, H = 300_000, 8, 64, 8
+    ids = draw_expert_ids(N, E, K, seed_index=2100, zipf_s=1.2)
+    x = draw_tokens(N, H, seed_index=2100)
+    opts = dict(drop_pad_mode=1, expert_capacity=20_000, quant_mode=1, expert_tokens_num_type=2)
+    got = run_v2(x, ids, E, opts)
+    want = oracle_v2(x, ids, E, opts)
+    check_v2(got, want, opts)
