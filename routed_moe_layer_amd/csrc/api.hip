@@ -376,9 +376,6 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
            hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  hipError_t e = launch_quantize_nvfp4(x, 1, T, H, qx, ws + L.pub.x_codes, ws + L.pub.x_scales,
-                                     reinterpret_cast<uint16_t*>(ws + L.pub.x_dec), s);
-  if (e != hipSuccess || !mark(1)) return MOE_ERR_HIP;
   RouteBuffers b{};
   b.tile_hist = reinterpret_cast<int32_t*>(ws + L.tile_hist);
   b.counts = reinterpret_cast<int32_t*>(ws + L.pub.expert_counts);
@@ -391,7 +388,22 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   b.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   b.amax_reset = a.a_amax;
-  if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+  uint8_t* x_codes = ws + L.pub.x_codes;
+  uint8_t* x_scales = ws + L.pub.x_scales;
+  uint16_t* x_dec = reinterpret_cast<uint16_t*>(ws + L.pub.x_dec);
+  if (route_fits_one_workgroup(R, E)) {
+    // small batch: quantization and routing in one launch (both stage marks after it)
+    const QuantizeArgs qa{x, static_cast<int64_t>(T) * (H / kGroup), H / kGroup, T, qx,
+                          x_codes, x_scales, x_dec};
+    if (launch_quantize_route_small(qa, expert_ids, R, E, b, s) != hipSuccess || !mark(1) ||
+        !mark(2))
+      return MOE_ERR_HIP;
+  } else {
+    if (launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales, x_dec, s) != hipSuccess ||
+        !mark(1))
+      return MOE_ERR_HIP;
+    if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+  }
   if (launch_fc1(a, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
   if (launch_fc2(a, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
   if (launch_finalize(a, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;

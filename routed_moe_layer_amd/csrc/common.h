@@ -145,4 +145,43 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Group-16 NVFP4 quantization of 16-value block b of BF16 rows (blocks_per_row blocks per
+// row, one encoding scale q[row / rows_per_group] per group of rows): 8 bytes of codes, the
+// E4M3 block scale and, when `decoded` is given, the block's decoded values in f16 (code
+// times block scale, exact).  Shared by the quantization kernel and the fused
+// quantize-and-route kernel.
+__device__ __forceinline__ void quantize_nvfp4_block(const uint16_t* __restrict__ src, int64_t b,
+                                                     int blocks_per_row, int64_t rows_per_group,
+                                                     const float* __restrict__ q,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     uint16_t* __restrict__ decoded) {
+  const int64_t row = b / blocks_per_row;
+  const float qv = q[row / rows_per_group];
+  const uint4* p = reinterpret_cast<const uint4*>(src + b * kGroup);
+  const uint4 lo = p[0], hi = p[1];
+  const uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(wv[i] << 16);
+    v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  float enc;
+  const uint32_t sb = nvfp4_block_scale(amax, qv, &enc);
+  uint2 out;
+  out.x = pack8_codes(v, enc);
+  out.y = pack8_codes(v + 8, enc);
+  reinterpret_cast<uint2*>(codes)[b] = out;
+  scales[b] = static_cast<uint8_t>(sb);
+  if (decoded) {
+    const f16x2 sc = scale_f16x2(sb);
+    f16x8* d = reinterpret_cast<f16x8*>(decoded + b * kGroup);
+    d[0] = decode8(out.x, sc);
+    d[1] = decode8(out.y, sc);
+  }
+}
+
 }  // namespace rmoe

@@ -67,6 +67,22 @@ struct RouteBuffers {
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
                         hipStream_t stream);
 
+// Small batches: NVFP4 quantization of the tokens and the router in one launch, when the
+// router runs as a single workgroup (route_fits_one_workgroup).
+struct QuantizeArgs {
+  const uint16_t* src;       // BF16 rows
+  int64_t nblocks;           // 16-value blocks in all rows
+  int blocks_per_row;
+  int64_t rows_per_group;
+  const float* q;            // encoding scale per group of rows
+  uint8_t* codes;
+  uint8_t* scales;
+  uint16_t* decoded;         // or null
+};
+bool route_fits_one_workgroup(int64_t n, int E);
+hipError_t launch_quantize_route_small(const QuantizeArgs& qa, const int32_t* ids, int64_t n,
+                                       int E, const RouteBuffers& b, hipStream_t stream);
+
 // Token movement of the routing primitive: token row t goes to rows map[t*K + j] (skipped
 // when negative or >= limit).  may_skip: some tokens may have no row to go to (an expert
 // range, capacity or row limit); such tokens are then not read.  quant 0: BF16 copy (plus row_scale[t] to expanded_scale

@@ -282,11 +282,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
 // histograms [4][E] (after the ranking, exclusive over waves) and the expert offsets [E].
 constexpr int kRouteSmallThreads = 1024;
 
-__global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
-  extern __shared__ int32_t lds[];
-  __shared__ uint64_t sh[16];
-  __shared__ int carry[3];
+__device__ __forceinline__ void route_small_body(const int32_t* __restrict__ ids, int64_t n,
+                                                 int E, int nbits, const RouteBuffers& b,
+                                                 int32_t* lds, uint64_t* sh, int* carry) {
   constexpr int nw = kRouteThreads / kWave;            // ranking waves
   int32_t* wave_hist = lds;
   int32_t* off_sh = lds + nw * E;
@@ -328,12 +326,52 @@ __global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
   }
 }
 
+__global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
+  extern __shared__ int32_t lds[];
+  __shared__ uint64_t sh[16];
+  __shared__ int carry[3];
+  route_small_body(ids, n, E, nbits, b, lds, sh, carry);
+}
+
+// Small batches: the token quantization and the single-workgroup router in one launch
+// (they are independent).  Workgroup 0 routes; workgroups 1.. quantize 1024 blocks each.
+__global__ __launch_bounds__(kRouteSmallThreads) void quantize_route_small_kernel(
+    QuantizeArgs qa, const int32_t* __restrict__ ids, int64_t n, int E, int nbits,
+    RouteBuffers b) {
+  extern __shared__ int32_t lds[];
+  __shared__ uint64_t sh[16];
+  __shared__ int carry[3];
+  if (blockIdx.x == 0) {
+    route_small_body(ids, n, E, nbits, b, lds, sh, carry);
+    return;
+  }
+  const int64_t blk = static_cast<int64_t>(blockIdx.x - 1) * kRouteSmallThreads + threadIdx.x;
+  if (blk < qa.nblocks)
+    quantize_nvfp4_block(qa.src, blk, qa.blocks_per_row, qa.rows_per_group, qa.q, qa.codes,
+                         qa.scales, qa.decoded);
+}
+
+bool route_fits_one_workgroup(int64_t n, int E) {
+  const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
+  return route_tiles(n) == 1 && small_lds <= kRouteSmallMaxLds;
+}
+
+hipError_t launch_quantize_route_small(const QuantizeArgs& qa, const int32_t* ids, int64_t n,
+                                       int E, const RouteBuffers& b, hipStream_t stream) {
+  const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
+  const int64_t qblocks = (qa.nblocks + kRouteSmallThreads - 1) / kRouteSmallThreads;
+  quantize_route_small_kernel<<<dim3(static_cast<unsigned>(1 + qblocks)), dim3(kRouteSmallThreads),
+                                small_lds, stream>>>(qa, ids, n, E, bits_for(E), b);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
                         hipStream_t stream) {
   const int nt = route_tiles(n);
   if (nt == 0) return hipSuccess;
   const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
-  if (nt == 1 && small_lds <= kRouteSmallMaxLds) {
+  if (route_fits_one_workgroup(n, E)) {
     route_small_kernel<<<dim3(1), dim3(kRouteSmallThreads), small_lds, stream>>>(
         ids, n, E, bits_for(E), b);
     return hipGetLastError();
