@@ -233,6 +233,11 @@ moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, in
   b.sorted_row_idx = sorted_row_idx;
   b.expanded_row_idx = expanded_row_idx;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (route_permute_fits_one_workgroup(n, num_experts, num_rows, hidden)) {
+    const PermuteArgs p{x, num_rows, hidden, top_k, static_cast<int>(quant), INT64_MAX,
+                        nullptr, nullptr, nullptr, expanded_x, expanded_scale};
+    return hip_status(launch_route_permute_small(expert_idx, n, num_experts, b, p, s));
+  }
   hipError_t e = launch_route(expert_idx, n, num_experts, b, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_route_permute(x, num_rows, hidden, top_k, static_cast<int>(quant), expanded_row_idx,
@@ -301,15 +306,22 @@ moe_status_t moe_route_v2(int32_t num_rows, int32_t hidden, int32_t num_experts,
     else { b.key_value = expert_tokens; b.kv_rows = num_experts; }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_route(expert_idx, n, E_act, b, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   const int quant = o.quant_mode == -1 ? 0 : (o.quant_mode == 1 ? 1 : 2);
   const int64_t limit = drop_pad ? static_cast<int64_t>(num_experts) * o.expert_capacity
                                  : (o.active_num > 0 ? o.active_num : INT64_MAX);
-  const bool may_skip = E_act != num_experts || drop_pad || o.active_num > 0;
-  e = launch_route_permute(x, num_rows, hidden, top_k, quant, map, limit, may_skip,
-                           o.quant_mode == -1 ? scale : nullptr, scale, offset, expanded_x,
-                           expanded_scale, s);
+  const float* row_scale = o.quant_mode == -1 ? scale : nullptr;
+  hipError_t e;
+  if (route_permute_fits_one_workgroup(n, E_act, num_rows, hidden)) {
+    const PermuteArgs p{x, num_rows, hidden, top_k, quant, limit, row_scale, scale, offset,
+                        expanded_x, expanded_scale};
+    e = launch_route_permute_small(expert_idx, n, E_act, b, p, s);
+  } else {
+    e = launch_route(expert_idx, n, E_act, b, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    const bool may_skip = E_act != num_experts || drop_pad || o.active_num > 0;
+    e = launch_route_permute(x, num_rows, hidden, top_k, quant, map, limit, may_skip,
+                             row_scale, scale, offset, expanded_x, expanded_scale, s);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (drop_pad) {
     const int64_t row_bytes = static_cast<int64_t>(hidden) * (quant == 0 ? 2 : 1);

@@ -184,4 +184,39 @@ __device__ __forceinline__ void quantize_nvfp4_block(const uint16_t* __restrict_
   }
 }
 
+// Routing-primitive int8 helpers (shared by the permute kernel and the fused small
+// route-and-permute kernel).
+// Maximum of v over the workgroup (red: one float per wave in LDS).
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < static_cast<int>(blockDim.x / kWave); ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// Static quantization of one value: the product and the sum are rounded to fp32 one at a
+// time (no fused multiply-add), then rounded half to even and saturated.
+__device__ __forceinline__ float static_int8(float x, float s, float o) {
+#pragma clang fp contract(off)
+  const float y = x * s + o;
+  return fminf(fmaxf(rintf(y), -128.0f), 127.0f);
+}
+
+// Eight BF16 values (one 16-byte vector) to eight int8 codes through q().
+template <class Q>
+__device__ __forceinline__ uint2 quant8(uint4 d, Q q) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
+    const float qf = q(__uint_as_float(bits));
+    packed[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+
 }  // namespace rmoe

@@ -80,6 +80,23 @@ struct QuantizeArgs {
   uint16_t* decoded;         // or null
 };
 bool route_fits_one_workgroup(int64_t n, int E);
+
+// Routing primitive on a few tokens: routing and token movement in one workgroup (see
+// launch_route_permute for the modes).  Applies when route_permute_fits_one_workgroup.
+struct PermuteArgs {
+  const uint16_t* x;
+  int64_t N;
+  int H, K, quant;
+  int64_t limit;
+  const float* row_scale;
+  const float* static_scale;
+  const float* static_offset;
+  void* expanded_x;
+  float* expanded_scale;
+};
+bool route_permute_fits_one_workgroup(int64_t n, int E, int64_t N, int H);
+hipError_t launch_route_permute_small(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
+                                      const PermuteArgs& p, hipStream_t stream);
 hipError_t launch_quantize_route_small(const QuantizeArgs& qa, const int32_t* ids, int64_t n,
                                        int E, const RouteBuffers& b, hipStream_t stream);
 

@@ -223,13 +223,14 @@ __device__ __forceinline__ void rank_wave_ids(const int32_t* __restrict__ ids, i
 
 // Final placement of in-range flat id f of expert key e, rank r_in within its expert and
 // expert offset off.
-__device__ __forceinline__ void place_id(const RouteBuffers& b, int e, int64_t f, int off,
-                                         int r_in) {
+__device__ __forceinline__ int32_t place_id(const RouteBuffers& b, int e, int64_t f, int off,
+                                            int r_in) {
   const int pos = off + r_in;
   if (b.sorted_ids) b.sorted_ids[pos] = e + b.e_base;
   if (b.sorted_row_idx) b.sorted_row_idx[pos] = static_cast<int32_t>(f);
-  b.expanded_row_idx[f] =
-      b.capacity > 0 ? (r_in < b.capacity ? e * b.capacity + r_in : -1) : pos;
+  const int32_t m = b.capacity > 0 ? (r_in < b.capacity ? e * b.capacity + r_in : -1) : pos;
+  b.expanded_row_idx[f] = m;
+  return m;
 }
 
 // Sorted positions at and past the in-range total hold no id: -1.
@@ -284,7 +285,8 @@ constexpr int kRouteSmallThreads = 1024;
 
 __device__ __forceinline__ void route_small_body(const int32_t* __restrict__ ids, int64_t n,
                                                  int E, int nbits, const RouteBuffers& b,
-                                                 int32_t* lds, uint64_t* sh, int* carry) {
+                                                 int32_t* lds, uint64_t* sh, int* carry,
+                                                 int32_t* map_lds = nullptr) {
   constexpr int nw = kRouteThreads / kWave;            // ranking waves
   int32_t* wave_hist = lds;
   int32_t* off_sh = lds + nw * E;
@@ -322,7 +324,8 @@ __device__ __forceinline__ void route_small_body(const int32_t* __restrict__ ids
     fill_tail(b, f, n, total);
     const int e = key[r];
     if (e < 0) continue;
-    place_id(b, e, f, off_sh[e], wave_hist[w * E + e] + rank[r]);
+    const int32_t m = place_id(b, e, f, off_sh[e], wave_hist[w * E + e] + rank[r]);
+    if (map_lds) map_lds[f] = m;
   }
 }
 
@@ -350,6 +353,105 @@ __global__ __launch_bounds__(kRouteSmallThreads) void quantize_route_small_kerne
   if (blk < qa.nblocks)
     quantize_nvfp4_block(qa.src, blk, qa.blocks_per_row, qa.rows_per_group, qa.q, qa.codes,
                          qa.scales, qa.decoded);
+}
+
+// Routing primitive on a few tokens (the page's case of small shapes: loading, sorting
+// and moving in one kernel): the single-workgroup router, which also keeps every id's
+// row-map entry in LDS, then the token rows moved by the same workgroup, one token at a
+// time, each row held in registers (up to kFusedCache 16-byte vectors per thread).
+constexpr int kFusedMaxTokens = 8;
+constexpr int kFusedCache = 8;
+
+__global__ __launch_bounds__(kRouteSmallThreads) void route_permute_small_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b,
+    PermuteArgs p) {
+  extern __shared__ int32_t lds[];
+  __shared__ uint64_t sh[16];
+  __shared__ int carry[3];
+  __shared__ float red[kRouteSmallThreads / kWave];
+  __shared__ int32_t dst[64];
+  int32_t* map = lds + (kRouteThreads / kWave + 1) * E;
+  for (int f = threadIdx.x; f < n; f += blockDim.x) map[f] = -1;   // ordered by the body's barrier
+  route_small_body(ids, n, E, nbits, b, lds, sh, carry, map);
+  __syncthreads();
+  const int nvec = p.H / 8;
+  const float s_st = p.quant == 2 ? p.static_scale[0] : 0.0f;
+  const float o_st = p.quant == 2 ? p.static_offset[0] : 0.0f;
+  for (int t = 0; t < p.N; ++t) {
+    if (threadIdx.x < p.K) {
+      const int32_t d = map[t * p.K + threadIdx.x];
+      dst[threadIdx.x] = (d >= 0 && d < p.limit) ? d : -1;
+    }
+    __syncthreads();
+    bool any = false;
+    for (int j = 0; j < p.K; ++j) any |= dst[j] >= 0;
+    if (any) {                                           // uniform over the workgroup
+      const uint4* xr = reinterpret_cast<const uint4*>(p.x + static_cast<int64_t>(t) * p.H);
+      uint4 r[kFusedCache];
+#pragma unroll
+      for (int i = 0; i < kFusedCache; ++i) {
+        const int v = threadIdx.x + i * kRouteSmallThreads;
+        r[i] = v < nvec ? xr[v] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      float scale = 0.0f;
+      if (p.quant == 1) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kFusedCache; ++i) {
+          const uint32_t w4[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(w4[q] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w4[q] & 0xFFFF0000u)));
+          }
+        }
+        scale = block_max(amax, red) / 127.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kFusedCache; ++i) {
+        const int v = threadIdx.x + i * kRouteSmallThreads;
+        if (v >= nvec) continue;
+        if (p.quant == 0) {
+          for (int j = 0; j < p.K; ++j)
+            if (dst[j] >= 0)
+              reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.expanded_x) +
+                                       static_cast<int64_t>(dst[j]) * p.H)[v] = r[i];
+          continue;
+        }
+        const uint2 pv =
+            p.quant == 2 ? quant8(r[i], [=](float xv) { return static_int8(xv, s_st, o_st); })
+                         : quant8(r[i], [=](float xv) {
+                             const float qf = (scale == 0.0f) ? 0.0f : rintf(xv / scale);
+                             return fminf(fmaxf(qf, -127.0f), 127.0f);
+                           });
+        for (int j = 0; j < p.K; ++j)
+          if (dst[j] >= 0)
+            reinterpret_cast<uint2*>(static_cast<int8_t*>(p.expanded_x) +
+                                     static_cast<int64_t>(dst[j]) * p.H)[v] = pv;
+      }
+      if (threadIdx.x < p.K && dst[threadIdx.x] >= 0 && p.expanded_scale) {
+        if (p.quant == 1) p.expanded_scale[dst[threadIdx.x]] = scale;
+        else if (p.quant == 0 && p.row_scale) p.expanded_scale[dst[threadIdx.x]] = p.row_scale[t];
+      }
+    }
+    __syncthreads();                                     // dst[] and red[] are reused
+  }
+}
+
+bool route_permute_fits_one_workgroup(int64_t n, int E, int64_t N, int H) {
+  const size_t lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t) +
+                     static_cast<size_t>(n) * sizeof(int32_t);
+  return route_tiles(n) == 1 && lds <= kRouteSmallMaxLds && N <= kFusedMaxTokens &&
+         H / 8 <= kFusedCache * kRouteSmallThreads;
+}
+
+hipError_t launch_route_permute_small(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
+                                      const PermuteArgs& p, hipStream_t stream) {
+  const size_t lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t) +
+                     static_cast<size_t>(n) * sizeof(int32_t);
+  route_permute_small_kernel<<<dim3(1), dim3(kRouteSmallThreads), lds, stream>>>(
+      ids, n, E, bits_for(E), b, p);
+  return hipGetLastError();
 }
 
 bool route_fits_one_workgroup(int64_t n, int E) {

@@ -161,6 +161,13 @@ V2_CASES = [
      dict(quant_mode=0, expert_start=2, expert_end=9), False),
     ("bf16_two_chunks_droppad", 30, 2, 4, 9000, 0.0,
      dict(drop_pad_mode=1, expert_capacity=5, quant_mode=-1), False),
+    # at most 8 tokens: routing and movement in one workgroup
+    ("few_tokens_dynamic_long_rows", 3, 8, 256, 16392, 0.0,
+     dict(quant_mode=1, expert_tokens_num_type=2), False),
+    ("few_tokens_droppad_static", 8, 8, 64, 136, 1.0,
+     dict(drop_pad_mode=1, expert_capacity=2, quant_mode=0), False),
+    ("few_tokens_range_scatter_row_scale", 5, 4, 16, 72, 0.0,
+     dict(quant_mode=-1, expert_start=3, expert_end=11, row_idx_type=1, active_num=9), True),
 ]
 
 
