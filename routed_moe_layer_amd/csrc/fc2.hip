@@ -49,9 +49,19 @@ __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int l
 // over the LDS-resident token tile and, after a slab's last chunk, stores the slab's BF16
 // rows.  Two slabs per loop trip keep the chunk index, the register set and the epilogue
 // compile-time; a slab's first K-step starts from a zero accumulator.
+// The output of one wave for one 16-token block and one slab, 16 rows x 16*WRG columns of
+// BF16, passes through a per-wave LDS buffer (rows padded by 8 elements) so that the
+// global stores are whole 16-byte pieces of consecutive columns: one store instruction
+// then covers 64/(2*WRG) token rows with 32*WRG contiguous bytes each, instead of 16 rows
+// with 32 bytes each in the MFMA output layout (the rows are scattered over the FC2
+// output, so fewer, longer runs per instruction cut the memory transactions 4x at WRG 4).
+template <int WRG>
+constexpr int fc2_out_stride() { return 16 * WRG + 8; }
+
 template <int NW, int WRG, int BN, int NCBA, int NCH>
 __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
-                                         int nslabs, const _Float16* __restrict__ s_tok) {
+                                         int nslabs, const _Float16* __restrict__ s_tok,
+                                         uint16_t* __restrict__ s_out) {
   constexpr int kSlabGroups = NW * WRG;                 // 16-row groups per slab
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int e = td.expert;
@@ -59,13 +69,14 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   const float al = a.alpha2[e];
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
   // FC2 rows are stored at their flat id t*k + j, so that the finalization reads each
-  // token's k rows as one contiguous run
-  uint16_t* orow_cb[NCBA];
+  // token's k rows as one contiguous run; lane l holds the flat id of block row l % 16
+  int32_t flat_cb[NCBA];
 #pragma unroll
   for (int cb = 0; cb < NCBA; ++cb) {
     const int n = min(cb * 16 + (lane & 15), td.nrows - 1);
-    orow_cb[cb] = a.o_rows + static_cast<int64_t>(a.sorted_row_idx[td.row_start + n]) * a.H + 4 * g;
+    flat_cb[cb] = a.sorted_row_idx[td.row_start + n];
   }
+  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
   f32x4 acc[WRG][NCBA];
 
   auto decode = [&](const W2Regs<WRG>& cur, const int s, f16x8 (&wf)[WRG]) {
@@ -117,20 +128,31 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
     }
     if (c == NCH - 1) {
       const int G0 = j * kSlabGroups + w * WRG;
+      constexpr int kStride = fc2_out_stride<WRG>();
+      constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
+      constexpr int kRowsPerPass = 64 / kPieces;
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const int n = cb * 16 + (lane & 15);
-        if (n < td.nrows) {
-          uint16_t* orow = orow_cb[cb];
+        // the MFMA layout (4 columns 16r + 4g.. of block row lane % 16) into LDS
 #pragma unroll
-          for (int r = 0; r < WRG; ++r) {
-            const f32x4 o = acc[r][cb];
-            uint2 v;
-            v.x = pack_bf16x2(o[0] * al, o[1] * al);
-            v.y = pack_bf16x2(o[2] * al, o[3] * al);
-            *reinterpret_cast<uint2*>(orow + 16 * (G0 + r)) = v;
-          }
+        for (int r = 0; r < WRG; ++r) {
+          const f32x4 o = acc[r][cb];
+          u32x2 v;
+          v[0] = pack_bf16x2(o[0] * al, o[1] * al);
+          v[1] = pack_bf16x2(o[2] * al, o[3] * al);
+          *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
         }
+        __builtin_amdgcn_wave_barrier();
+        // back as whole pieces of rows (the wave's LDS operations complete in order)
+#pragma unroll
+        for (int pass = 0; pass < 16 / kRowsPerPass; ++pass) {
+          const int row = pass * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
+          const u32x4 q = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
+          const int64_t flat = __shfl(flat_cb[cb], row);
+          if (cb * 16 + row < td.nrows)
+            *reinterpret_cast<u32x4*>(a.o_rows + flat * a.H + 16 * G0 + 8 * piece) = q;
+        }
+        __builtin_amdgcn_wave_barrier();
       }
       // the next slab's MFMAs (fresh accumulators) stay after these stores, so the two
       // accumulator sets are never live together
@@ -159,6 +181,7 @@ template <int NW, int WRG, int BN, int SPW, int SPLIT>
 __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   __shared__ _Float16 s_tok[BN * kFc2LdsRow];
   __shared__ int64_t s_row[BN];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * fc2_out_stride<WRG>()];
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
   const int ntiles = a.num_tiles[big];
   const int n_slabs = a.H / (NW * WRG * 16);
@@ -194,9 +217,9 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   auto run = [&](auto ncba) {
     constexpr int NCBA = decltype(ncba)::value;
     switch (a.Ip / kChunk) {
-      case 1: fc2_tile<NW, WRG, BN, NCBA, 1>(a, td, slab0, nslabs, s_tok); break;
-      case 2: fc2_tile<NW, WRG, BN, NCBA, 2>(a, td, slab0, nslabs, s_tok); break;
-      default: fc2_tile<NW, WRG, BN, NCBA, 3>(a, td, slab0, nslabs, s_tok); break;
+      case 1: fc2_tile<NW, WRG, BN, NCBA, 1>(a, td, slab0, nslabs, s_tok, s_out); break;
+      case 2: fc2_tile<NW, WRG, BN, NCBA, 2>(a, td, slab0, nslabs, s_tok, s_out); break;
+      default: fc2_tile<NW, WRG, BN, NCBA, 3>(a, td, slab0, nslabs, s_tok, s_out); break;
     }
   };
   using std::integral_constant;
