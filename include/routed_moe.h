@@ -243,8 +243,10 @@ moe_status_t moe_forward(moe_dims_t d, int32_t T, const uint16_t* x, const int32
  * handles created by the caller; event i is recorded on `stream` at the start of stage i
  * and event MOE_FORWARD_STAGES after the last stage.  The stages are, in order: 0 NVFP4
  * quantization of x, 1 routing (histogram, scan, scatter), 2 FC1 + SiTU + requantization,
- * 3 FC2, 4 finalization.  The caller reads the stage durations with hipEventElapsedTime
- * once the events have completed.  NULL events -> MOE_ERR_INVALID_ARG. */
+ * 3 FC2, 4 finalization.  With at most 1024 routed rows (T*k) and E <= 3276 the
+ * quantization and the routing run as one launch; events 1 and 2 are then both recorded
+ * after it, so stage 0 holds both and stage 1 is empty.  The caller reads the stage durations with
+ * hipEventElapsedTime once the events have completed.  NULL events -> MOE_ERR_INVALID_ARG. */
 #define MOE_FORWARD_STAGES 5
 moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
                                const int32_t* expert_ids, const uint16_t* route_weights,
