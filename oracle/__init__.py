@@ -28,6 +28,7 @@ from .nvfp4 import quantize_nvfp4, dequantize_nvfp4, pack_nibbles, unpack_nibble
 from .calib import (global_scale_from_amax, calibrate_layer, calibrate_tokens,
                     calibrate_weights, quantize_expert_stack)
 from .routing import route, route_int8, route_v2, int8_static_quant
+from .router import topk_softmax
 from .layer import (situ, fc_exact, layer_forward, layer_forward_dense, token_forward,
                     calibrate_intermediate, intermediate_amax,
                     expert_weights_decoded)
@@ -39,7 +40,7 @@ __all__ = [
     "global_scale_from_amax", "calibrate_layer", "calibrate_tokens", "calibrate_weights",
     "quantize_expert_stack",
     "calibrate_intermediate", "intermediate_amax",
-    "route", "route_int8", "route_v2", "int8_static_quant",
+    "route", "route_int8", "route_v2", "int8_static_quant", "topk_softmax",
     "situ", "fc_exact", "layer_forward", "layer_forward_dense", "token_forward",
     "expert_weights_decoded",
 ]
