@@ -371,6 +371,24 @@ def route_options_workload(case, cfg, torch, rm, steps, warmup, events):
             "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
 
 
+def topk_workload(T, E, k, torch, rm, steps, warmup, events):
+    """Time moe_topk_softmax (router logits -> the layer's expert ids and route weights).
+    Algorithmic bytes: the f32 logits read once, the ids and BF16 weights written once."""
+    rng = np.random.default_rng(T + E)
+    z = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.int16, device="cuda")
+
+    def call():
+        rm.moe_topk_softmax(T, E, k, z, ids, w)
+
+    gpu_ms, wall_ms = _time_calls(call, torch, steps, warmup, events)
+    nbytes = T * E * 4 + T * k * 6
+    return {"workload": f"topk_softmax_T{T}_E{E}_k{k}", "us_per_call": gpu_ms * 1e3,
+            "wall_us_per_call": wall_ms * 1e3, "algorithmic_bytes": float(nbytes),
+            "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
+
+
 def cpu_baseline(cfg, keep, torch, n_tokens):
     """The oracle, as it stands, on a bounded sample of the same workload's tokens."""
     import oracle
@@ -682,6 +700,12 @@ def main():
         route_res = route_workload(ROUTE_8K, torch, rm, args.steps, args.warmup, events)
         log(f"  {route_res['routed_rows_per_s']:.3e} routed rows/s, {route_res['ms_per_call']:.3f} ms, "
             f"{100 * route_res['hbm_frac']:.1f}% of HBM peak")
+        route_res["topk"] = {}
+        for T in (16384, 16):
+            r = topk_workload(T, 896, 16, torch, rm, args.steps, args.warmup, events)
+            route_res["topk"][f"T{T}"] = r
+            log(f"  {r['workload']}: {r['us_per_call']:.1f} us/call, "
+                f"{100 * r['hbm_frac']:.1f}% of HBM peak")
         route_res["options"] = {}
         for case in ROUTE_OPTION_CASES:
             r = route_options_workload(case, ROUTE_8K, torch, rm, args.steps, args.warmup,

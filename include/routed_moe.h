@@ -257,6 +257,22 @@ moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
                                void* const* events);
 
 /* ------------------------------------------------------------------------------------
+ * The step before the layer: top-k expert selection with softmax route weights.  The
+ * layer takes expert ids and BF16 route weights as given ("Cake SiTU backend", intro);
+ * the pages do not define the gate that makes the router logits, so they are an input:
+ *   expert_ids[t, 0..k-1] = the k largest logits of token t in decreasing order (equal
+ *       logits in increasing expert id);
+ *   route_weights[t, j] = BF16(exp(l_j - l_0) / sum_i exp(l_i - l_0)) over those k logits
+ *       (fp32 arithmetic, round to nearest even).
+ * Buffers (device): logits f32 [T, num_experts] (finite values), expert_ids i32 [T, k],
+ * route_weights BF16 [T, k] -- the layout moe_forward takes.  Limits: 1 <= T,
+ * 1 <= num_experts <= 4096, 1 <= top_k <= min(num_experts, 64).
+ * ------------------------------------------------------------------------------------ */
+moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
+                              const float* logits, int32_t* expert_ids, uint16_t* route_weights,
+                              moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Chunk-streamed front end, one rank ("[RFC] Chunk-ready symmetric-buffer protocol for
  * streaming MegaMoE inputs": sections "Fixed-capacity ring", "Independent readiness
  * generations", "Memory ordering", "Chunk-aware dispatch scheduling" option 1 --

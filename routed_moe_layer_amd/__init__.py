@@ -17,7 +17,8 @@ __all__ = [
     "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_route_v2",
     "MoeRouteOptions", "moe_forward", "moe_forward_timed", "MOE_FORWARD_STAGES",
     "MoeRing", "make_ring", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
-    "moe_ring_publish", "moe_forward_streamed", "MOE_RING_ROUTE", "MOE_RING_LAYOUT",
+    "moe_ring_publish", "moe_forward_streamed", "moe_topk_softmax", "MOE_RING_ROUTE",
+    "MOE_RING_LAYOUT",
     "MOE_RING_OK", "MOE_RING_CONSUMER_TIMEOUT", "MOE_RING_PRODUCER_TIMEOUT",
     "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
 ]
@@ -35,7 +36,7 @@ EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_siz
             "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
             "moe_prepare_weights", "moe_route", "moe_route_v2", "moe_forward",
             "moe_forward_timed", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
-            "moe_ring_publish", "moe_forward_streamed")
+            "moe_ring_publish", "moe_forward_streamed", "moe_topk_softmax")
 
 MOE_RING_ROUTE = 0
 MOE_RING_LAYOUT = 1
@@ -116,6 +117,7 @@ def _lib():
             "moe_forward_timed": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P,
                                        ctypes.POINTER(P)]),
             "moe_ring_layout": (st, [MoeDims, I32, I32, ctypes.POINTER(_RingLayout)]),
+            "moe_topk_softmax": (st, [I32, I32, I32, P, P, P, P]),
             "moe_ring_init": (st, [MoeDims, ctypes.POINTER(MoeRing), P]),
             "moe_ring_acquire": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, ctypes.c_int,
                                       ctypes.c_uint32, P]),
@@ -287,3 +289,9 @@ def moe_forward_streamed(dims, ring, total_tokens, first_chunk, num_chunks, prep
         dims, ctypes.byref(ring), total_tokens, first_chunk, num_chunks, _ptr(prepared), _ptr(qx),
         _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
         timeout_us, _ptr(workspace), nb, _ptr(out), _stream(stream)))
+
+
+def moe_topk_softmax(T, num_experts, top_k, logits, expert_ids, route_weights, stream=None):
+    _check("moe_topk_softmax", _lib().moe_topk_softmax(
+        T, num_experts, top_k, _ptr(logits), _ptr(expert_ids), _ptr(route_weights),
+        _stream(stream)))

@@ -541,4 +541,16 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring, int32_t 
   return MOE_OK;
 }
 
+moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
+                              const float* logits, int32_t* expert_ids, uint16_t* route_weights,
+                              moe_stream_t stream) {
+  if (T < 1 || num_experts < 1 || top_k < 1 || top_k > num_experts) return MOE_ERR_INVALID_ARG;
+  if (num_experts > 4096 || top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (!logits || !expert_ids || !route_weights) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(expert_ids, 4) || !aligned(route_weights, 2))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_topk_softmax(logits, T, num_experts, top_k, expert_ids, route_weights,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -132,6 +132,11 @@ hipError_t launch_ring_wait(const uint32_t* a, const uint32_t* b, const uint32_t
                             hipStream_t stream);
 hipError_t launch_ring_publish(uint32_t* gen, uint32_t* seq, hipStream_t stream);
 
+// Top-k expert selection with softmax weights over the picks (topk.hip): logits f32
+// [T, E] (E <= 4096), k <= 64 -> ids i32 [T, k], BF16 weights [T, k].
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                               uint16_t* weights, hipStream_t stream);
+
 hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
                                   const uint8_t* w13_sf, const uint8_t* w2,
                                   const uint8_t* w2_sf, uint8_t* prepared, hipStream_t stream);

@@ -160,6 +160,19 @@ def test_route_workspace_holds_the_position_map():
     assert rm.moe_route_workspace_size(8192, 8, 256) >= (n // 1024) * 256 * 4 + 257 * 4 + 4 * n
 
 
+def test_topk_softmax_validation():
+    base = dict(T=16, num_experts=896, top_k=16, logits=4096, expert_ids=8192,
+                route_weights=16384, stream=0)
+    for kw, code in ((dict(T=0), -1), (dict(top_k=0), -1), (dict(top_k=897), -1),
+                     (dict(num_experts=5000, top_k=8), -2), (dict(top_k=65, num_experts=100), -2),
+                     (dict(logits=None), -1), (dict(logits=4098), -1),
+                     (dict(route_weights=16385), -1)):
+        a = dict(base); a.update(kw)
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_topk_softmax(**a)
+        assert ei.value.status == code, kw
+
+
 def test_quantize_validation():
     for kw in (dict(K=24), dict(src=None), dict(src=4098), dict(groups=0)):
         a = dict(src=4096, groups=1, rows_per_group=4, K=256, q=256, codes=8192, scales=16384,
