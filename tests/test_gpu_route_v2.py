@@ -267,3 +267,45 @@ def test_route_v2_drop_pad_kv_many_ids():
     got = run_v2(x, ids, E, opts)
     want = oracle_v2(x, ids, E, opts)
     check_v2(got, want, opts)
+
+
+def test_route_v2_graph_capture_replay():
+    """moe_route_v2 (drop/pad with its zero-fill launch, key_value histogram, dynamic int8)
+    captured into a graph and replayed with eager work between the replays; every replay
+    must equal the eager call."""
+    _say("route_v2 graph capture/replay")
+    N, K, E, H = 300, 8, 64, 136
+    ids = draw_expert_ids(N, E, K, seed_index=2200, zipf_s=1.1)
+    x = draw_tokens(N, H, seed_index=2200)
+    opts = rm.MoeRouteOptions(drop_pad_mode=1, expert_capacity=40, quant_mode=1,
+                              expert_tokens_num_type=2)
+    xd, idd = dev(x), dev(ids)
+    rows = E * 40
+    ex = torch.zeros((rows, H), dtype=torch.int8, device="cuda")
+    eri = torch.zeros(N * K, dtype=torch.int32, device="cuda")
+    tok = torch.zeros((E, 2), dtype=torch.int32, device="cuda")
+    esc = torch.zeros(rows, dtype=torch.float32, device="cuda")
+    ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
+
+    def call(stream=None):
+        rm.moe_route_v2(N, H, E, K, xd, idd, opts, ex, eri, expert_tokens=tok,
+                        expanded_scale=esc, workspace=ws, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    want = [host(t).copy() for t in (ex, eri, tok, esc)]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(stream=s)
+    for rep in range(4):
+        for t in (ex, eri, tok, esc):
+            t.fill_(-1 if t.dtype != torch.float32 else float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in (ex, eri, tok, esc)]
+        for a, b in zip(got, want):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {rep}"
+        call()                                          # eager work between replays
+        torch.cuda.synchronize()

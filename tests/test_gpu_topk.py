@@ -74,3 +74,27 @@ def test_topk_feeds_the_layer_layout():
     assert all(len(set(r)) == 16 for r in ids.tolist())
     wf = oracle.bf16_bits_to_f32(w).astype(np.float64)
     assert np.all(np.abs(wf.sum(1) - 1) <= 16 * 2.0 ** -9)
+
+
+def test_topk_graph_capture_replay():
+    _say("topk graph capture/replay")
+    rng = np.random.default_rng(12)
+    z = dev(rng.standard_normal((64, 896)).astype(np.float32))
+    ids = torch.zeros((64, 16), dtype=torch.int32, device="cuda")
+    w = torch.zeros((64, 16), dtype=torch.int16, device="cuda")
+    rm.moe_topk_softmax(64, 896, 16, z, ids, w)
+    torch.cuda.synchronize()
+    want_i, want_w = host(ids).copy(), host(w).copy()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rm.moe_topk_softmax(64, 896, 16, z, ids, w, stream=s)
+    for rep in range(3):
+        ids.fill_(-1)
+        w.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ids), want_i) and np.array_equal(host(w), want_w), rep
+        rm.moe_topk_softmax(64, 896, 16, z, ids, w)
+        torch.cuda.synchronize()
