@@ -220,11 +220,11 @@ STREAM_CASES = {"prefill": (4096, 2), "mid": (256, 2)}
 
 
 def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmup, events):
-    """Time the streamed layer on a layer workload's inputs: per step, the consumer
-    (moe_forward_streamed over every chunk) is enqueued on the launch stream and a
-    producer on a second stream fills a `slots`-slot ring chunk by chunk (copies of the
-    resident ids, route weights and x into the slot, each part acquired and published),
-    so production overlaps the layer's work on earlier chunks."""
+    """Time the streamed layer on a layer workload's inputs: per step, a producer on a
+    second stream fills a `slots`-slot ring chunk by chunk (copies of the resident ids,
+    route weights and x into the slot, each part acquired and published) and the
+    consumer (moe_forward_streamed, one chunk per call) runs on the launch stream, so
+    production overlaps the layer's work on earlier chunks."""
     E, H, I, k, T = cfg.E, cfg.H, cfg.I, cfg.k, cfg.T
     dims = rm.MoeDims(H, I, E, k)
     x, rw = keep["x"], keep["rw"]
@@ -243,11 +243,12 @@ def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmu
     torch.cuda.synchronize()
 
     def step():
-        rm.moe_forward_streamed(dims, ring, T, 0, n, prepared, keep["qx"], keep["alpha1"],
-                                keep["qa"], keep["alpha2"], keep["beta"], keep["lam"], ws, out)
-        with torch.cuda.stream(prod):
-            for i in range(n):
-                sl, lo, hi = i % slots, i * chunk, min(T, (i + 1) * chunk)
+        # chunk by chunk: produce chunk i on the producer stream, then consume it on the
+        # launch stream; every wait needs only publishes enqueued before it, so the step
+        # is valid whether or not the runtime gives the two streams separate queues
+        for i in range(n):
+            sl, lo, hi = i % slots, i * chunk, min(T, (i + 1) * chunk)
+            with torch.cuda.stream(prod):
                 rm.moe_ring_acquire(dims, ring, sl, rm.MOE_RING_ROUTE, stream=prod)
                 rids[sl, :hi - lo].copy_(ids[lo:hi])
                 rrw[sl, :hi - lo].copy_(rw[lo:hi])
@@ -255,6 +256,9 @@ def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmu
                 rm.moe_ring_acquire(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
                 rx[sl, :hi - lo].copy_(x[lo:hi])
                 rm.moe_ring_publish(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
+            rm.moe_forward_streamed(dims, ring, T, i, 1, prepared, keep["qx"], keep["alpha1"],
+                                    keep["qa"], keep["alpha2"], keep["beta"], keep["lam"], ws,
+                                    out)
 
     gpu_ms, wall_ms = _time_calls(step, torch, steps, warmup, events)
     torch.cuda.synchronize()

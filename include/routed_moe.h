@@ -298,11 +298,14 @@ moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
  * Progress: every wait is a one-workgroup kernel bounded by timeout_us (0 = 1 s).  When
  * a wait expires it records MOE_RING_CONSUMER_TIMEOUT or MOE_RING_PRODUCER_TIMEOUT in the
  * ring's status word (the first failure is kept) and returns; the work after it then runs
- * on whatever the slot holds, and the ring must be re-initialized.  Serialized execution
- * is valid whenever every publish a wait needs is enqueued before that wait on the same
- * stream (for example all chunks produced into a ring of at least as many slots, then
- * consumed; or produce/consume alternating per chunk).  Producer and consumer on
- * different streams overlap.
+ * on whatever the slot holds, and the ring must be re-initialized.  The rule for progress:
+ * enqueue every publish before the waits that need it (in host enqueue order, across
+ * streams), for example all chunks produced into a ring of at least as many slots and
+ * then consumed, or produce and consume alternating per chunk.  Then any placement of the
+ * streams works: streams on different hardware queues overlap, and streams the runtime
+ * puts on one hardware queue run in enqueue order.  A wait enqueued before a publish it
+ * needs can make progress only if the runtime runs the two streams on different hardware
+ * queues; otherwise it expires.
  * ------------------------------------------------------------------------------------ */
 typedef enum { MOE_RING_ROUTE = 0, MOE_RING_LAYOUT = 1 } moe_ring_role_t;
 

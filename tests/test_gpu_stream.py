@@ -140,17 +140,39 @@ def test_streamed_one_slot_alternating(layer):
 
 
 def test_streamed_producer_and_consumer_on_two_streams(layer):
-    """The consumer is enqueued first, on its own stream, over all chunks of a two-slot
-    ring; the producer follows on another stream and must wait for slots to be freed."""
+    """Producer and consumer on two streams through a two-slot ring, enqueued chunk by
+    chunk (produce chunk i, then consume chunk i): every wait then needs only publishes
+    enqueued before it, which is valid whether the runtime puts the two streams on
+    different hardware queues (they overlap; the producer's wait for a free slot depends
+    on the consumer's stream) or on one (they run in enqueue order)."""
     _say("streamed two streams")
     p, L, batch = layer
     R = Ring(L, 2, 16)
     n = R.chunks(CFG.T)
     torch.cuda.synchronize()
     cons, prod = torch.cuda.Stream(), torch.cuda.Stream()
-    R.consume(CFG.T, 0, n, stream=cons, timeout_us=10_000_000)
     for i in range(n):
         R.produce(i, CFG.T, stream=prod, timeout_us=10_000_000)
+        R.consume(CFG.T, i, 1, stream=cons, timeout_us=10_000_000)
+    torch.cuda.synchronize()
+    assert R.status() == rm.MOE_RING_OK
+    R.check()
+    assert np.array_equal(host(R.out, np.uint16), batch)
+
+
+def test_streamed_all_chunks_produced_first_on_another_stream(layer):
+    """A ring with a slot per chunk, every chunk produced on one stream and then the
+    whole stream consumed on another: the consumer's waits depend on the other stream's
+    publishes only."""
+    _say("streamed produce-all then consume, two streams")
+    p, L, batch = layer
+    R = Ring(L, 7, 32)
+    n = R.chunks(CFG.T)
+    torch.cuda.synchronize()
+    cons, prod = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(n):
+        R.produce(i, CFG.T, stream=prod, timeout_us=10_000_000)
+    R.consume(CFG.T, 0, n, stream=cons, timeout_us=10_000_000)
     torch.cuda.synchronize()
     assert R.status() == rm.MOE_RING_OK
     R.check()
