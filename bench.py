@@ -528,7 +528,7 @@ def summarize_profiles(src, out_dir):
         line = _bench_line(os.path.join(src, f"trace_{w}.log"))
         rows = _read_csv(stats)
         md = [f"# Kernel trace: routed-MoE layer, {cfg.name}", "",
-              "Command (from the repository root on the GPU box, after "
+              "Command (run from the repository root, after "
               "`cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd_trace.format(w=w), "```", "",
               "Per-kernel statistics (`*_kernel_stats.csv`; all calls of the run: weight "
               "preparation, calibration, warmup and timed steps; `at::` kernels are the "
@@ -610,7 +610,7 @@ def _summarize_routing(src, out_dir, cmd_trace):
             if ln.startswith("{") and '"routing_primitive"' in ln:
                 line = json.loads(ln)["routing_primitive"]
     md = ["# Kernel trace: routing primitive", "",
-          "Command (from the repository root on the GPU box, after "
+          "Command (run from the repository root, after "
           "`cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd_trace.format(w="route"), "```", "",
           "Per-kernel statistics (all calls of the run: moe_route on "
           "route_N8192_H7168_E256_K8_zipf1.1_int8, then the moe_route_v2 cases, each with "
