@@ -671,9 +671,8 @@ def main():
         summarize_profiles(args.summarize, os.path.join(ROOT, "profiles"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
-              "not part of this build (the layer is one TP rank's work; see the design notes "
-              "on sharding).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer (one TP rank's work); the "
+              "library has no multi-GPU path, so --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
