@@ -1,0 +1,56 @@
+/* Plain-C consumer of include/routed_moe.h: compiled with gcc against the header and the
+ * shared library, it calls only host-side entry points (sizes, layouts, status strings)
+ * and argument validation that returns before any HIP call, so it runs without a GPU.
+ * Prints "ok" and exits 0 when every check holds. */
+#include <stdio.h>
+#include <string.h>
+
+#include "routed_moe.h"
+
+static int failures = 0;
+#define CHECK(cond)                                                          \
+  do {                                                                       \
+    if (!(cond)) {                                                           \
+      fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond);     \
+      ++failures;                                                            \
+    }                                                                        \
+  } while (0)
+
+int main(void) {
+  moe_dims_t d = {3584, 384, 896, 16};
+  size_t ws16 = 0, ws16k = 0, prep = 0, route = 0;
+  CHECK(moe_workspace_size(d, 16, &ws16) == MOE_OK);
+  CHECK(moe_workspace_size(d, MOE_MAX_TOKENS, &ws16k) == MOE_OK);
+  CHECK(ws16 > 0 && ws16 <= ws16k);
+  CHECK(moe_prepared_weights_size(d, &prep) == MOE_OK);
+  /* FC1 codes + scales and FC2 codes + scales of 896 experts */
+  CHECK(prep == (size_t)896 * (768 * 1792 + 768 * 224 + 3584 * 192 + 3584 * 24));
+  moe_workspace_layout_t lay;
+  CHECK(moe_workspace_layout(d, 16, &lay) == MOE_OK);
+  CHECK(lay.total == ws16 && lay.x_codes < lay.total && lay.o_rows < lay.total);
+  CHECK(moe_route_workspace_size(8192, 8, 256, &route) == MOE_OK && route > 0);
+  moe_ring_layout_t rl;
+  CHECK(moe_ring_layout(d, 2, 64, &rl) == MOE_OK && rl.total > rl.counters);
+
+  /* validation errors come back as codes, before any device work */
+  moe_dims_t bad = {3584, 384, 896, 0};
+  CHECK(moe_workspace_size(bad, 16, &ws16) == MOE_ERR_INVALID_ARG);
+  moe_dims_t odd = {3500, 384, 896, 16};
+  CHECK(moe_workspace_size(odd, 16, &ws16) == MOE_ERR_UNSUPPORTED);
+  CHECK(moe_forward(d, 16, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                    0, NULL, 0) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_topk_softmax(16, 896, 17 * 60, (const float*)0x1000, (int32_t*)0x2000,
+                         (uint16_t*)0x3000, 0) == MOE_ERR_INVALID_ARG);
+  moe_route_options_t o;
+  memset(&o, 0, sizeof(o));
+  o.quant_mode = 5;
+  CHECK(moe_route_v2(64, 256, 32, 8, (const uint16_t*)0x1000, (const int32_t*)0x2000, NULL, NULL,
+                     &o, (void*)0x3000, (int32_t*)0x4000, NULL, NULL, NULL, (void*)0x5000,
+                     route, 0) == MOE_ERR_INVALID_ARG);
+  CHECK(strcmp(moe_status_string(MOE_OK), "ok") == 0);
+  CHECK(moe_status_string((moe_status_t)12345) != NULL);
+
+  if (failures) return 1;
+  printf("ok\n");
+  return 0;
+}

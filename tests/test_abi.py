@@ -188,3 +188,22 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(rm, "library_path", "/nonexistent/libroutedmoe.so")
     with pytest.raises(RuntimeError, match="not built"):
         rm.moe_workspace_size(FULL, 16)
+
+
+def test_plain_c_program_uses_the_abi(tmp_path):
+    """A C program compiled with gcc against include/routed_moe.h and linked to the shared
+    library calls the host-side entry points and the validation paths."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(__file__))
+    libdir = os.path.dirname(rm.library_path)
+    exe = tmp_path / "abi_check"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c", "abi_check.c"), "-L", libdir,
+                    "-lroutedmoe", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok"
