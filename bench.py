@@ -626,10 +626,11 @@ def _summarize_routing(src, out_dir, cmd_trace):
         # library's kernels in dispatch order.
         kern = [r for r in _read_csv(trace) if "rmoe::route" in r["Kernel_Name"]]
         kern.sort(key=lambda r: int(r["Start_Timestamp"]))
-        # one library call starts with the histogram (or the fused small router) launch
+        # one library call starts with the histogram launch, or is one fused small kernel
+        starts = ("route_hist", "route_small", "route_permute_small", "quantize_route_small")
         calls = []
         for r in kern:
-            if not calls or _short(r["Kernel_Name"]).startswith(("route_hist", "route_small")):
+            if not calls or _short(r["Kernel_Name"]).startswith(starts):
                 calls.append([])
             calls[-1].append(r)
         cases = [("moe_route", line)] + [(c, r) for c, r in line.get("options", {}).items()]
