@@ -367,6 +367,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   a.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
   a.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   a.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  a.expert_offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   a.max_small = max_small_tiles(R, E);
   a.max_big = max_big_tiles(R, E);
   const uint8_t* p = static_cast<const uint8_t*>(prepared);

@@ -106,11 +106,13 @@ __device__ __forceinline__ uint32_t pack8_codes(const float* v, float enc) {
 // a power-of-two scale, so it runs with scale 1 (exact E2M1 values) and the E4M3 scale
 // (at most 4 significant bits, range 2^-9..448) multiplies in f16: every product has at
 // most 6 significant bits and lies in [2^-10, 2688], so it is exact in f16.
-__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 scale2) {
-  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+// `one` is the conversion's scale operand: any value in [1, 2) gives the same result (only
+// its power of two is applied); a loop-variant one keeps a decode inside its loop.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 scale2, float one = 1.0f) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, one, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, one, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, one, 2);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, one, 3);
   a *= scale2; b *= scale2; c *= scale2; d *= scale2;
   f16x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
@@ -121,6 +123,22 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 scale2) {
 __device__ __forceinline__ f16x2 scale_f16x2(uint32_t e4m3_byte) {
   _Float16 h = static_cast<_Float16>(e4m3_to_f32(e4m3_byte));   // exact: E4M3 fits f16
   f16x2 r; r[0] = h; r[1] = h;
+  return r;
+}
+
+// The four E4M3 scale bytes of one dword as f16 (exact; sign bits ignored like
+// e4m3_to_f32): lo = {byte 0, byte 1}, hi = {byte 2, byte 3}.
+__device__ __forceinline__ void scales4_f16(uint32_t w, f16x2* lo, f16x2* hi) {
+  const uint32_t m = w & 0x7F7F7F7Fu;
+  *lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m, 1.0f, false);
+  *hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m, 1.0f, true);
+}
+
+// Element i of a scale pair in both halves.
+__device__ __forceinline__ f16x2 bcast_f16x2(f16x2 pair, int i) {
+  f16x2 r;
+  r[0] = pair[i];
+  r[1] = pair[i];
   return r;
 }
 

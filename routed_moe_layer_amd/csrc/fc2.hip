@@ -247,6 +247,188 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   }
 }
 
+// Weight-stationary FC2 for big tiles when there are many routed rows.
+//
+// One workgroup per (run, slab).  A run is up to NT consecutive big tiles of one expert,
+// i.e. a contiguous range of its sorted rows, and a slab is NW*WRG*16 output columns.  The
+// slab's weight codes and scales for the whole reduction (NCH chunks of 128) stay in
+// registers for the run, and the run's token rows pass through one LDS tile
+// kFc2PassRows at a time: the next pass's codes are loaded into registers while the
+// current pass's MFMAs run, and are decoded into LDS between two barriers.  An expert's
+// weights are thus read once per run rather than once per 64-row sub-tile.  The slabs of a
+// run are consecutive workgroups on one XCD, so the run's token rows are fetched from HBM
+// once and reread by the other slabs from that XCD's L2.
+constexpr int kFc2PassRows = 64;
+constexpr int kFc2RunTiles = 4;
+
+template <int NW, int WRG, int NCH, int NT>
+__global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a) {
+  constexpr int kSlabGroups = NW * WRG;
+  constexpr int kThreads = NW * 64;
+  __shared__ __attribute__((aligned(16))) _Float16 s_tok[kFc2PassRows * kFc2LdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * fc2_out_stride<WRG>()];
+
+  // logical id (tile, slab): the n_slabs slabs of one tile are consecutive on one XCD
+  const int n_slabs = a.H / (kSlabGroups * 16);
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int L = ((slot / n_slabs) * kXcds + xcd) * n_slabs + slot % n_slabs;
+  const int tj = L / n_slabs, slab = L - tj * n_slabs;
+  if (tj >= a.num_tiles[1]) return;
+  const TileDesc td = a.tiles_big[tj];
+  const int e = td.expert;
+  const int e_lo = a.expert_offsets[e], e_hi = a.expert_offsets[e + 1];
+  // The big tiles of one expert all have the same size except the last, so the previous
+  // tile gives the size when this one is the last: a run starts at every NT-th tile.
+  const int tile_rows = (td.row_start + td.nrows >= e_hi && td.row_start > e_lo)
+                            ? a.tiles_big[tj - 1].nrows : td.nrows;
+  if (((td.row_start - e_lo) / tile_rows) % NT != 0) return;
+  const int row_end = min(e_hi, td.row_start + NT * tile_rows);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
+  const int code_bytes = a.I / 2, scale_cols = a.I / 16;
+  W2Regs<WRG> wr[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) fc2_load<NW, WRG>(a, e, w, lane, slab, c, NCH, wr[c]);
+  // the block scales of K-steps (0, 1) and (2, 3) of every chunk and row group, as f16
+  f16x2 wsc[NCH][WRG][2];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
+
+  // Token rows [p0, p0 + nr) of the run (rows past nr repeat the last one; they are not
+  // stored).  Four threads per row, each NCH 16-byte pieces of codes (32 values) and the
+  // two scale bytes of each piece.
+  static_assert(kThreads == 4 * kFc2PassRows, "four threads per staged row");
+  const int st_row = tid >> 2, st_part = (tid & 3) * NCH;   // piece index within the row
+  u32x4 pc[NCH];
+  uint32_t ps[NCH];
+  auto fetch = [&](int p0, int nr) {
+    const int64_t row = p0 + min(st_row, nr - 1);
+    const u32x4* codes = reinterpret_cast<const u32x4*>(a.a_codes + row * code_bytes) + st_part;
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.a_scales + row * scale_cols) + st_part;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      pc[j] = codes[j];
+      ps[j] = scales[j];
+    }
+  };
+  auto stage = [&]() {
+    f16x8* dst = reinterpret_cast<f16x8*>(s_tok + st_row * kFc2LdsRow) + 4 * st_part;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const f16x2 s0 = scale_f16x2(ps[j] & 0xFFu), s1 = scale_f16x2(ps[j] >> 8);
+      dst[4 * j + 0] = decode8(pc[j][0], s0);
+      dst[4 * j + 1] = decode8(pc[j][1], s0);
+      dst[4 * j + 2] = decode8(pc[j][2], s1);
+      dst[4 * j + 3] = decode8(pc[j][3], s1);
+    }
+  };
+
+  const float al = a.alpha2[e];
+  const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
+  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
+  uint16_t* out_cols = a.o_rows + 16 * (slab * kSlabGroups + w * WRG);
+  int32_t flat[kFc2PassRows / 16];
+  int p0 = td.row_start;
+  int nr = min(kFc2PassRows, row_end - p0);
+
+  // One pass over NCB 16-token blocks: all K-steps from the resident weights, then the
+  // BF16 rows (stored at their flat ids, through the per-wave LDS transpose).
+  auto pass = [&](auto ncb_c) {
+    constexpr int NCB = decltype(ncb_c)::value;
+    f32x4 acc[WRG][NCB];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // The decoded weights are the same in every pass: an opaque 1.0 as the conversion's
+        // scale (a scalar register, no vector work) keeps the compiler from hoisting all of
+        // them (NCH*4*WRG*4 registers) out of the pass loop.
+        uint32_t one_bits = 0x3F800000u;
+        asm volatile("" : "+s"(one_bits));
+        const float one = __uint_as_float(one_bits);
+        f16x8 xf[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          xf[cb] = *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
+#pragma unroll
+        for (int r = 0; r < WRG; ++r) {
+          const uint4& cc = wr[c].c[r];
+          const uint32_t cw = s == 0 ? cc.x : s == 1 ? cc.y : s == 2 ? cc.z : cc.w;
+          const f16x8 wf = decode8(cw, bcast_f16x2(wsc[c][r][s >> 1], s & 1), one);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            acc[r][cb] = mfma16x16x32(wf, xf[cb],
+                                      (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bounds the live decoded weights to one K-step
+      }
+    }
+    constexpr int kStride = fc2_out_stride<WRG>();
+    constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
+    constexpr int kRowsPerPass = 64 / kPieces;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int r = 0; r < WRG; ++r) {
+        const f32x4 o = acc[r][cb];
+        u32x2 v;
+        v[0] = pack_bf16x2(o[0] * al, o[1] * al);
+        v[1] = pack_bf16x2(o[2] * al, o[3] * al);
+        *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 16 / kRowsPerPass; ++q) {
+        const int row = q * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
+        const int64_t f = __shfl(flat[cb], row);
+        if (cb * 16 + row < nr)
+          *reinterpret_cast<u32x4*>(out_cols + f * a.H + 8 * piece) = val;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+
+  fetch(p0, nr);
+  stage();
+  __syncthreads();
+  using std::integral_constant;
+  for (;;) {
+    // flat ids of this pass's rows (lane l: block row l % 16), loaded before the next
+    // pass's codes so that waiting for them does not wait for those
+#pragma unroll
+    for (int cb = 0; cb < kFc2PassRows / 16; ++cb)
+      flat[cb] = a.sorted_row_idx[p0 + min(cb * 16 + (lane & 15), nr - 1)];
+    const int next = p0 + kFc2PassRows;
+    const bool more = next < row_end;
+    const int nr_next = more ? min(kFc2PassRows, row_end - next) : 0;
+    if (more) fetch(next, nr_next);
+    switch ((nr + 15) / 16) {
+      case 1: pass(integral_constant<int, 1>{}); break;
+      case 2: pass(integral_constant<int, 2>{}); break;
+      case 3: pass(integral_constant<int, 3>{}); break;
+      default: pass(integral_constant<int, 4>{}); break;
+    }
+    if (!more) break;
+    __syncthreads();
+    stage();
+    __syncthreads();
+    p0 = next;
+    nr = nr_next;
+  }
+}
+
+template <int NW, int WRG, int NCH>
+static void launch_fc2_stationary(const LayerArgs& a, hipStream_t stream) {
+  const int n_slabs = a.H / (NW * WRG * 16);
+  const int64_t grid = round_up(a.max_big, kXcds) * n_slabs;
+  if (grid > 0)
+    fc2_stationary_kernel<NW, WRG, NCH, kFc2RunTiles>
+        <<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a);
+}
+
 template <int NW, int WRG, int BN, int SPW, int SPLIT = 1>
 static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
                                hipStream_t stream) {
@@ -260,7 +442,8 @@ static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
 }
 
 // Small tiles: 128-row slabs in groups of 4 (enough workgroups for decode-size batches);
-// big tiles: 256-row slabs (128 when H is not a multiple of 256), all slabs in one group.
+// big tiles: the weight-stationary kernel on 256-column slabs (H a multiple of 256, I of
+// 128), else the token-resident kernel on 128-column slabs, all slabs in one group.
 bool fc2_resident_fits(const LayerArgs& a) { return a.Ip <= kFc2MaxIp; }
 
 void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
@@ -268,10 +451,15 @@ void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
 }
 
 void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream) {
-  if (a.H % 256 == 0)
-    launch_fc2_variant<4, 4, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
-  else
+  if (a.H % 256 == 0 && a.I == a.Ip) {
+    switch (a.Ip / kChunk) {
+      case 1: launch_fc2_stationary<4, 4, 1>(a, stream); break;
+      case 2: launch_fc2_stationary<4, 4, 2>(a, stream); break;
+      default: launch_fc2_stationary<4, 4, 3>(a, stream); break;
+    }
+  } else {
     launch_fc2_variant<4, 2, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
+  }
 }
 
 }  // namespace rmoe

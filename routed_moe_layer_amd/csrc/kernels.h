@@ -151,6 +151,7 @@ struct LayerArgs {
   const TileDesc* tiles_small;
   const TileDesc* tiles_big;
   const int32_t* num_tiles;    // [2]
+  const int32_t* expert_offsets;   // [E + 1] first sorted row of each expert, then the total
   int64_t max_small, max_big;
   const uint8_t* w13_codes;    // prepared
   const uint8_t* w13_scales;

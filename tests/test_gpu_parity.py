@@ -252,6 +252,10 @@ EDGE = [
     # T*k = 65536 routed rows: FC2 big tiles take the LDS-resident kernel
     ("resident_fc2", _edge("edge_res", T=16384, E=16, k=4, H=256, I=128, seed_index=40),
      None),
+    # 65536 routed rows, Zipf-skewed: the weight-stationary FC2 on two slabs and two
+    # 128-wide chunks, with runs split inside hot experts and ragged last passes
+    ("stationary_fc2_skewed", _edge("edge_stat", T=8192, E=64, k=8, H=512, I=256,
+                                    zipf_s=1.0, seed_index=41), None),
 ]
 
 
