@@ -142,6 +142,15 @@ __device__ __forceinline__ f16x2 bcast_f16x2(f16x2 pair, int i) {
   return r;
 }
 
+// scale_f16x2 of byte b of a dword of E4M3 scales, by one packed conversion of the byte
+// pair that holds it (b is a compile-time constant after unrolling).
+__device__ __forceinline__ f16x2 scale_f16x2_of(uint32_t w, int b) {
+  const uint32_t m = w & 0x7F7F7F7Fu;
+  const f16x2 pair = b >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m, 1.0f, true)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m, 1.0f, false);
+  return bcast_f16x2(pair, b & 1);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -83,7 +83,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
 #pragma unroll
     for (int r = 0; r < WRG; ++r) {
       const uint32_t cw = s == 0 ? cur.c[r].x : s == 1 ? cur.c[r].y : s == 2 ? cur.c[r].z : cur.c[r].w;
-      wf[r] = decode8(cw, scale_f16x2((cur.s[r] >> (8 * s)) & 0xFFu));
+      wf[r] = decode8(cw, scale_f16x2_of(cur.s[r], s));
     }
   };
   auto step = [&](const int j, const int c, W2Regs<WRG>& cur) {
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
     f16x8* dst = reinterpret_cast<f16x8*>(s_tok + st_row * kFc2LdsRow) + 4 * st_part;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const f16x2 s0 = scale_f16x2(ps[j] & 0xFFu), s1 = scale_f16x2(ps[j] >> 8);
+      const f16x2 s0 = scale_f16x2_of(ps[j], 0), s1 = scale_f16x2_of(ps[j], 1);
       dst[4 * j + 0] = decode8(pc[j][0], s0);
       dst[4 * j + 1] = decode8(pc[j][1], s0);
       dst[4 * j + 2] = decode8(pc[j][2], s1);

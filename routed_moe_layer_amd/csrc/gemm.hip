@@ -211,7 +211,7 @@ struct CodeStage {
     _Float16* dst = buf + trow * kLdsRow + part_byte * 2;
 #pragma unroll
     for (int i = 0; i < kNdw; ++i) {
-      const f16x8 v = decode8(R.w[i], scale_f16x2((R.sc >> (8 * (i >> 1))) & 0xFFu));
+      const f16x8 v = decode8(R.w[i], scale_f16x2_of(R.sc, i >> 1));
       *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
     }
   }
