@@ -85,7 +85,7 @@ bool ring_ticks(uint32_t timeout_us, int64_t* ticks) {
 
 struct Layout {
   moe_workspace_layout_t pub;
-  size_t offsets, tile_hist, tiles_small, tiles_big, num_tiles;
+  size_t offsets, tile_hist, tiles_small, tiles_big, runs, num_tiles;
 };
 
 Layout make_layout(const moe_dims_t& d, int64_t T) {
@@ -104,7 +104,8 @@ Layout make_layout(const moe_dims_t& d, int64_t T) {
   L.tile_hist = c.take(static_cast<size_t>(route_tiles(R)) * E * 4);
   L.tiles_small = c.take(static_cast<size_t>(max_small_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
   L.tiles_big = c.take(static_cast<size_t>(max_big_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
-  L.num_tiles = c.take(8);
+  L.runs = c.take(static_cast<size_t>(max_big_tiles(R, static_cast<int>(E))) * sizeof(TileDesc));
+  L.num_tiles = c.take(16);
   L.pub.a_codes = c.take(R * I / 2);
   L.pub.a_scales = c.take(R * I / 16);
   L.pub.o_rows = c.take(R * H * 2);
@@ -367,7 +368,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   a.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
   a.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   a.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
-  a.expert_offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  a.runs = reinterpret_cast<TileDesc*>(ws + L.runs);
   a.max_small = max_small_tiles(R, E);
   a.max_big = max_big_tiles(R, E);
   const uint8_t* p = static_cast<const uint8_t*>(prepared);
@@ -399,6 +400,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   b.expanded_row_idx = expanded_row_idx;
   b.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
   b.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
+  b.runs = reinterpret_cast<TileDesc*>(ws + L.runs);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   b.amax_reset = a.a_amax;
   uint8_t* x_codes = ws + L.pub.x_codes;

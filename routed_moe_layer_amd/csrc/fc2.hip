@@ -249,52 +249,35 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
 
 // Weight-stationary FC2 for big tiles when there are many routed rows.
 //
-// One workgroup per (run, slab).  A run is up to NT consecutive big tiles of one expert,
-// i.e. a contiguous range of its sorted rows, and a slab is NW*WRG*16 output columns.  The
-// slab's weight codes and scales for the whole reduction (NCH chunks of 128) stay in
-// registers for the run, and the run's token rows pass through one LDS tile
-// kFc2PassRows at a time: the next pass's codes are loaded into registers while the
-// current pass's MFMAs run, and are decoded into LDS between two barriers.  An expert's
-// weights are thus read once per run rather than once per 64-row sub-tile.  The slabs of a
-// run are consecutive workgroups on one XCD, so the run's token rows are fetched from HBM
-// once and reread by the other slabs from that XCD's L2.
+// Work items are (run, slab) pairs.  A run is up to kRunTiles consecutive big tiles of one
+// expert (a contiguous range of its sorted rows, listed by the router), and a slab is
+// NW*WRG*16 output columns.  For an item, the slab's weight codes and scales for the whole
+// reduction (NCH chunks of 128) stay in registers, and the run's token rows pass through
+// one LDS tile kFc2PassRows at a time: the next pass's codes are loaded into registers
+// while the current pass's MFMAs run, and are decoded into LDS between two barriers.  An
+// expert's weights are thus read once per run rather than once per 64-row sub-tile.
+// The kernel is persistent (two workgroups per CU, each taking items at a fixed stride), so
+// the grid never holds workgroups with no work; the items of run r go to the workgroups
+// of XCD r % 8, the slabs of one run to consecutive workgroups there, so the run's token
+// rows are fetched from HBM once and reread by the other slabs from that XCD's L2.
 constexpr int kFc2PassRows = 64;
-constexpr int kFc2RunTiles = 4;
+constexpr int kFc2StationaryGrid = 2 * 256;     // two workgroups on each of 256 CUs
 
-template <int NW, int WRG, int NCH, int NT>
+template <int NW, int WRG, int NCH>
 __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a) {
   constexpr int kSlabGroups = NW * WRG;
   constexpr int kThreads = NW * 64;
+  static_assert(kFc2StationaryGrid % kXcds == 0, "whole XCD strides");
   __shared__ __attribute__((aligned(16))) _Float16 s_tok[kFc2PassRows * kFc2LdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * fc2_out_stride<WRG>()];
 
-  // logical id (tile, slab): the n_slabs slabs of one tile are consecutive on one XCD
   const int n_slabs = a.H / (kSlabGroups * 16);
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int L = ((slot / n_slabs) * kXcds + xcd) * n_slabs + slot % n_slabs;
-  const int tj = L / n_slabs, slab = L - tj * n_slabs;
-  if (tj >= a.num_tiles[1]) return;
-  const TileDesc td = a.tiles_big[tj];
-  const int e = td.expert;
-  const int e_lo = a.expert_offsets[e], e_hi = a.expert_offsets[e + 1];
-  // The big tiles of one expert all have the same size except the last, so the previous
-  // tile gives the size when this one is the last: a run starts at every NT-th tile.
-  const int tile_rows = (td.row_start + td.nrows >= e_hi && td.row_start > e_lo)
-                            ? a.tiles_big[tj - 1].nrows : td.nrows;
-  if (((td.row_start - e_lo) / tile_rows) % NT != 0) return;
-  const int row_end = min(e_hi, td.row_start + NT * tile_rows);
-
+  const int n_runs = a.num_tiles[2];
+  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
   const int code_bytes = a.I / 2, scale_cols = a.I / 16;
-  W2Regs<WRG> wr[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) fc2_load<NW, WRG>(a, e, w, lane, slab, c, NCH, wr[c]);
-  // the block scales of K-steps (0, 1) and (2, 3) of every chunk and row group, as f16
-  f16x2 wsc[NCH][WRG][2];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
+  const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
+  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
 
   // Token rows [p0, p0 + nr) of the run (rows past nr repeat the last one; they are not
   // stored).  Four threads per row, each NCH 16-byte pieces of codes (32 values) and the
@@ -325,108 +308,121 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
     }
   };
 
-  const float al = a.alpha2[e];
-  const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
-  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
-  uint16_t* out_cols = a.o_rows + 16 * (slab * kSlabGroups + w * WRG);
-  int32_t flat[kFc2PassRows / 16];
-  int p0 = td.row_start;
-  int nr = min(kFc2PassRows, row_end - p0);
+  for (int k = blockIdx.x / kXcds;; k += per_xcd) {
+    const int run = xcd + kXcds * (k / n_slabs);
+    if (run >= n_runs) break;
+    const int slab = k - (k / n_slabs) * n_slabs;
+    const TileDesc rd = a.runs[run];
+    const int e = rd.expert, row_end = rd.row_start + rd.nrows;
 
-  // One pass over NCB 16-token blocks: all K-steps from the resident weights, then the
-  // BF16 rows (stored at their flat ids, through the per-wave LDS transpose).
-  auto pass = [&](auto ncb_c) {
-    constexpr int NCB = decltype(ncb_c)::value;
-    f32x4 acc[WRG][NCB];
+    W2Regs<WRG> wr[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < NCH; ++c) fc2_load<NW, WRG>(a, e, w, lane, slab, c, NCH, wr[c]);
+    // the block scales of K-steps (0, 1) and (2, 3) of every chunk and row group, as f16
+    f16x2 wsc[NCH][WRG][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // The decoded weights are the same in every pass: an opaque 1.0 as the conversion's
-        // scale (a scalar register, no vector work) keeps the compiler from hoisting all of
-        // them (NCH*4*WRG*4 registers) out of the pass loop.
-        uint32_t one_bits = 0x3F800000u;
-        asm volatile("" : "+s"(one_bits));
-        const float one = __uint_as_float(one_bits);
-        f16x8 xf[NCB];
+    for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          xf[cb] = *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
+      for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
+
+    const float al = a.alpha2[e];
+    uint16_t* out_cols = a.o_rows + 16 * (slab * kSlabGroups + w * WRG);
+    int32_t flat[kFc2PassRows / 16];
+    int p0 = rd.row_start;
+    int nr = min(kFc2PassRows, row_end - p0);
+
+    // One pass over NCB 16-token blocks: all K-steps from the resident weights, then the
+    // BF16 rows (stored at their flat ids, through the per-wave LDS transpose).
+    auto pass = [&](auto ncb_c) {
+      constexpr int NCB = decltype(ncb_c)::value;
+      f32x4 acc[WRG][NCB];
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) {
-          const uint4& cc = wr[c].c[r];
-          const uint32_t cw = s == 0 ? cc.x : s == 1 ? cc.y : s == 2 ? cc.z : cc.w;
-          const f16x8 wf = decode8(cw, bcast_f16x2(wsc[c][r][s >> 1], s & 1), one);
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          // The decoded weights are the same in every pass: an opaque 1.0 as the
+          // conversion's scale (a scalar register, no vector work) keeps the compiler from
+          // hoisting all of them (NCH*4*WRG*4 registers) out of the pass loop.
+          uint32_t one_bits = 0x3F800000u;
+          asm volatile("" : "+s"(one_bits));
+          const float one = __uint_as_float(one_bits);
+          f16x8 xf[NCB];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            acc[r][cb] = mfma16x16x32(wf, xf[cb],
-                                      (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
+            xf[cb] = *reinterpret_cast<const f16x8*>(xrow + cb * 16 * kFc2LdsRow + c * kChunk + 32 * s);
+#pragma unroll
+          for (int r = 0; r < WRG; ++r) {
+            const uint4& cc = wr[c].c[r];
+            const uint32_t cw = s == 0 ? cc.x : s == 1 ? cc.y : s == 2 ? cc.z : cc.w;
+            const f16x8 wf = decode8(cw, bcast_f16x2(wsc[c][r][s >> 1], s & 1), one);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[r][cb] = mfma16x16x32(wf, xf[cb],
+                                        (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // bounds the live decoded weights to one K-step
         }
-        __builtin_amdgcn_sched_barrier(0);   // bounds the live decoded weights to one K-step
       }
-    }
-    constexpr int kStride = fc2_out_stride<WRG>();
-    constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
-    constexpr int kRowsPerPass = 64 / kPieces;
+      constexpr int kStride = fc2_out_stride<WRG>();
+      constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
+      constexpr int kRowsPerPass = 64 / kPieces;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int r = 0; r < WRG; ++r) {
-        const f32x4 o = acc[r][cb];
-        u32x2 v;
-        v[0] = pack_bf16x2(o[0] * al, o[1] * al);
-        v[1] = pack_bf16x2(o[2] * al, o[3] * al);
-        *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
+        for (int r = 0; r < WRG; ++r) {
+          const f32x4 o = acc[r][cb];
+          u32x2 v;
+          v[0] = pack_bf16x2(o[0] * al, o[1] * al);
+          v[1] = pack_bf16x2(o[2] * al, o[3] * al);
+          *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 16 / kRowsPerPass; ++q) {
+          const int row = q * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
+          const int64_t f = __shfl(flat[cb], row);
+          if (cb * 16 + row < nr)
+            *reinterpret_cast<u32x4*>(out_cols + f * a.H + 8 * piece) = val;
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int q = 0; q < 16 / kRowsPerPass; ++q) {
-        const int row = q * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
-        const int64_t f = __shfl(flat[cb], row);
-        if (cb * 16 + row < nr)
-          *reinterpret_cast<u32x4*>(out_cols + f * a.H + 8 * piece) = val;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  };
+    };
 
-  fetch(p0, nr);
-  stage();
-  __syncthreads();
-  using std::integral_constant;
-  for (;;) {
-    // flat ids of this pass's rows (lane l: block row l % 16), loaded before the next
-    // pass's codes so that waiting for them does not wait for those
-#pragma unroll
-    for (int cb = 0; cb < kFc2PassRows / 16; ++cb)
-      flat[cb] = a.sorted_row_idx[p0 + min(cb * 16 + (lane & 15), nr - 1)];
-    const int next = p0 + kFc2PassRows;
-    const bool more = next < row_end;
-    const int nr_next = more ? min(kFc2PassRows, row_end - next) : 0;
-    if (more) fetch(next, nr_next);
-    switch ((nr + 15) / 16) {
-      case 1: pass(integral_constant<int, 1>{}); break;
-      case 2: pass(integral_constant<int, 2>{}); break;
-      case 3: pass(integral_constant<int, 3>{}); break;
-      default: pass(integral_constant<int, 4>{}); break;
-    }
-    if (!more) break;
-    __syncthreads();
+    fetch(p0, nr);
     stage();
     __syncthreads();
-    p0 = next;
-    nr = nr_next;
+    using std::integral_constant;
+    for (;;) {
+      // flat ids of this pass's rows (lane l: block row l % 16), loaded before the next
+      // pass's codes so that waiting for them does not wait for those
+#pragma unroll
+      for (int cb = 0; cb < kFc2PassRows / 16; ++cb)
+        flat[cb] = a.sorted_row_idx[p0 + min(cb * 16 + (lane & 15), nr - 1)];
+      const int next = p0 + kFc2PassRows;
+      const bool more = next < row_end;
+      const int nr_next = more ? min(kFc2PassRows, row_end - next) : 0;
+      if (more) fetch(next, nr_next);
+      switch ((nr + 15) / 16) {
+        case 1: pass(integral_constant<int, 1>{}); break;
+        case 2: pass(integral_constant<int, 2>{}); break;
+        case 3: pass(integral_constant<int, 3>{}); break;
+        default: pass(integral_constant<int, 4>{}); break;
+      }
+      __syncthreads();      // the tile is read; the next pass or item overwrites it
+      if (!more) break;
+      stage();
+      __syncthreads();
+      p0 = next;
+      nr = nr_next;
+    }
   }
 }
 
 template <int NW, int WRG, int NCH>
 static void launch_fc2_stationary(const LayerArgs& a, hipStream_t stream) {
-  const int n_slabs = a.H / (NW * WRG * 16);
-  const int64_t grid = round_up(a.max_big, kXcds) * n_slabs;
-  if (grid > 0)
-    fc2_stationary_kernel<NW, WRG, NCH, kFc2RunTiles>
-        <<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a);
+  fc2_stationary_kernel<NW, WRG, NCH>
+      <<<dim3(kFc2StationaryGrid), dim3(NW * 64), 0, stream>>>(a);
 }
 
 template <int NW, int WRG, int BN, int SPW, int SPLIT = 1>

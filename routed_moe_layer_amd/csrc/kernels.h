@@ -22,10 +22,16 @@ constexpr int kRouteTile = 1024;
 constexpr int kRouteThreads = 256;
 // Grouped-GEMM token tiles (the N side of both FC kernels).  An expert with at most
 // kSmallRows routed rows gets one "small" tile; a larger expert is split into
-// nb = ceil(cnt / kBigRows) "big" tiles of near-equal size (a multiple of 16 rows, the last
-// one shorter).  The two lists feed two variants of the GEMM kernels.
+// nb = ceil(cnt / kBigTileRows) "big" tiles of near-equal size (a multiple of 16 rows, the
+// last one shorter).  The two lists feed two variants of the GEMM kernels, whose big-tile
+// LDS tiles are kBigRows rows; big tiles hold at most seven 16-row blocks, so the kernels
+// need no accumulators for an eighth.
 constexpr int kSmallRows = 32;
 constexpr int kBigRows = 128;
+constexpr int kBigTileRows = 112;
+// FC2 for many routed rows works on runs of up to kRunTiles consecutive big tiles of one
+// expert (a contiguous range of its sorted rows).
+constexpr int kRunTiles = 4;
 
 inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
 inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
@@ -33,7 +39,7 @@ inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
 inline int64_t max_small_tiles(int64_t R, int E) { return R < E ? R : E; }
 inline int64_t max_big_tiles(int64_t R, int E) {
   const int64_t big_experts = R / (kSmallRows + 1);
-  return R / kBigRows + (big_experts < E ? big_experts : E);
+  return R / kBigTileRows + (big_experts < E ? big_experts : E);
 }
 
 hipError_t launch_quantize_nvfp4(const uint16_t* src, int64_t groups, int64_t rows_per_group,
@@ -53,7 +59,8 @@ struct RouteBuffers {
   int32_t* expanded_row_idx; // [n] position map: sorted position of f, -1 out of range
   TileDesc* tiles_small;     // [max_small_tiles] or null
   TileDesc* tiles_big;       // [max_big_tiles] or null
-  int32_t* num_tiles;        // [2]: small, big; or null
+  TileDesc* runs;            // [max_big_tiles] FC2 runs (needs the tile lists) or null
+  int32_t* num_tiles;        // [2] small, big (or [3] with runs); or null
   float* amax_reset;         // [E] zeroed by the scan kernel, or null
   int32_t* key_value;        // [kv_rows, 2]: (expert id, count) of the experts with a
                              // nonzero count in increasing id, then zero rows; or null.
@@ -150,8 +157,8 @@ struct LayerArgs {
   const int32_t* expanded_row_idx;
   const TileDesc* tiles_small;
   const TileDesc* tiles_big;
-  const int32_t* num_tiles;    // [2]
-  const int32_t* expert_offsets;   // [E + 1] first sorted row of each expert, then the total
+  const TileDesc* runs;        // FC2 runs (list length max_big_tiles)
+  const int32_t* num_tiles;    // [3]: small tiles, big tiles, runs
   int64_t max_small, max_big;
   const uint8_t* w13_codes;    // prepared
   const uint8_t* w13_scales;

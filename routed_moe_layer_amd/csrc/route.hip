@@ -101,8 +101,8 @@ __device__ __forceinline__ void expert_tiles(int cnt, int* n_small, int* n_big, 
   *n_small = 0; *n_big = 0; *base = 0;
   if (cnt <= 0) return;
   if (cnt <= kSmallRows) { *n_small = 1; *base = cnt; return; }
-  const int nb = (cnt + kBigRows - 1) / kBigRows;
-  const int b = min(kBigRows, ((cnt + nb - 1) / nb + 15) / 16 * 16);
+  const int nb = (cnt + kBigTileRows - 1) / kBigTileRows;
+  const int b = min(kBigTileRows, ((cnt + nb - 1) / nb + 15) / 16 * 16);
   *base = b;
   *n_big = (cnt + b - 1) / b;
 }
@@ -110,8 +110,9 @@ __device__ __forceinline__ void expert_tiles(int cnt, int* n_small, int* n_big, 
 // One round of the expert scan over experts e0 .. e0 + blockDim.x - 1; thread e - e0 holds
 // expert e's count `cnt` (0 for e >= E).  Writes the expert offsets (also to off_sh when
 // given), the inclusive cumsum, and either the grouped-GEMM tile lists or the key-value
-// pairs.  carry[0..2] are the running totals of rows, small tiles (or nonzero experts)
-// and big tiles; they are updated for the next round.
+// pairs, and when asked the FC2 runs (up to kRunTiles consecutive big tiles of one
+// expert).  carry[0..3] are the running totals of rows, small tiles (or nonzero experts),
+// big tiles and runs; they are updated for the next round.
 __device__ void scan_experts_round(const RouteBuffers& b, int E, int e, int cnt, uint64_t* sh,
                                    int* carry, int32_t* off_sh) {
   const bool lists = b.tiles_small != nullptr;
@@ -139,8 +140,22 @@ __device__ void scan_experts_round(const RouteBuffers& b, int E, int e, int cnt,
     for (int j = 0; j < n_big; ++j)
       b.tiles_big[carry[2] + bexcl + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
   }
+  int rtotal = 0;
+  if (b.runs) {
+    const int n_runs = (n_big + kRunTiles - 1) / kRunTiles;
+    uint64_t rtot;
+    const int rexcl = static_cast<int>(block_excl_scan64(static_cast<uint64_t>(n_runs), sh, &rtot));
+    rtotal = static_cast<int>(rtot);
+    if (e < E)
+      for (int j = 0; j < n_runs; ++j) {
+        const int r0 = j * kRunTiles * base;
+        b.runs[carry[3] + rexcl + j] = TileDesc{e, off + r0, min(kRunTiles * base, cnt - r0), 0};
+      }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) { carry[0] += total; carry[1] += stotal; carry[2] += btotal; }
+  if (threadIdx.x == 0) {
+    carry[0] += total; carry[1] += stotal; carry[2] += btotal; carry[3] += rtotal;
+  }
   __syncthreads();
 }
 
@@ -150,7 +165,11 @@ __device__ void scan_experts_finish(const RouteBuffers& b, int E, const int* car
   if (threadIdx.x == 0) {
     b.offsets[E] = carry[0];
     if (b.available) b.available[0] = carry[0];
-    if (b.num_tiles) { b.num_tiles[0] = carry[1]; b.num_tiles[1] = carry[2]; }
+    if (b.num_tiles) {
+      b.num_tiles[0] = carry[1];
+      b.num_tiles[1] = carry[2];
+      if (b.runs) b.num_tiles[2] = carry[3];
+    }
   }
   if (b.key_value)
     for (int i = carry[1] + threadIdx.x; i < b.kv_rows; i += blockDim.x) {
@@ -161,8 +180,8 @@ __device__ void scan_experts_finish(const RouteBuffers& b, int E, const int* car
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int ntiles, int E) {
   __shared__ uint64_t sh[16];
-  __shared__ int carry[3];
-  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
+  __shared__ int carry[4];
+  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; carry[3] = 0; }
   __syncthreads();
   int32_t* __restrict__ tile_hist = b.tile_hist;
   // Experts are handled in rounds of 1024 (E <= 4096).
@@ -291,7 +310,7 @@ __device__ __forceinline__ void route_small_body(const int32_t* __restrict__ ids
   int32_t* wave_hist = lds;
   int32_t* off_sh = lds + nw * E;
   for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
-  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; }
+  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; carry[3] = 0; }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t wave_base = static_cast<int64_t>(w) * (kRouteTile / nw);
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(kRouteSmallThreads) void route_small_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
   extern __shared__ int32_t lds[];
   __shared__ uint64_t sh[16];
-  __shared__ int carry[3];
+  __shared__ int carry[4];
   route_small_body(ids, n, E, nbits, b, lds, sh, carry);
 }
 
@@ -344,7 +363,7 @@ __global__ __launch_bounds__(kRouteSmallThreads) void quantize_route_small_kerne
     RouteBuffers b) {
   extern __shared__ int32_t lds[];
   __shared__ uint64_t sh[16];
-  __shared__ int carry[3];
+  __shared__ int carry[4];
   if (blockIdx.x == 0) {
     route_small_body(ids, n, E, nbits, b, lds, sh, carry);
     return;
@@ -367,7 +386,7 @@ __global__ __launch_bounds__(kRouteSmallThreads) void route_permute_small_kernel
     PermuteArgs p) {
   extern __shared__ int32_t lds[];
   __shared__ uint64_t sh[16];
-  __shared__ int carry[3];
+  __shared__ int carry[4];
   __shared__ float red[kRouteSmallThreads / kWave];
   __shared__ int32_t dst[64];
   int32_t* map = lds + (kRouteThreads / kWave + 1) * E;
