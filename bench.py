@@ -480,8 +480,8 @@ def _bench_line(log_path):
 
 def _short(name):
     n = name.replace("void ", "").replace("rmoe::", "")
-    if n.startswith(("grouped_gemm_kernel", "fc2_kernel", "finalize", "quantize", "route",
-                     "prepare")):
+    if n.startswith(("grouped_gemm_kernel", "fc2_kernel", "fc2_stationary_kernel", "finalize",
+                     "quantize", "route", "prepare", "topk")):
         return n.split("(")[0]
     return n if len(n) <= 72 else n[:72] + "..."
 
@@ -490,7 +490,7 @@ def _role(name):
     n = _short(name)
     if n.startswith("grouped_gemm_kernel<0"):
         return "fc1_kernel"
-    if n.startswith("grouped_gemm_kernel<1") or n.startswith("fc2_kernel"):
+    if n.startswith(("grouped_gemm_kernel<1", "fc2_kernel", "fc2_stationary_kernel")):
         return "fc2_kernel"
     if n.startswith("finalize_kernel"):
         return "finalize_kernel"

@@ -534,7 +534,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 // FC1's tokens as f16 rows.  Big tiles (up to kBigRows tokens) run 4 waves x 2
 // groups, FC1 with f16 rows; with at least kManyRows routed rows (about two big tiles
 // per CU) FC1's big tiles run 4 waves x 4 groups instead (half the LDS operand reads per
-// MFMA), also staging f16 rows (no token decode).
+// MFMA; the tokens are staged as codes, a quarter of the f16 rows' bytes: each token row is
+// fetched once per slab, so f16 rows would double the kernel's memory traffic).
 // A slab that does not divide the rows falls back to 128-row slabs.
 constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
 constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
@@ -565,7 +566,7 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
     launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
   if constexpr (MODE == 0) {
     if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
-      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, true>(a, a.max_big, 1, stream);
+      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);
       return hipGetLastError();
     }
   }
