@@ -262,6 +262,7 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
 // rows are fetched from HBM once and reread by the other slabs from that XCD's L2.
 constexpr int kFc2PassRows = 64;
 constexpr int kFc2StationaryGrid = 2 * 256;     // two workgroups on each of 256 CUs
+constexpr int kFc2StationaryRows = 2 * kFc2PassRows;
 
 template <int NW, int WRG, int NCH>
 __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a) {
@@ -439,7 +440,8 @@ static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
 
 // Small tiles: 128-row slabs in groups of 4 (enough workgroups for decode-size batches);
 // big tiles: the weight-stationary kernel on 256-column slabs (H a multiple of 256, I of
-// 128), else the token-resident kernel on 128-column slabs, all slabs in one group.
+// 128, long runs), else the token-resident kernel on 256-column slabs (128 when H is not a
+// multiple of 256), all slabs in one group.
 bool fc2_resident_fits(const LayerArgs& a) { return a.Ip <= kFc2MaxIp; }
 
 void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
@@ -447,12 +449,18 @@ void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
 }
 
 void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream) {
-  if (a.H % 256 == 0 && a.I == a.Ip) {
+  // The stationary kernel loads a slab's weights once per run, so it pays off when runs
+  // span several passes: experts with at least kFc2StationaryRows routed rows on average.
+  const bool long_runs = static_cast<int64_t>(a.T) * a.k >=
+                         static_cast<int64_t>(kFc2StationaryRows) * a.E;
+  if (a.H % 256 == 0 && a.I == a.Ip && long_runs) {
     switch (a.Ip / kChunk) {
       case 1: launch_fc2_stationary<4, 4, 1>(a, stream); break;
       case 2: launch_fc2_stationary<4, 4, 2>(a, stream); break;
       default: launch_fc2_stationary<4, 4, 3>(a, stream); break;
     }
+  } else if (a.H % 256 == 0) {
+    launch_fc2_variant<4, 4, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
   } else {
     launch_fc2_variant<4, 2, kBigRows / 2, 1 << 20, 2>(a, a.max_big, 1, stream);
   }

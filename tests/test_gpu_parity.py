@@ -256,6 +256,10 @@ EDGE = [
     # 128-wide chunks, with runs split inside hot experts and ragged last passes
     ("stationary_fc2_skewed", _edge("edge_stat", T=8192, E=64, k=8, H=512, I=256,
                                     zipf_s=1.0, seed_index=41), None),
+    # 65536 routed rows over 1024 experts (64 rows each on average): the token-resident
+    # FC2 on 256-column slabs, big tiles split into 64-row sub-tiles
+    ("resident_fc2_short_runs", _edge("edge_short", T=8192, E=1024, k=8, H=256, I=128,
+                                      seed_index=42), None),
 ]
 
 
