@@ -414,7 +414,8 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
         !mark(2))
       return MOE_ERR_HIP;
   } else {
-    if (launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales, x_dec, s) != hipSuccess ||
+    if (launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales,
+                              layer_writes_x_dec(R) ? x_dec : nullptr, s) != hipSuccess ||
         !mark(1))
       return MOE_ERR_HIP;
     if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;

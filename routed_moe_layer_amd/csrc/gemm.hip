@@ -542,7 +542,6 @@ constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
 // FC1 small tiles: 4 row groups per wave (256-row slabs), so that a decode-size batch's
 // workgroups fit the chip in one round instead of 1.3.
 constexpr int kFc1SmallWRG = 4;
-constexpr int64_t kManyRows = 2 * 256 * kBigRows;
 
 template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
 static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipStream_t stream) {
@@ -560,10 +559,17 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   constexpr bool kRows = MODE == 0;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const bool many = static_cast<int64_t>(a.T) * a.k >= kManyRows;
-  if (MODE == 0 && rows_total % GemmCfg<MODE, 4, kFc1SmallWRG, kSmallRows>::kWgRows == 0)
+  const bool small_wide =
+      MODE == 0 && rows_total % GemmCfg<MODE, 4, kFc1SmallWRG, kSmallRows>::kWgRows == 0;
+  if (kRows && many) {
+    // no f16 copy of x: the small tiles stage codes too
+    if (small_wide) launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, false>(a, a.max_small, 0, stream);
+    else launch_variant<MODE, 4, 2, kSmallRows, 1, false>(a, a.max_small, 0, stream);
+  } else if (small_wide) {
     launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, kRows>(a, a.max_small, 0, stream);
-  else
+  } else {
     launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
+  }
   if constexpr (MODE == 0) {
     if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
       launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);

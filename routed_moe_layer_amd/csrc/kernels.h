@@ -32,6 +32,10 @@ constexpr int kBigTileRows = 112;
 // FC2 for many routed rows works on runs of up to kRunTiles consecutive big tiles of one
 // expert (a contiguous range of its sorted rows).
 constexpr int kRunTiles = 4;
+// From kManyRows routed rows on (about two big tiles per CU), FC1 stages every token tile
+// as NVFP4 codes and the layer does not write the f16 copy of x (x_dec).
+constexpr int64_t kManyRows = 2 * 256 * kBigRows;
+inline bool layer_writes_x_dec(int64_t R) { return R < kManyRows; }
 
 inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
 inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }

@@ -25,6 +25,8 @@ import oracle
 
 OUT_RTOL = 2e-2
 CODE_DIFF_FRAC = 1e-3
+# moe_forward writes the f16 copy of x (x_dec) only below this many routed rows
+X_DEC_MAX_ROWS = 65536
 
 # signed position of each E2M1 code on the value line (+0 and -0 share position 0)
 _POS = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, -1, -2, -3, -4, -5, -6, -7])
@@ -83,9 +85,11 @@ def check_layer(p, gpu_out, inter, ref):
     # bit-exact: x codes and scales, routing
     assert np.array_equal(inter["x_scales"], ref["x_scales"])
     assert np.array_equal(inter["x_codes"], oracle.pack_nibbles(ref["x_codes"]))
-    # FC1's f16 operand: the exact values of x's NVFP4 blocks
-    assert np.array_equal(inter["x_dec"].astype(np.float64),
-                          oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
+    # FC1's f16 operand: the exact values of x's NVFP4 blocks (written below 65536 routed
+    # rows; with more, FC1 stages the codes)
+    if cfg.T * cfg.k < X_DEC_MAX_ROWS:
+        assert np.array_equal(inter["x_dec"].astype(np.float64),
+                              oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
     for key in ("sorted_ids", "sorted_row_idx", "expanded_row_idx", "counts", "cumsum"):
         assert np.array_equal(inter[key], ref[key]), key
     # intermediate codes

@@ -85,8 +85,9 @@ def test_full_layer_parity(full_weights, cfg):
     ref = oracle_dense(p, sample, weight_cache=p["weight_cache"])
     assert np.array_equal(inter["x_codes"][sample], oracle.pack_nibbles(ref["x_codes"]))
     assert np.array_equal(inter["x_scales"][sample], ref["x_scales"])
-    assert np.array_equal(inter["x_dec"][sample].astype(np.float64),
-                          oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
+    if cfg.T * k < compare.X_DEC_MAX_ROWS:
+        assert np.array_equal(inter["x_dec"][sample].astype(np.float64),
+                              oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
     pos = inter["expanded_row_idx"].reshape(cfg.T, k)[sample]            # [n, k]
     gc = compare.unpack(inter["a_codes"][pos.ravel()])
     gs = inter["a_scales"][pos.ravel()]

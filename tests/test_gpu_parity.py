@@ -260,6 +260,10 @@ EDGE = [
     # FC2 on 256-column slabs, big tiles split into 64-row sub-tiles
     ("resident_fc2_short_runs", _edge("edge_short", T=8192, E=1024, k=8, H=256, I=128,
                                       seed_index=42), None),
+    # 65536 routed rows, Zipf 1.2 over 512 experts: 241 small tiles staged as codes (no f16
+    # copy of x at this size) beside a 4081-row expert
+    ("many_rows_small_tiles", _edge("edge_many_small", T=4096, E=512, k=16, H=256, I=128,
+                                    zipf_s=1.2, seed_index=43), None),
 ]
 
 
