@@ -219,12 +219,15 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
 STREAM_CASES = {"prefill": (4096, 2), "mid": (256, 2)}
 
 
-def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmup, events):
+def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmup, events,
+                      sealed=False):
     """Time the streamed layer on a layer workload's inputs: per step, a producer on a
     second stream fills a `slots`-slot ring chunk by chunk (copies of the resident ids,
     route weights and x into the slot, each part acquired and published) and the
-    consumer (moe_forward_streamed, one chunk per call) runs on the launch stream, so
-    production overlaps the layer's work on earlier chunks."""
+    consumer runs on the launch stream, so production overlaps the consumer's work on
+    earlier chunks.  The consumer is moe_forward_streamed (one chunk per call: chunk-local
+    expert pools) or, when `sealed`, moe_forward_absorb per chunk and moe_forward_seal at
+    the end of the stream (reservations across chunks)."""
     E, H, I, k, T = cfg.E, cfg.H, cfg.I, cfg.k, cfg.T
     dims = rm.MoeDims(H, I, E, k)
     x, rw = keep["x"], keep["rw"]
@@ -235,7 +238,9 @@ def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmu
     rx = buf[lay["x"]:].view(torch.int16)[:slots * chunk * H].view(slots, chunk, H)
     rids = buf[lay["expert_ids"]:].view(torch.int32)[:slots * chunk * k].view(slots, chunk, k)
     rrw = buf[lay["route_weights"]:].view(torch.int16)[:slots * chunk * k].view(slots, chunk, k)
-    ws = torch.empty(rm.moe_workspace_size(dims, chunk), dtype=torch.uint8, device="cuda")
+    ws_bytes = (rm.moe_sealed_workspace_size(dims, T) if sealed
+                else rm.moe_workspace_size(dims, chunk))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     n = (T + chunk - 1) // chunk
     prod = torch.cuda.Stream()
@@ -256,16 +261,23 @@ def streamed_workload(cfg, keep, torch, rm, prepared, chunk, slots, steps, warmu
                 rm.moe_ring_acquire(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
                 rx[sl, :hi - lo].copy_(x[lo:hi])
                 rm.moe_ring_publish(dims, ring, sl, rm.MOE_RING_LAYOUT, stream=prod)
-            rm.moe_forward_streamed(dims, ring, T, i, 1, prepared, keep["qx"], keep["alpha1"],
-                                    keep["qa"], keep["alpha2"], keep["beta"], keep["lam"], ws,
-                                    out)
+            if sealed:
+                rm.moe_forward_absorb(dims, ring, T, i, 1, keep["qx"], ws)
+            else:
+                rm.moe_forward_streamed(dims, ring, T, i, 1, prepared, keep["qx"],
+                                        keep["alpha1"], keep["qa"], keep["alpha2"],
+                                        keep["beta"], keep["lam"], ws, out)
+        if sealed:
+            rm.moe_forward_seal(dims, T, prepared, keep["alpha1"], keep["qa"], keep["alpha2"],
+                                keep["beta"], keep["lam"], ws, out)
 
     gpu_ms, wall_ms = _time_calls(step, torch, steps, warmup, events)
     torch.cuda.synchronize()
     status = int(buf[lay["status"]:lay["status"] + 4].view(torch.int32).item())
     if status != rm.MOE_RING_OK:
         raise RuntimeError(f"streamed run ended with ring status {status}")
-    return {"workload": f"{cfg.name}_streamed_C{chunk}_S{slots}", "chunks": n,
+    tag = "sealed" if sealed else "streamed"
+    return {"workload": f"{cfg.name}_{tag}_C{chunk}_S{slots}", "chunks": n,
             "tokens_per_s": T / (wall_ms * 1e-3), "ms_per_step": wall_ms,
             "gpu_ms_per_step": gpu_ms}
 
@@ -731,13 +743,15 @@ def main():
             if name not in keeps:
                 continue
             cfg = cfgs[name][0]
-            log(f"timing {cfg.name} streamed in chunks of {chunk} through {slots} slots")
-            r = streamed_workload(cfg, keeps[name], torch, rm, prepared, chunk, slots,
-                                  args.steps, args.warmup, events)
-            r["batch_tokens_per_s"] = results[name]["tokens_per_s"]
-            streamed[name] = r
-            log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step "
-                f"(batch {results[name]['tokens_per_s']:.1f})")
+            for sealed in (False, True):
+                tag = "sealed" if sealed else "streamed"
+                log(f"timing {cfg.name} {tag} in chunks of {chunk} through {slots} slots")
+                r = streamed_workload(cfg, keeps[name], torch, rm, prepared, chunk, slots,
+                                      args.steps, args.warmup, events, sealed=sealed)
+                r["batch_tokens_per_s"] = results[name]["tokens_per_s"]
+                streamed[name + ("_sealed" if sealed else "")] = r
+                log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step "
+                    f"(batch {results[name]['tokens_per_s']:.1f})")
     if not chosen:                      # routing primitive only
         print(json.dumps({"routing_primitive": route_res}), flush=True)
         return

@@ -277,8 +277,10 @@ moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
 /* ------------------------------------------------------------------------------------
  * Chunk-streamed front end, one rank ("[RFC] Chunk-ready symmetric-buffer protocol for
  * streaming MegaMoE inputs": sections "Fixed-capacity ring", "Independent readiness
- * generations", "Memory ordering", "Chunk-aware dispatch scheduling" option 1 --
- * chunk-local expert pools -- and "Progress and deadlock requirements").
+ * generations", "Memory ordering", "Chunk-aware dispatch scheduling" options 1 --
+ * chunk-local expert pools, moe_forward_streamed -- and 2 -- reservations across chunks
+ * with an end-of-stream seal, moe_forward_absorb + moe_forward_seal -- and "Progress and
+ * deadlock requirements").
  *
  * A caller-owned ring of num_slots slots of tokens_per_slot (C) tokens.  Token chunk n
  * (tokens n*C .. min((n+1)*C, total) - 1) lives in slot n % num_slots.  Two producers fill
@@ -356,6 +358,40 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring /*host*/,
                                   const float* situ_beta, const float* situ_linear_beta,
                                   uint32_t timeout_us, void* workspace, size_t workspace_bytes,
                                   uint16_t* out, moe_stream_t stream);
+
+/* Scheduling option 2 of the same RFC section, with the completion rule that every expert
+ * block is complete at the end-of-stream seal: the stream's routed rows are packed per
+ * expert over all its chunks, as in one moe_forward over the whole stream.
+ *
+ * moe_forward_absorb consumes chunks first_chunk .. first_chunk + num_chunks - 1 of a
+ * stream of total_tokens tokens in order, like moe_forward_streamed: for each it waits for
+ * both parts, quantizes the chunk's tokens (qx as in moe_forward) into the stream's rows of
+ * the workspace, copies its expert ids and route weights there, and publishes the slot as
+ * consumed, so the slot can be refilled before the stream ends.  Absorb the chunks in
+ * stream order, each once, in any number of calls (for example one call per chunk,
+ * alternating with the producers, under the progress rule above).
+ *
+ * moe_forward_seal then runs the routing, FC1, SiTU, requantization, FC2 and the
+ * finalization once over all total_tokens tokens into out, BF16 [total_tokens, H]; the
+ * result equals moe_forward on the whole stream bit for bit.
+ *
+ * workspace: moe_sealed_workspace_size(d, total_tokens) bytes, 256-byte aligned (device),
+ * the same buffer for every absorb call and the seal of one stream; its first
+ * moe_workspace_size(d, total_tokens) bytes hold moe_forward's workspace layout for
+ * total_tokens tokens (moe_workspace_layout) after the seal. */
+moe_status_t moe_sealed_workspace_size(moe_dims_t d, int32_t total_tokens,
+                                       size_t* bytes /*host*/);
+
+moe_status_t moe_forward_absorb(moe_dims_t d, const moe_ring_t* ring /*host*/,
+                                int32_t total_tokens, int32_t first_chunk, int32_t num_chunks,
+                                const float* qx, uint32_t timeout_us, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream);
+
+moe_status_t moe_forward_seal(moe_dims_t d, int32_t total_tokens, const void* prepared,
+                              const float* alpha1, const float* qa, const float* alpha2,
+                              const float* situ_beta, const float* situ_linear_beta,
+                              void* workspace, size_t workspace_bytes, uint16_t* out,
+                              moe_stream_t stream);
 
 #ifdef __cplusplus
 }

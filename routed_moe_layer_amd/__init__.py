@@ -17,7 +17,8 @@ __all__ = [
     "moe_quantize_nvfp4", "moe_prepare_weights", "moe_route", "moe_route_v2",
     "MoeRouteOptions", "moe_forward", "moe_forward_timed", "MOE_FORWARD_STAGES",
     "MoeRing", "make_ring", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
-    "moe_ring_publish", "moe_forward_streamed", "moe_topk_softmax", "MOE_RING_ROUTE",
+    "moe_ring_publish", "moe_forward_streamed", "moe_sealed_workspace_size",
+    "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax", "MOE_RING_ROUTE",
     "MOE_RING_LAYOUT",
     "MOE_RING_OK", "MOE_RING_CONSUMER_TIMEOUT", "MOE_RING_PRODUCER_TIMEOUT",
     "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
@@ -36,7 +37,8 @@ EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_siz
             "moe_workspace_layout", "moe_route_workspace_size", "moe_quantize_nvfp4",
             "moe_prepare_weights", "moe_route", "moe_route_v2", "moe_forward",
             "moe_forward_timed", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
-            "moe_ring_publish", "moe_forward_streamed", "moe_topk_softmax")
+            "moe_ring_publish", "moe_forward_streamed", "moe_sealed_workspace_size",
+            "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax")
 
 MOE_RING_ROUTE = 0
 MOE_RING_LAYOUT = 1
@@ -124,6 +126,10 @@ def _lib():
             "moe_ring_publish": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, ctypes.c_int, P]),
             "moe_forward_streamed": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, I32, I32, P, P,
                                           P, P, P, P, P, ctypes.c_uint32, P, SZ, P, P]),
+            "moe_sealed_workspace_size": (st, [MoeDims, I32, ctypes.POINTER(SZ)]),
+            "moe_forward_absorb": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, I32, I32, P,
+                                        ctypes.c_uint32, P, SZ, P]),
+            "moe_forward_seal": (st, [MoeDims, I32, P, P, P, P, P, P, P, SZ, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -289,6 +295,30 @@ def moe_forward_streamed(dims, ring, total_tokens, first_chunk, num_chunks, prep
         dims, ctypes.byref(ring), total_tokens, first_chunk, num_chunks, _ptr(prepared), _ptr(qx),
         _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
         timeout_us, _ptr(workspace), nb, _ptr(out), _stream(stream)))
+
+
+def moe_sealed_workspace_size(dims, total_tokens):
+    n = ctypes.c_size_t()
+    _check("moe_sealed_workspace_size",
+           _lib().moe_sealed_workspace_size(dims, total_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward_absorb(dims, ring, total_tokens, first_chunk, num_chunks, qx, workspace,
+                       timeout_us=0, workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_forward_absorb", _lib().moe_forward_absorb(
+        dims, ctypes.byref(ring), total_tokens, first_chunk, num_chunks, _ptr(qx), timeout_us,
+        _ptr(workspace), nb, _stream(stream)))
+
+
+def moe_forward_seal(dims, total_tokens, prepared, alpha1, qa, alpha2, situ_beta,
+                     situ_linear_beta, workspace, out, workspace_bytes=None, stream=None):
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check("moe_forward_seal", _lib().moe_forward_seal(
+        dims, total_tokens, _ptr(prepared), _ptr(alpha1), _ptr(qa), _ptr(alpha2),
+        _ptr(situ_beta), _ptr(situ_linear_beta), _ptr(workspace), nb, _ptr(out),
+        _stream(stream)))
 
 
 def moe_topk_softmax(T, num_experts, top_k, logits, expert_ids, route_weights, stream=None):

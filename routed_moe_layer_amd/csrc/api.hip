@@ -338,14 +338,16 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
                                  const float* qa, const float* alpha2, const float* situ_beta,
                                  const float* situ_linear_beta, void* workspace,
                                  size_t workspace_bytes, uint16_t* out, moe_stream_t stream,
-                                 void* const* events) {
+                                 void* const* events, bool quantized = false) {
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
   if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
-  if (!x || !expert_ids || !route_weights || !prepared || !qx || !alpha1 || !qa || !alpha2 ||
-      !workspace || !out)
+  // quantized: x's codes and scales (and, below 65536 routed rows, its f16 copy) are
+  // already in the workspace; x and qx are not used
+  if ((!quantized && (!x || !qx)) || !expert_ids || !route_weights || !prepared || !alpha1 ||
+      !qa || !alpha2 || !workspace || !out)
     return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(prepared, kAlign) ||
+  if ((!quantized && !aligned(x, 16)) || !aligned(out, 16) || !aligned(prepared, kAlign) ||
       !aligned(workspace, kAlign) || !aligned(expert_ids, 4) || !aligned(route_weights, 2))
     return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d, T);
@@ -406,7 +408,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   uint8_t* x_codes = ws + L.pub.x_codes;
   uint8_t* x_scales = ws + L.pub.x_scales;
   uint16_t* x_dec = reinterpret_cast<uint16_t*>(ws + L.pub.x_dec);
-  if (route_fits_one_workgroup(R, E)) {
+  if (!quantized && route_fits_one_workgroup(R, E)) {
     // small batch: quantization and routing in one launch (both stage marks after it)
     const QuantizeArgs qa{x, static_cast<int64_t>(T) * (H / kGroup), H / kGroup, T, qx,
                           x_codes, x_scales, x_dec};
@@ -414,8 +416,9 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
         !mark(2))
       return MOE_ERR_HIP;
   } else {
-    if (launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales,
-                              layer_writes_x_dec(R) ? x_dec : nullptr, s) != hipSuccess ||
+    if ((!quantized && launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales,
+                                             layer_writes_x_dec(R) ? x_dec : nullptr,
+                                             s) != hipSuccess) ||
         !mark(1))
       return MOE_ERR_HIP;
     if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
@@ -543,6 +546,108 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring, int32_t 
       return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+// Workspace of the sealed front end for a stream of `tokens` tokens: the layer's workspace
+// for that many tokens, then the stream's expert ids and route weights.
+struct SealedLayout {
+  size_t layer_bytes, ids, weights, total;   // the layer's part starts at offset 0
+};
+static moe_status_t sealed_layout(moe_dims_t d, int32_t tokens, SealedLayout* out) {
+  if (tokens < 1 || tokens > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  size_t layer = 0;
+  moe_status_t st = moe_workspace_size(d, tokens, &layer);
+  if (st != MOE_OK) return st;
+  Carver c;
+  c.take(layer);
+  out->layer_bytes = layer;
+  out->ids = c.take(static_cast<size_t>(tokens) * d.top_k * 4);
+  out->weights = c.take(static_cast<size_t>(tokens) * d.top_k * 2);
+  out->total = c.off;
+  return MOE_OK;
+}
+
+moe_status_t moe_sealed_workspace_size(moe_dims_t d, int32_t total_tokens, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  SealedLayout S;
+  moe_status_t st = sealed_layout(d, total_tokens, &S);
+  if (st == MOE_OK) *bytes = S.total;
+  return st;
+}
+
+static moe_status_t check_sealed_workspace(moe_dims_t d, int32_t total_tokens,
+                                           const void* workspace, size_t workspace_bytes,
+                                           SealedLayout* S) {
+  moe_status_t st = sealed_layout(d, total_tokens, S);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < S->total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_absorb(moe_dims_t d, const moe_ring_t* ring, int32_t total_tokens,
+                                int32_t first_chunk, int32_t num_chunks, const float* qx,
+                                uint32_t timeout_us, void* workspace, size_t workspace_bytes,
+                                moe_stream_t stream) {
+  moe_ring_layout_t RL;
+  moe_status_t st = check_ring(d, ring, &RL);
+  if (st != MOE_OK) return st;
+  const int64_t C = ring->tokens_per_slot, S = ring->num_slots;
+  if (total_tokens < 1 || first_chunk < 0 || num_chunks < 1 || !qx) return MOE_ERR_INVALID_ARG;
+  const int64_t chunks = (total_tokens + C - 1) / C;
+  if (static_cast<int64_t>(first_chunk) + num_chunks > chunks) return MOE_ERR_INVALID_ARG;
+  SealedLayout SL;
+  st = check_sealed_workspace(d, total_tokens, workspace, workspace_bytes, &SL);
+  if (st != MOE_OK) return st;
+  int64_t ticks = 0;
+  if (!ring_ticks(timeout_us, &ticks)) return MOE_ERR_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ring->base);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const Layout L = make_layout(d, total_tokens);
+  const int H = d.hidden, k = d.top_k;
+  const bool with_dec = layer_writes_x_dec(static_cast<int64_t>(total_tokens) * k);
+  for (int64_t n = first_chunk; n < first_chunk + num_chunks; ++n) {
+    const int64_t slot = n % S;
+    const int32_t valid = static_cast<int32_t>(std::min<int64_t>(C, total_tokens - n * C));
+    RingSlot* rs = ring_slots(ring, RL) + slot;
+    if (launch_ring_wait(&rs->route_ready, &rs->layout_ready, &rs->consumer_seq, 1u, ticks,
+                         ring_status(ring, RL), MOE_RING_CONSUMER_TIMEOUT, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(base + RL.x) + slot * C * H;
+    const int32_t* ids = reinterpret_cast<const int32_t*>(base + RL.expert_ids) + slot * C * k;
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(base + RL.route_weights) + slot * C * k;
+    const int64_t t0 = n * C;
+    // the chunk's tokens are rows t0 .. of the stream's batch: quantized in place, and
+    // their ids and route weights copied out of the slot before it is released
+    uint16_t* dec = with_dec ? reinterpret_cast<uint16_t*>(ws + L.pub.x_dec) + t0 * H : nullptr;
+    if (launch_quantize_nvfp4(x, 1, valid, H, qx, ws + L.pub.x_codes + t0 * (H / 2),
+                              ws + L.pub.x_scales + t0 * (H / kGroup), dec, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (hipMemcpyAsync(ws + SL.ids + t0 * k * 4, ids, static_cast<size_t>(valid) * k * 4,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(ws + SL.weights + t0 * k * 2, w, static_cast<size_t>(valid) * k * 2,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (launch_ring_publish(&rs->consumed, &rs->consumer_seq, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_seal(moe_dims_t d, int32_t total_tokens, const void* prepared,
+                              const float* alpha1, const float* qa, const float* alpha2,
+                              const float* situ_beta, const float* situ_linear_beta,
+                              void* workspace, size_t workspace_bytes, uint16_t* out,
+                              moe_stream_t stream) {
+  SealedLayout SL;
+  moe_status_t st = check_sealed_workspace(d, total_tokens, workspace, workspace_bytes, &SL);
+  if (st != MOE_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return forward_impl(d, total_tokens, nullptr, reinterpret_cast<const int32_t*>(ws + SL.ids),
+                      reinterpret_cast<const uint16_t*>(ws + SL.weights), prepared, nullptr,
+                      alpha1, qa, alpha2, situ_beta, situ_linear_beta, workspace, SL.layer_bytes, out,
+                      stream, nullptr, /*quantized=*/true);
 }
 
 moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,

@@ -1,4 +1,5 @@
-"""GPU tests of the chunk-streamed front end (moe_ring_* and moe_forward_streamed).
+"""GPU tests of the chunk-streamed front end (moe_ring_*, moe_forward_streamed, and
+moe_forward_absorb + moe_forward_seal).
 
 The streamed layer runs each token chunk as a layer call of its own; every token's result
 is computed exactly as in a whole-batch call (same kernels' per-row arithmetic, same K
@@ -69,6 +70,7 @@ class Ring:
         self.rw = b[self.lay["route_weights"]:self.lay["route_weights"] + slots * C * k * 2].view(
             torch.int16).view(slots, C, k)
         self.ws = empty_bytes(rm.moe_workspace_size(L.dims, C))
+        self.sws = empty_bytes(rm.moe_sealed_workspace_size(L.dims, CFG.T))
         self.out = torch.full((CFG.T, CFG.H), -1, dtype=torch.int16, device="cuda")
         rm.moe_ring_init(L.dims, self.ring)
 
@@ -98,6 +100,15 @@ class Ring:
                                 L.qa, L.alpha2, L.beta, L.lam, self.ws, self.out,
                                 timeout_us=timeout_us, stream=stream)
 
+    def absorb(self, T, first, num, stream=None, timeout_us=0):
+        rm.moe_forward_absorb(self.L.dims, self.ring, T, first, num, self.L.qx, self.sws,
+                              timeout_us=timeout_us, stream=stream)
+
+    def seal(self, T, stream=None):
+        L = self.L
+        rm.moe_forward_seal(L.dims, T, L.prepared, L.alpha1, L.qa, L.alpha2, L.beta, L.lam,
+                            self.sws, self.out, stream=stream)
+
     def status(self):
         torch.cuda.synchronize()
         st = self.lay["status"]
@@ -107,6 +118,7 @@ class Ring:
         torch.cuda.synchronize()
         assert torch.all(self.buf[self.lay["total"]:] == 0xA5), "ring guard overwritten"
         check_guard(self.ws)
+        check_guard(self.sws)
 
 
 @pytest.mark.parametrize("C", [1, 7, 64, 200, 256])
@@ -218,6 +230,94 @@ def test_streamed_graph_replay(layer):
     R.check()
 
 
+@pytest.mark.parametrize("C", [1, 7, 64, 200, 256])
+def test_sealed_serialized_equals_batch(layer, C):
+    """Scheduling option 2: all chunks produced into a ring with a slot per chunk,
+    absorbed in one call, then sealed: the batch call's result bit for bit."""
+    _say(f"sealed serialized C={C}")
+    p, L, batch = layer
+    n = (CFG.T + C - 1) // C
+    R = Ring(L, n, C)
+    for i in range(n):
+        R.produce(i, CFG.T)
+    R.absorb(CFG.T, 0, n)
+    R.seal(CFG.T)
+    assert R.status() == rm.MOE_RING_OK
+    R.check()
+    assert np.array_equal(host(R.out, np.uint16), batch)
+
+
+def test_sealed_one_slot_alternating(layer):
+    """Produce and absorb alternate chunk by chunk through one slot (the slot is released
+    by every absorb before the stream ends), then one seal."""
+    _say("sealed one slot alternating")
+    p, L, batch = layer
+    R = Ring(L, 1, 16)
+    n = R.chunks(CFG.T)
+    for i in range(n):
+        R.produce(i, CFG.T, parts=("layout", "route") if i % 2 else ("route", "layout"))
+        R.absorb(CFG.T, i, 1)
+    R.seal(CFG.T)
+    assert R.status() == rm.MOE_RING_OK
+    R.check()
+    assert np.array_equal(host(R.out, np.uint16), batch)
+
+
+def test_sealed_producer_and_consumer_on_two_streams(layer):
+    """Producer and consumer on two streams through a two-slot ring, enqueued chunk by
+    chunk (the progress rule), the seal on the consumer's stream."""
+    _say("sealed two streams")
+    p, L, batch = layer
+    R = Ring(L, 2, 16)
+    n = R.chunks(CFG.T)
+    torch.cuda.synchronize()
+    cons, prod = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(n):
+        R.produce(i, CFG.T, stream=prod, timeout_us=10_000_000)
+        R.absorb(CFG.T, i, 1, stream=cons, timeout_us=10_000_000)
+    R.seal(CFG.T, stream=cons)
+    torch.cuda.synchronize()
+    assert R.status() == rm.MOE_RING_OK
+    R.check()
+    assert np.array_equal(host(R.out, np.uint16), batch)
+
+
+def test_sealed_graph_replay(layer):
+    """Production, absorption and the seal of all chunks captured into one graph (two-slot
+    ring); every replay must equal a batch call on the current source tokens."""
+    _say("sealed graph replay")
+    p, L, batch = layer
+    R = Ring(L, 2, 32)
+    n = R.chunks(CFG.T)
+    src_x = L.x.clone()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(n):
+            R.produce(i, CFG.T, src=(src_x, L.ids, L.rw), stream=s)
+            R.absorb(CFG.T, i, 1, stream=s)
+        R.seal(CFG.T, stream=s)
+    rng = np.random.default_rng(6)
+    for rep in range(4):
+        if rep % 2:
+            perm = torch.from_numpy(rng.permutation(CFG.T)).cuda()
+            src_x.copy_(L.x[perm])
+        else:
+            src_x.copy_(L.x)
+        R.out.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert R.status() == rm.MOE_RING_OK, f"replay {rep}"
+        got = host(R.out, np.uint16)
+        ref_out = torch.empty_like(L.out)
+        rm.moe_forward(L.dims, CFG.T, src_x, L.ids, L.rw, L.prepared, L.qx, L.alpha1, L.qa,
+                       L.alpha2, L.beta, L.lam, L.workspace, ref_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, host(ref_out, np.uint16)), f"replay {rep}"
+    R.check()
+
+
 def test_wait_timeouts_set_status_and_return(layer):
     """Time-outs forced from the host with a 2 ms limit: a consumer waiting on a slot
     nobody publishes, and a producer re-acquiring a slot the consumer never freed."""
@@ -267,6 +367,48 @@ def test_streamed_chunks_take_other_kernels_than_the_batch():
             rm.moe_ring_publish(L.dims, ring, s, role)
         rm.moe_forward_streamed(L.dims, ring, cfg.T, i, 1, L.prepared, L.qx, L.alpha1, L.qa,
                                 L.alpha2, L.beta, L.lam, ws, out)
+    torch.cuda.synchronize()
+    st = lay["status"]
+    assert int(buf[st:st + 4].view(torch.int32).item()) == rm.MOE_RING_OK
+    check_guard(ws)
+    got = host(out, np.uint16)
+    diff = np.nonzero(np.any(got != batch, axis=1))[0]
+    assert diff.size == 0, f"{diff.size} rows differ, first {diff[:5]}"
+
+
+def test_sealed_many_rows_equals_batch():
+    """T*k = 65536 routed rows sealed from chunks of 5000 tokens through a two-slot ring:
+    the seal takes the many-rows kernels (no f16 copy of x), like the batch call, and must
+    equal it bit for bit."""
+    _say("sealed many rows")
+    cfg = LayerConfig(name="stream_T16384_H256_I128_E16_k4", T=16384, H=256, I=128, E=16, k=4,
+                      w_std=0.05, seed_index=61)
+    p = build_layer_problem(cfg, calib_tokens=np.arange(8))
+    prepared = prepare(cfg, p["w13"], p["w13_sf"], p["w2"], p["w2_sf"])
+    L = DeviceLayer(p, prepared)
+    batch = host(L.forward().clone(), np.uint16)
+    C = 5000
+    n = (cfg.T + C - 1) // C
+    lay = rm.moe_ring_layout(L.dims, 2, C)
+    buf = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    ring = rm.make_ring(buf, 2, C)
+    rm.moe_ring_init(L.dims, ring)
+    x = buf[lay["x"]:].view(torch.int16)[:2 * C * cfg.H].view(2, C, cfg.H)
+    ids = buf[lay["expert_ids"]:].view(torch.int32)[:2 * C * cfg.k].view(2, C, cfg.k)
+    rw = buf[lay["route_weights"]:].view(torch.int16)[:2 * C * cfg.k].view(2, C, cfg.k)
+    ws = empty_bytes(rm.moe_sealed_workspace_size(L.dims, cfg.T))
+    out = torch.full((cfg.T, cfg.H), -1, dtype=torch.int16, device="cuda")
+    for i in range(n):
+        s, lo, hi = i % 2, i * C, min(cfg.T, (i + 1) * C)
+        for role, parts in ((rm.MOE_RING_ROUTE, ((ids, L.ids), (rw, L.rw))),
+                            (rm.MOE_RING_LAYOUT, ((x, L.x),))):
+            rm.moe_ring_acquire(L.dims, ring, s, role)
+            for dst, src in parts:
+                dst[s, :hi - lo].copy_(src[lo:hi])
+            rm.moe_ring_publish(L.dims, ring, s, role)
+        rm.moe_forward_absorb(L.dims, ring, cfg.T, i, 1, L.qx, ws)
+    rm.moe_forward_seal(L.dims, cfg.T, L.prepared, L.alpha1, L.qa, L.alpha2, L.beta, L.lam, ws,
+                        out)
     torch.cuda.synchronize()
     st = lay["status"]
     assert int(buf[st:st + 4].view(torch.int32).item()) == rm.MOE_RING_OK

@@ -68,6 +68,44 @@ def test_ring_calls_validate_before_any_hip_call():
         assert ei.value.status == code
 
 
+def test_sealed_calls_validate_before_any_hip_call():
+    """moe_forward_absorb / moe_forward_seal (scheduling option 2) reject bad arguments on
+    the host; the sealed workspace holds the layer's workspace for the whole stream plus
+    its expert ids and route weights."""
+    T, k = 20, D.top_k
+    ws = rm.moe_sealed_workspace_size(D, T)
+    assert ws >= rm.moe_workspace_size(D, T) + T * k * 4 + T * k * 2
+    assert rm.moe_sealed_workspace_size(D, 2 * T) > ws
+    for bad in (0, rm.MOE_MAX_TOKENS + 1):
+        with pytest.raises(rm.MoeError) as ei:
+            rm.moe_sealed_workspace_size(D, bad)
+        assert ei.value.status == -1
+    lay = rm.moe_ring_layout(D, 2, 8)
+    good = rm.MoeRing(1 << 20, lay["total"], 2, 8)
+    absorb = dict(dims=D, ring=good, total_tokens=T, first_chunk=0, num_chunks=3, qx=256,
+                  workspace=1 << 26, workspace_bytes=ws, stream=0)
+    seal = dict(dims=D, total_tokens=T, prepared=1 << 24, alpha1=512, qa=768, alpha2=1024,
+                situ_beta=None, situ_linear_beta=None, workspace=1 << 26, out=1 << 28,
+                workspace_bytes=ws, stream=0)
+    cases = []
+    for kw, code in ((dict(num_chunks=4), -1), (dict(first_chunk=3, num_chunks=1), -1),
+                     (dict(total_tokens=0), -1), (dict(qx=None), -1),
+                     (dict(workspace_bytes=ws - 1), -3), (dict(workspace=(1 << 26) + 16), -1),
+                     (dict(ring=rm.MoeRing(1 << 20, lay["total"] - 1, 2, 8)), -3),
+                     (dict(dims=rm.MoeDims(200, 64, 16, 4)), -2)):
+        a = dict(absorb); a.update(kw)
+        cases.append((lambda a=a: rm.moe_forward_absorb(**a), code))
+    for kw, code in ((dict(total_tokens=0), -1), (dict(workspace_bytes=ws - 1), -3),
+                     (dict(workspace=None), -1), (dict(out=(1 << 28) + 8), -1),
+                     (dict(prepared=None), -1), (dict(dims=rm.MoeDims(200, 64, 16, 4)), -2)):
+        a = dict(seal); a.update(kw)
+        cases.append((lambda a=a: rm.moe_forward_seal(**a), code))
+    for fn, code in cases:
+        with pytest.raises(rm.MoeError) as ei:
+            fn()
+        assert ei.value.status == code
+
+
 class RingModel:
     def __init__(self, S):
         self.S = S
