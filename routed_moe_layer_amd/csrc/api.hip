@@ -624,10 +624,10 @@ moe_status_t moe_forward_absorb(moe_dims_t d, const moe_ring_t* ring, int32_t to
     if (launch_quantize_nvfp4(x, 1, valid, H, qx, ws + L.pub.x_codes + t0 * (H / 2),
                               ws + L.pub.x_scales + t0 * (H / kGroup), dec, s) != hipSuccess)
       return MOE_ERR_HIP;
-    if (hipMemcpyAsync(ws + SL.ids + t0 * k * 4, ids, static_cast<size_t>(valid) * k * 4,
-                       hipMemcpyDeviceToDevice, s) != hipSuccess ||
-        hipMemcpyAsync(ws + SL.weights + t0 * k * 2, w, static_cast<size_t>(valid) * k * 2,
-                       hipMemcpyDeviceToDevice, s) != hipSuccess)
+    if (launch_slot_copy(ws + SL.ids + t0 * k * 4, ids, static_cast<int64_t>(valid) * k * 4,
+                         s) != hipSuccess ||
+        launch_slot_copy(ws + SL.weights + t0 * k * 2, w, static_cast<int64_t>(valid) * k * 2,
+                         s) != hipSuccess)
       return MOE_ERR_HIP;
     if (launch_ring_publish(&rs->consumed, &rs->consumer_seq, s) != hipSuccess)
       return MOE_ERR_HIP;

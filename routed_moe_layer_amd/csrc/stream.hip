@@ -17,6 +17,8 @@
 // ends, so a missing publish never leaves a wave spinning.  Publishes are system-scope
 // release stores issued after the payload writes that precede them on the same stream.
 #include "common.h"
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace rmoe {
@@ -60,6 +62,26 @@ __global__ __launch_bounds__(64) void ring_publish_kernel(uint32_t* gen, uint32_
   const uint32_t v = *seq + 1u;
   *seq = v;
   __hip_atomic_store(gen, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Copy of a slot's expert ids or route weights into the stream's rows (sealed scheduling),
+// in 2-byte units, so that the slot can be released before the stream ends.
+__global__ __launch_bounds__(256) void slot_copy_kernel(uint16_t* __restrict__ dst,
+                                                        const uint16_t* __restrict__ src,
+                                                        int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride)
+    dst[i] = src[i];
+}
+
+hipError_t launch_slot_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t n = bytes / 2;
+  if (n <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((n + 255) / 256, 1024);
+  slot_copy_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream>>>(
+      static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_ring_init(uint32_t* words, int n, hipStream_t stream) {
