@@ -576,10 +576,16 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  if (rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
+  // (from kManyRows on there is no f16 copy of x: FC1's fallback slabs stage codes too)
+  const bool big_slabs = rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
+  if (kRows && many) {
+    if (big_slabs) launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
+    else launch_variant<MODE, 4, 2, kBigRows, 1, false>(a, a.max_big, 1, stream);
+  } else if (big_slabs) {
     launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE, kRows>(a, a.max_big, 1, stream);
-  else
+  } else {
     launch_variant<MODE, 4, 2, kBigRows, 1, kRows>(a, a.max_big, 1, stream);
+  }
   return hipGetLastError();
 }
 

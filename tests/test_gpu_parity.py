@@ -264,6 +264,10 @@ EDGE = [
     # copy of x at this size) beside a 4081-row expert
     ("many_rows_small_tiles", _edge("edge_many_small", T=4096, E=512, k=16, H=256, I=128,
                                     zipf_s=1.2, seed_index=43), None),
+    # 65536 routed rows with H not a multiple of 256 and I not of 128: the token-resident
+    # FC2 on 128-column slabs, FC2's reduction padded from 192 to 256
+    ("many_rows_fallback_shapes", _edge("edge_fallback", T=16384, E=16, k=4, H=384, I=192,
+                                        seed_index=44), None),
 ]
 
 
