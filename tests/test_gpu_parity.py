@@ -268,6 +268,12 @@ EDGE = [
     # FC2 on 128-column slabs, FC2's reduction padded from 192 to 256
     ("many_rows_fallback_shapes", _edge("edge_fallback", T=16384, E=16, k=4, H=384, I=192,
                                         seed_index=44), None),
+    # I > 384: FC2 through the grouped kernel for both tile lists; I=576 pads FC2's
+    # reduction to 640 (zero codes and scales past I)
+    ("wide_I_small_tiles", _edge("edge_wideI_s", T=64, E=64, k=4, H=256, I=576,
+                                 seed_index=45), None),
+    ("wide_I_big_tiles", _edge("edge_wideI_b", T=100, E=8, k=4, H=384, I=512,
+                               seed_index=46), None),
 ]
 
 
