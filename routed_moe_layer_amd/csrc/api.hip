@@ -404,6 +404,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   b.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
   b.runs = reinterpret_cast<TileDesc*>(ws + L.runs);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  b.small_only = R <= kSmallOnlyRows ? 1 : 0;
   b.amax_reset = a.a_amax;
   uint8_t* x_codes = ws + L.pub.x_codes;
   uint8_t* x_scales = ws + L.pub.x_scales;

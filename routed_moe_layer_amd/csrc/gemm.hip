@@ -570,6 +570,8 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   } else {
     launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
   }
+  // batches of at most kSmallOnlyRows routed rows have small tiles only
+  if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows) return hipGetLastError();
   if constexpr (MODE == 0) {
     if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
       launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);
@@ -593,6 +595,7 @@ hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream) { return launch_ge
 hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
   if (!fc2_resident_fits(a)) return launch_gemm<1>(a, stream);
   launch_fc2_resident_small(a, stream);
+  if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows) return hipGetLastError();
   // The resident kernel gives each big tile one workgroup; below about two big tiles per
   // CU that leaves the chip idle, and the grouped kernel (tiles x row slabs) is faster.
   if (static_cast<int64_t>(a.T) * a.k >= kManyRows) launch_fc2_resident_big(a, stream);

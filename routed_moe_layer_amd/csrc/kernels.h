@@ -40,7 +40,14 @@ inline bool layer_writes_x_dec(int64_t R) { return R < kManyRows; }
 inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
 inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
 // Upper bounds of the list lengths for R routed rows over E experts.
-inline int64_t max_small_tiles(int64_t R, int E) { return R < E ? R : E; }
+// Batches of at most kSmallOnlyRows routed rows take small tiles only (an expert with more
+// than kSmallRows rows gets several), so their GEMMs need no big-tile launches.
+constexpr int64_t kSmallOnlyRows = 1024;
+inline int64_t max_small_tiles(int64_t R, int E) {
+  // (the second term stays at its largest value above kSmallOnlyRows, so the bound, and
+  // the workspace, never shrink as R grows)
+  return (R < E ? R : E) + (R < kSmallOnlyRows ? R : kSmallOnlyRows) / kSmallRows;
+}
 inline int64_t max_big_tiles(int64_t R, int E) {
   const int64_t big_experts = R / (kSmallRows + 1);
   return R / kBigTileRows + (big_experts < E ? big_experts : E);
@@ -64,6 +71,7 @@ struct RouteBuffers {
   TileDesc* tiles_small;     // [max_small_tiles] or null
   TileDesc* tiles_big;       // [max_big_tiles] or null
   TileDesc* runs;            // [max_big_tiles] FC2 runs (needs the tile lists) or null
+  int small_only;            // every tile a small one (layer batches of <= kSmallOnlyRows rows)
   int32_t* num_tiles;        // [2] small, big (or [3] with runs); or null
   float* amax_reset;         // [E] zeroed by the scan kernel, or null
   int32_t* key_value;        // [kv_rows, 2]: (expert id, count) of the experts with a

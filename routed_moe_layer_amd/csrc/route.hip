@@ -97,10 +97,17 @@ __device__ uint64_t block_excl_scan64(uint64_t v, uint64_t* sh, uint64_t* total)
 }
 
 // Token tiles of one expert with `cnt` rows: (number of tiles, rows per tile but the last).
-__device__ __forceinline__ void expert_tiles(int cnt, int* n_small, int* n_big, int* base) {
+// With small_only every tile is a small one (at most kSmallRows rows).
+__device__ __forceinline__ void expert_tiles(int cnt, bool small_only, int* n_small,
+                                             int* n_big, int* base) {
   *n_small = 0; *n_big = 0; *base = 0;
   if (cnt <= 0) return;
   if (cnt <= kSmallRows) { *n_small = 1; *base = cnt; return; }
+  if (small_only) {
+    *n_small = (cnt + kSmallRows - 1) / kSmallRows;
+    *base = kSmallRows;
+    return;
+  }
   const int nb = (cnt + kBigTileRows - 1) / kBigTileRows;
   const int b = min(kBigTileRows, ((cnt + nb - 1) / nb + 15) / 16 * 16);
   *base = b;
@@ -117,7 +124,7 @@ __device__ void scan_experts_round(const RouteBuffers& b, int E, int e, int cnt,
                                    int* carry, int32_t* off_sh) {
   const bool lists = b.tiles_small != nullptr;
   int n_small, n_big, base;
-  expert_tiles(lists ? cnt : 0, &n_small, &n_big, &base);
+  expert_tiles(lists ? cnt : 0, b.small_only != 0, &n_small, &n_big, &base);
   if (b.key_value) n_small = cnt > 0 ? 1 : 0;
   uint64_t tot;
   const uint64_t ex = block_excl_scan64(pack_counts(cnt, n_small, n_big), sh, &tot);
@@ -131,7 +138,8 @@ __device__ void scan_experts_round(const RouteBuffers& b, int E, int e, int cnt,
     if (n_small) {
       const int slot = carry[1] + sexcl;
       if (lists) {
-        b.tiles_small[slot] = TileDesc{e, off, cnt, 0};
+        for (int j = 0; j < n_small; ++j)
+          b.tiles_small[slot + j] = TileDesc{e, off + j * base, min(base, cnt - j * base), 0};
       } else {
         b.key_value[2 * slot] = e + b.e_base;
         b.key_value[2 * slot + 1] = cnt;

@@ -248,7 +248,7 @@ EDGE = [
                        seed_index=37), None),
     ("wide_H", _edge("edge_wideH", T=8, H=1024, I=192, E=16, k=6, seed_index=38), None),
     # several 100-row big tiles per expert through the 64-row-per-wave FC1 (2I % 256 == 0)
-    ("big_tiles", _edge("edge_big", T=200, E=4, k=4, H=256, I=128, seed_index=39), None),
+    ("big_tiles", _edge("edge_big", T=300, E=4, k=4, H=256, I=128, seed_index=39), None),
     # T*k = 65536 routed rows: FC2 big tiles take the LDS-resident kernel
     ("resident_fc2", _edge("edge_res", T=16384, E=16, k=4, H=256, I=128, seed_index=40),
      None),
@@ -272,8 +272,12 @@ EDGE = [
     # reduction to 640 (zero codes and scales past I)
     ("wide_I_small_tiles", _edge("edge_wideI_s", T=64, E=64, k=4, H=256, I=576,
                                  seed_index=45), None),
-    ("wide_I_big_tiles", _edge("edge_wideI_b", T=100, E=8, k=4, H=384, I=512,
+    ("wide_I_big_tiles", _edge("edge_wideI_b", T=300, E=8, k=4, H=384, I=512,
                                seed_index=46), None),
+    # at most 1024 routed rows the tiles are all small ones: an expert with 90 rows is
+    # split into 32-row tiles, and no big-tile kernel is launched
+    ("small_batch_split_experts", _edge("edge_split", T=90, E=4, k=2, H=256, I=128,
+                                        seed_index=47), None),
 ]
 
 
