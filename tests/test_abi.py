@@ -48,6 +48,19 @@ def test_workspace_size_is_monotone_and_covers_the_layout():
     assert rm.moe_workspace_size(FULL, 16384) < 4 * 2 ** 30
 
 
+def test_workspace_size_is_monotone_at_every_T_near_the_tile_thresholds():
+    # small H and I with many experts, so the tile-list bounds weigh in the layout: every
+    # T around 1024 routed rows (small tiles only at or below it) keeps the size monotone,
+    # so a workspace sized for max_tokens covers every smaller call
+    d = rm.MoeDims(128, 64, 4096, 4)
+    prev = 0
+    for T in list(range(1, 41)) + list(range(240, 272)):
+        n = rm.moe_workspace_size(d, T)
+        assert n >= prev, T
+        prev = n
+        assert rm.moe_workspace_layout(d, T)["total"] == n
+
+
 def test_prepared_size_matches_the_page_storage_shapes():
     # FC1 [896,768,1792] + [896,768,224], FC2 [896,3584,192] + [896,3584,24]: I = 384 is
     # a multiple of 128, so the prepared layout is exactly as large as the canonical one.
