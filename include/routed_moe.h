@@ -376,7 +376,8 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring /*host*/,
  * result equals moe_forward on the whole stream bit for bit.
  *
  * workspace: moe_sealed_workspace_size(d, total_tokens) bytes, 256-byte aligned (device),
- * the same buffer for every absorb call and the seal of one stream; its first
+ * the same buffer and the same total_tokens for every absorb call and the seal of one
+ * stream; every chunk of the stream must be absorbed before the seal.  Its first
  * moe_workspace_size(d, total_tokens) bytes hold moe_forward's workspace layout for
  * total_tokens tokens (moe_workspace_layout) after the seal. */
 moe_status_t moe_sealed_workspace_size(moe_dims_t d, int32_t total_tokens,
