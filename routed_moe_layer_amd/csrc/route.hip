@@ -8,12 +8,15 @@
 // availableIdxNum is the in-range count), the count and key_value histogram modes, and
 // drop/pad slots e*capacity + rank (-1 past the capacity).
 //
-// Three launches (one for at most kRouteTile ids, see route_small_kernel), no host
+// Three launches (four above 64 tiles; one for at most kRouteTile ids, see
+// route_small_kernel), no host
 // readback ("Cake SiTU backend", intro: routing values never take part in host dispatch):
 //   hist    : one workgroup per tile of 1024 flat ids; LDS histogram -> tile_hist[tile][e].
-//   scan    : one workgroup; per expert, exclusive scan of tile_hist over tiles (in place),
-//             counts, exclusive/inclusive expert offsets; optionally the two grouped-GEMM
-//             work lists (small and big token tiles) and a reset of the SiTU amax stats.
+//   scan    : per expert, exclusive scan of tile_hist over tiles (in place; above 64 tiles
+//             by a column kernel with one workgroup per 64 experts) and the counts; then
+//             one workgroup: exclusive/inclusive expert offsets, optionally the grouped-GEMM
+//             work lists (small and big token tiles, FC2 runs), and a reset of the SiTU
+//             amax stats.
 //   scatter : one workgroup per tile; each wave ranks its 256 ids stably with ballot-based
 //             key matching (one ballot per key bit), waves are ordered through an LDS
 //             per-wave histogram, and every id lands at
@@ -186,7 +189,71 @@ __device__ void scan_experts_finish(const RouteBuffers& b, int E, const int* car
     }
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int ntiles, int E) {
+// Column scan for many tiles: workgroup c owns experts [64c, 64c + 64) (one per lane); its
+// 16 waves split the tiles into 16 contiguous ranges, sum them, take the exclusive prefix
+// over waves in LDS, and rewrite their tile histograms in place as per-tile bases
+// (exclusive over tiles) while the last wave writes the expert counts.  Each thread has
+// one batch of loads in flight per range pass, where one workgroup walking all the tiles
+// of every expert waits ntiles / kScanBatch memory latencies.
+constexpr int kScanExperts = 64, kScanWaves = 16;
+constexpr int kColumnScanTiles = 64;        // above this many tiles the column scan runs
+
+__global__ __launch_bounds__(kScanExperts * kScanWaves) void route_colscan_kernel(
+    RouteBuffers b, int ntiles, int E) {
+  __shared__ int part[kScanWaves][kScanExperts];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int e = blockIdx.x * kScanExperts + lane;
+  const int per = (ntiles + kScanWaves - 1) / kScanWaves;
+  const int t0 = min(ntiles, w * per), t1 = min(ntiles, t0 + per);
+  int32_t* __restrict__ col = b.tile_hist + e;
+  int sum = 0;
+  int v[kScanBatch];
+  if (e < E) {
+    for (int tb = t0; tb < t1; tb += kScanBatch) {
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = tb + i < t1 ? col[static_cast<int64_t>(tb + i) * E] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) sum += v[i];
+    }
+  }
+  part[w][lane] = sum;
+  __syncthreads();
+  if (e >= E) return;
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += part[i][lane];
+  if (t1 - t0 <= kScanBatch) {
+    // one batch: its values are still in v
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (t0 + i < t1) {
+        col[static_cast<int64_t>(t0 + i) * E] = base;
+        base += v[i];
+      }
+  } else {
+    for (int tb = t0; tb < t1; tb += kScanBatch) {
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = tb + i < t1 ? col[static_cast<int64_t>(tb + i) * E] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (tb + i < t1) {
+          col[static_cast<int64_t>(tb + i) * E] = base;
+          base += v[i];
+        }
+    }
+  }
+  if (w == kScanWaves - 1) {
+    b.counts[e] = base;
+    if (b.amax_reset) b.amax_reset[e] = 0.0f;
+  }
+}
+
+// The expert scan (one workgroup).  With `counted` the column scan has already turned the
+// tile histograms into bases and written the counts; otherwise each thread scans its
+// expert's tiles here first.
+__global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int ntiles, int E,
+                                                          int counted) {
   __shared__ uint64_t sh[16];
   __shared__ int carry[4];
   if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; carry[3] = 0; }
@@ -196,7 +263,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int nt
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x;
     int cnt = 0;
-    if (e < E) {
+    if (e < E && counted) {
+      cnt = b.counts[e];
+    } else if (e < E) {
       // exclusive over tiles, in place; kScanBatch independent loads in flight per step
       for (int t0 = 0; t0 < ntiles; t0 += kScanBatch) {
         int v[kScanBatch];
@@ -507,7 +576,11 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
   }
   route_hist_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
       ids, n, E, b.e_base, b.tile_hist);
-  route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(b, nt, E);
+  const int counted = nt > kColumnScanTiles ? 1 : 0;
+  if (counted)
+    route_colscan_kernel<<<dim3((E + kScanExperts - 1) / kScanExperts),
+                           dim3(kScanExperts * kScanWaves), 0, stream>>>(b, nt, E);
+  route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(b, nt, E, counted);
   route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
                          (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
       ids, n, E, bits_for(E), b);
