@@ -67,19 +67,15 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return v[0];
 }
 
-// E2M1 code of an fp32 value: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
-// saturating at 6; bit 3 carries the sign of y (so -0 and small negatives give 0x8).
-// On [0,2) the grid is code/2, so the code is rint(2a); on [2,4) it is code-2, so the
-// code is 4 + rint(a-2) (a-2 is exact there); above 4 only 4 (code 6) and 6 (code 7)
-// remain, split at the tie 5 which goes to the even code 6.  rint rounds half to even,
-// which is the even-code rule because the codes are consecutive on each piece.
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  const float a = fabsf(y);
-  uint32_t c;
-  if (a < 2.0f) c = static_cast<uint32_t>(rintf(a + a));
-  else if (a < 4.0f) c = 4u + static_cast<uint32_t>(rintf(a - 2.0f));
-  else c = a > 5.0f ? 7u : 6u;
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+// E2M1 codes of two fp32 values into byte SEL of w (the first value in the low nibble):
+// the nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating at 6 (also for
+// infinities), the sign in bit 3 (-0 and small negatives give 0x8).  gfx950's packed
+// conversion with scale 1 implements exactly this rule: on every non-NaN fp32 input it
+// gives the same code as the piecewise form (rint(2a) on [0,2), 4 + rint(a-2) on [2,4),
+// then 6 up to the tie at 5 and 7 above), checked over all 2^32 bit patterns on the GPU.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
 }
 
 // Group-16 NVFP4 quantization of one block with global encoding scale q:
@@ -96,8 +92,10 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float q, float
 
 __device__ __forceinline__ uint32_t pack8_codes(const float* v, float enc) {
   uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_encode(v[i] * enc) << (4 * i);
+  w = e2m1_pack2<0>(w, v[0] * enc, v[1] * enc);
+  w = e2m1_pack2<1>(w, v[2] * enc, v[3] * enc);
+  w = e2m1_pack2<2>(w, v[4] * enc, v[5] * enc);
+  w = e2m1_pack2<3>(w, v[6] * enc, v[7] * enc);
   return w;
 }
 

@@ -382,8 +382,9 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
         if (valid) wave_amax = fmaxf(wave_amax, m);
         float enc;
         const uint32_t sb = nvfp4_block_scale(m, qa, &enc);
-        const uint32_t b0 = e2m1_encode(av[0] * enc) | (e2m1_encode(av[1] * enc) << 4);
-        const uint32_t b1 = e2m1_encode(av[2] * enc) | (e2m1_encode(av[3] * enc) << 4);
+        const uint32_t w2 =
+            e2m1_pack2<1>(e2m1_pack2<0>(0u, av[0] * enc, av[1] * enc), av[2] * enc, av[3] * enc);
+        const uint32_t b0 = w2 & 0xFFu, b1 = (w2 >> 8) & 0xFFu;
         const int blk = (G0 >> 1) + p;
         if (valid) {
           uint8_t* ac = a.a_codes + row * (a.I / 2) + 8 * blk;
