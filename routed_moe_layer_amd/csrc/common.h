@@ -42,24 +42,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// E4M3 byte of a non-negative finite fp32 scale: clamp to 448, then round to nearest even.
-// Subnormal range (< 2^-6): multiples of 2^-9.  Normal range: 3 mantissa bits.
-__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float s) {
-  s = fminf(s, 448.0f);
-  if (s < 0.015625f) {                              // 2^-6, smallest normal E4M3
-    return static_cast<uint32_t>(rintf(s * 512.0f));  // exact scaling; rintf is half-even
-  }
-  uint32_t u = __float_as_uint(s);
-  int32_t e = static_cast<int32_t>(u >> 23) - 127;  // -6 .. 8
-  uint32_t m = u & 0x7FFFFFu;
-  uint32_t r = m >> 20;                             // top 3 mantissa bits
-  uint32_t rem = m & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-  if (r == 8u) { r = 0u; ++e; }
-  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | r;
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
 // fp32 value of an E4M3 byte (the byte's sign is ignored: block scales are >= 0).
 // gfx950's fp8 conversion is the OCP E4M3 ("fn") format.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
@@ -82,10 +64,19 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
 // s = E4M3(min(fp32(fp32(amax*q)/6), 448)); enc = q/s (0 if s == 0);
 // code_i = E2M1(fp32(v_i*enc)).  Returns the scale byte; codes packed two per byte,
 // element 2b in the low nibble of byte b (codes_lo: elements 0..7, codes_hi: 8..15).
+// The E4M3 byte rounds to nearest even after the clamp to 448 (subnormals in steps of
+// 2^-9): gfx950's fp32 -> E4M3 conversion does exactly that on [0, 448].  The quotient by
+// 6 is RN(1/6) times amax*q with one FMA correction of the residual; it can differ from the
+// IEEE quotient only where the scale byte is 0 either way.  Both facts were checked on the
+// GPU over every fp32 input (the byte equal to the IEEE quotient's software encode).
 __device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float q, float* enc_out) {
-  float s32 = (amax * q) / 6.0f;
-  uint32_t sb = e4m3_encode_nonneg(s32);
-  float s = e4m3_to_f32(sb);
+  constexpr float kSixth = 0.16666667163372040f;      // RN(1/6)
+  const float x = amax * q;
+  const float q0 = x * kSixth;
+  const float s32 = __builtin_fmaf(__builtin_fmaf(-6.0f, q0, x), kSixth, q0);
+  const uint32_t sb = static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(fminf(s32, 448.0f), 0.0f, 0, false)) & 0xFFu;
+  const float s = e4m3_to_f32(sb);
   *enc_out = (s == 0.0f) ? 0.0f : q / s;
   return sb;
 }
