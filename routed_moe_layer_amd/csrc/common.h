@@ -69,15 +69,24 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
 // 6 is RN(1/6) times amax*q with one FMA correction of the residual; it can differ from the
 // IEEE quotient only where the scale byte is 0 either way.  Both facts were checked on the
 // GPU over every fp32 input (the byte equal to the IEEE quotient's software encode).
-__device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float q, float* enc_out) {
+__device__ __forceinline__ uint32_t nvfp4_scale_byte(float amax, float q) {
   constexpr float kSixth = 0.16666667163372040f;      // RN(1/6)
   const float x = amax * q;
   const float q0 = x * kSixth;
   const float s32 = __builtin_fmaf(__builtin_fmaf(-6.0f, q0, x), kSixth, q0);
-  const uint32_t sb = static_cast<uint32_t>(
+  return static_cast<uint32_t>(
       __builtin_amdgcn_cvt_pk_fp8_f32(fminf(s32, 448.0f), 0.0f, 0, false)) & 0xFFu;
+}
+
+// The encode factor q/s of scale byte sb (0 when s is 0).
+__device__ __forceinline__ float nvfp4_encode_factor(uint32_t sb, float q) {
   const float s = e4m3_to_f32(sb);
-  *enc_out = (s == 0.0f) ? 0.0f : q / s;
+  return (s == 0.0f) ? 0.0f : q / s;
+}
+
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float q, float* enc_out) {
+  const uint32_t sb = nvfp4_scale_byte(amax, q);
+  *enc_out = nvfp4_encode_factor(sb, q);
   return sb;
 }
 

@@ -317,7 +317,8 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
 template <int MODE, int NW, int WRG, int BN, bool ROWS, int NCBA>
 __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
                                           const StageOf<MODE, NW, BN, ROWS>& st,
-                                          _Float16 (*s_tok)[BN * StageOf<MODE, NW, BN, ROWS>::kLdsRow]) {
+                                          _Float16 (*s_tok)[BN * StageOf<MODE, NW, BN, ROWS>::kLdsRow],
+                                          float* s_enc) {
   using Stage = StageOf<MODE, NW, BN, ROWS>;
   f32x4 acc[WRG][NCBA];
 #pragma unroll
@@ -358,6 +359,9 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
     // i = 8G + 2g.  Groups (2p, 2p+1) of the wave form NVFP4 group G0/2 + p.
     const float al = a.alpha1[e];
     const float qa = a.qa[e];
+    // the encode factor of every scale byte, once per tile (s_enc is read only below)
+    if (t.tid < 128) s_enc[t.tid] = nvfp4_encode_factor(t.tid, qa);
+    __syncthreads();
     const float beta = a.beta ? a.beta[e] : 4.0f;
     const float lam = a.lam ? a.lam[e] : 25.0f;
     const float ib = 1.0f / beta, il = 1.0f / lam;
@@ -380,8 +384,8 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         if (valid) wave_amax = fmaxf(wave_amax, m);
-        float enc;
-        const uint32_t sb = nvfp4_block_scale(m, qa, &enc);
+        const uint32_t sb = nvfp4_scale_byte(m, qa);
+        const float enc = s_enc[sb];
         const uint32_t w2 =
             e2m1_pack2<1>(e2m1_pack2<0>(0u, av[0] * enc, av[1] * enc), av[2] * enc, av[3] * enc);
         const uint32_t b0 = w2 & 0xFFu, b1 = (w2 >> 8) & 0xFFu;
@@ -426,6 +430,9 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   using Stage = StageOf<MODE, NW, BN, ROWS>;
   __shared__ _Float16 s_tok[2][BN * Stage::kLdsRow];
   __shared__ int64_t s_row[BN];
+  // FC1's requantization: the encode factor qa/s of every E4M3 scale byte s of this
+  // tile's expert, divided once per tile instead of once per 16-value block
+  __shared__ float s_enc[128];
 
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
   const int ntiles = a.num_tiles[big];
@@ -468,17 +475,17 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   // have compile-time trip counts (uniform branch per workgroup)
   const int ncb = (t.td.nrows + 15) / 16;
   if constexpr (BN == 32) {
-    if (ncb == 1) tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok);
-    else tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok);
+    if (ncb == 1) tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok, s_enc);
+    else tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok, s_enc);
   } else {
     switch (ncb) {
-      case 1: tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok); break;
-      case 2: tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok); break;
-      case 3: tile_body<MODE, NW, WRG, BN, ROWS, 3>(a, t, st, s_tok); break;
-      case 4: tile_body<MODE, NW, WRG, BN, ROWS, 4>(a, t, st, s_tok); break;
-      case 5: tile_body<MODE, NW, WRG, BN, ROWS, 5>(a, t, st, s_tok); break;
-      case 6: tile_body<MODE, NW, WRG, BN, ROWS, 6>(a, t, st, s_tok); break;
-      default: tile_body<MODE, NW, WRG, BN, ROWS, 7>(a, t, st, s_tok); break;   // kBigTileRows
+      case 1: tile_body<MODE, NW, WRG, BN, ROWS, 1>(a, t, st, s_tok, s_enc); break;
+      case 2: tile_body<MODE, NW, WRG, BN, ROWS, 2>(a, t, st, s_tok, s_enc); break;
+      case 3: tile_body<MODE, NW, WRG, BN, ROWS, 3>(a, t, st, s_tok, s_enc); break;
+      case 4: tile_body<MODE, NW, WRG, BN, ROWS, 4>(a, t, st, s_tok, s_enc); break;
+      case 5: tile_body<MODE, NW, WRG, BN, ROWS, 5>(a, t, st, s_tok, s_enc); break;
+      case 6: tile_body<MODE, NW, WRG, BN, ROWS, 6>(a, t, st, s_tok, s_enc); break;
+      default: tile_body<MODE, NW, WRG, BN, ROWS, 7>(a, t, st, s_tok, s_enc); break;   // kBigTileRows
     }
   }
 }
