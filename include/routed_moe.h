@@ -86,8 +86,11 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   expert_counts   i32 [E]   rows per expert;  expert_cumsum i32 [E] inclusive prefix sum
  *   a_codes   u8  [T*k, I/2]  requantized SiTU output, sorted row order
  *   a_scales  u8  [T*k, I/16]
- *   o_rows    bf16 [T*k, H]   FC2 output of routed row (t, j) at row t*k + j, alpha2
- *                             applied (rows of dropped ids are not written)
+ *   o_rows    f16  [T*k, H]   FC2 output O of routed row (t, j) at row t*k + j, alpha2
+ *                             applied, stored as O * 2^s with s the exponent of its
+ *                             32-column segment (rows of dropped ids are not written)
+ *   o_exp     i8   [T*k, H/32] s of each segment: the segment's largest |O| * 2^s lies
+ *                             in [2^14, 2^15] (s = 0 for an all-zero segment)
  *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
  *                             (0 for an expert with no rows; a calibration statistic) */
 typedef struct {
@@ -95,7 +98,7 @@ typedef struct {
   size_t sorted_ids, sorted_row_idx, expanded_row_idx;
   size_t expert_counts, expert_cumsum;
   size_t a_codes, a_scales;
-  size_t o_rows;
+  size_t o_rows, o_exp;
   size_t a_amax;
   size_t total;              /* bytes the call uses; <= moe_workspace_size(T) */
 } moe_workspace_layout_t;

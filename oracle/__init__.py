@@ -30,7 +30,9 @@ from .calib import (global_scale_from_amax, calibrate_layer, calibrate_tokens,
 from .routing import route, route_int8, route_v2, int8_static_quant
 from .router import topk_softmax
 from .layer import (situ, fc_exact, layer_forward, layer_forward_dense, token_forward,
+                    expert_rows, combine,
                     calibrate_intermediate, intermediate_amax,
+                    calibrate_intermediate_per_expert, intermediate_amax_per_expert,
                     expert_weights_decoded)
 
 __all__ = [
@@ -40,7 +42,9 @@ __all__ = [
     "global_scale_from_amax", "calibrate_layer", "calibrate_tokens", "calibrate_weights",
     "quantize_expert_stack",
     "calibrate_intermediate", "intermediate_amax",
+    "calibrate_intermediate_per_expert", "intermediate_amax_per_expert",
     "route", "route_int8", "route_v2", "int8_static_quant", "topk_softmax",
     "situ", "fc_exact", "layer_forward", "layer_forward_dense", "token_forward",
+    "expert_rows", "combine",
     "expert_weights_decoded",
 ]

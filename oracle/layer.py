@@ -91,8 +91,12 @@ def expert_weights_decoded(w13, w13_sf, w2, w2_sf, e):
     return w13d, w2d
 
 
-def _expert_rows(xdec_rows, w13d, w2d, alpha1_e, qA_e, alpha2_e, beta_e, lam_e):
-    """FC1 -> SiTU -> requant -> FC2 for the routed rows of one expert."""
+def expert_rows(xdec_rows, w13d, w2d, alpha1_e, qA_e, alpha2_e, beta_e, lam_e):
+    """FC1 -> SiTU -> requant -> FC2 for routed rows of one expert.
+
+    xdec_rows [R, H] float64 decoded NVFP4 token rows; w13d [2I, H], w2d [H, I] decoded
+    weights.  Returns h [R, 2I] (fp32 FC1 output after alpha1), a [R, I] (fp32 SiTU),
+    the requantized codes [R, I] and scales [R, I/16], and o [R, H] (fp32 FC2 output)."""
     I = w2d.shape[1]
     h = (fc_exact(xdec_rows, w13d) * np.float32(alpha1_e)).astype(np.float32)   # [R, 2I]
     g, u = h[:, :I], h[:, I:]
@@ -143,19 +147,29 @@ def layer_forward(x_bits, expert_ids, rw_bits, w13, w13_sf, w2, w2_sf,
         pos = np.arange(start, start + cnt)
         tok = r["sorted_row_idx"][pos].astype(np.int64) // k
         w13d, w2d = expert_weights_decoded(w13, w13_sf, w2, w2_sf, e)
-        h, a, ac, as_, o = _expert_rows(xdec[tok], w13d, w2d, alpha1[e], qA[e], alpha2[e],
+        h, a, ac, as_, o = expert_rows(xdec[tok], w13d, w2d, alpha1[e], qA[e], alpha2[e],
                                         beta_a[e], lam_a[e])
         h_all[pos], a_all[pos], ac_all[pos], as_all[pos], o_all[pos] = h, a, ac, as_, o
         start += cnt
-    wts = bf16_bits_to_f32(np.asarray(rw_bits, np.uint16)).astype(np.float64)
-    acc = np.zeros((T, H), np.float64)
     rows = r["expanded_row_idx"].reshape(T, k)
-    for j in range(k):
-        acc += wts[:, j:j + 1] * o_all[rows[:, j]].astype(np.float64)
+    acc = combine(o_all[rows], rw_bits)
     out = dict(r)
     out.update(x_codes=x_codes, x_scales=x_scales, h=h_all, a=a_all, a_codes=ac_all,
                a_scales=as_all, o=o_all, out_f64=acc, out=f64_to_bf16_bits(acc))
     return out
+
+
+def combine(o_tk, rw_bits):
+    """Finalization before the BF16 rounding: y[t] = sum_j w[t, j] * o[t, j] in j order,
+    float64.  o_tk [n, k, H] fp32 FC2 outputs of each token's k routed rows; rw_bits
+    [n, k] BF16 route weights (used as given).  The layer output is BF16(y), one
+    round-to-nearest-even (``f64_to_bf16_bits``)."""
+    o_tk = np.asarray(o_tk)
+    wts = bf16_bits_to_f32(np.asarray(rw_bits, np.uint16)).astype(np.float64)
+    acc = np.zeros((o_tk.shape[0], o_tk.shape[2]), np.float64)
+    for j in range(o_tk.shape[1]):
+        acc += wts[:, j:j + 1] * o_tk[:, j].astype(np.float64)
+    return acc
 
 
 def token_forward(tokens, x_bits, expert_ids, rw_bits, w13, w13_sf, w2, w2_sf,
@@ -194,7 +208,7 @@ def token_forward(tokens, x_bits, expert_ids, rw_bits, w13, w13_sf, w2, w2_sf,
             if e not in cache:
                 cache[e] = expert_weights_decoded(w13, w13_sf, w2, w2_sf, e)
             w13d, w2d = cache[e]
-            h, _, ac, as_, o = _expert_rows(xdec, w13d, w2d, alpha1[e], qA[e], alpha2[e],
+            h, _, ac, as_, o = expert_rows(xdec, w13d, w2d, alpha1[e], qA[e], alpha2[e],
                                             beta_a[e], lam_a[e])
             res["h"][i, j], res["a_codes"][i, j], res["a_scales"][i, j] = h[0], ac[0], as_[0]
             res["o"][i, j] = o[0]
@@ -212,26 +226,36 @@ def layer_forward_dense(x_bits, expert_ids, rw_bits, w13, w13_sf, w2, w2_sf,
                          qX, alpha1, qA, alpha2, beta, lam)
 
 
-def intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
-                      beta=None, lam=None, weight_cache=None):
-    """Largest |SiTU output| over the routed rows of the given tokens (calibration pass)."""
+def intermediate_amax_per_expert(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX,
+                                 alpha1, beta=None, lam=None, weight_cache=None):
+    """Largest |SiTU output| of each expert over the routed rows of the given tokens:
+    float32 [E], 0 for an expert none of those rows is routed to (calibration pass)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     E = w13.shape[0]
     I = w2.shape[2] * 2
     beta_a, lam_a = _situ_params(E, beta, lam)
-    cache = {} if weight_cache is None else weight_cache
     xc, xs = quantize_nvfp4(bf16_bits_to_f32(np.asarray(x_bits, np.uint16)[tokens]), np.float32(qX))
     xdec = dequantize_nvfp4(xc, xs)
-    amax = np.float32(0.0)
+    amax = np.zeros(E, np.float32)
     ids = np.asarray(expert_ids)[tokens]
     for e in np.unique(ids):
         rows = np.nonzero(np.any(ids == e, axis=1))[0]
-        if e not in cache:
-            cache[e] = expert_weights_decoded(w13, w13_sf, w2, w2_sf, e)
-        h = (fc_exact(xdec[rows], cache[e][0]) * np.float32(alpha1[e])).astype(np.float32)
+        if weight_cache is not None and e in weight_cache:
+            w13d = weight_cache[e][0]
+        else:
+            w13d = dequantize_nvfp4(unpack_nibbles(w13[e]), w13_sf[e])
+        h = (fc_exact(xdec[rows], w13d) * np.float32(alpha1[e])).astype(np.float32)
         a = situ(h[:, :I], h[:, I:], beta_a[e], lam_a[e])
-        amax = max(amax, np.float32(np.max(np.abs(a))))
-    return np.float32(amax)
+        amax[e] = np.float32(np.max(np.abs(a)))
+    return amax
+
+
+def intermediate_amax(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
+                      beta=None, lam=None, weight_cache=None):
+    """Largest |SiTU output| over the routed rows of the given tokens (calibration pass)."""
+    return np.float32(np.max(intermediate_amax_per_expert(
+        tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1, beta, lam,
+        weight_cache)))
 
 
 def calibrate_intermediate(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX, alpha1,
@@ -244,3 +268,17 @@ def calibrate_intermediate(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, q
                              beta, lam, weight_cache)
     d, q = global_scale_from_amax(amax)
     return np.full(E, d, np.float32), np.full(E, q, np.float32)
+
+
+def calibrate_intermediate_per_expert(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX,
+                                      alpha1, beta=None, lam=None, weight_cache=None):
+    """Per-expert intermediate scales: dA[e] = amax_e / 2688 with amax_e the largest
+    |SiTU output| of expert e's routed rows among the calibration tokens (the page's qA is
+    a float32 [E] tensor, one value per expert).  Reading taken: an expert with no routed
+    row in the calibration set takes the shared scale of the whole set.
+    Returns (dA [E], qA [E]) float32."""
+    per = intermediate_amax_per_expert(tokens, x_bits, expert_ids, w13, w13_sf, w2, w2_sf, qX,
+                                       alpha1, beta, lam, weight_cache)
+    shared = np.float32(np.max(per)) if per.size else np.float32(0.0)
+    d, q = global_scale_from_amax(np.where(per > 0, per, shared).astype(np.float32))
+    return np.asarray(d, np.float32), np.asarray(q, np.float32)

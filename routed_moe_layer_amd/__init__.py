@@ -88,7 +88,8 @@ class _RingLayout(ctypes.Structure):
 class _Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "x_codes", "x_scales", "x_dec", "sorted_ids", "sorted_row_idx", "expanded_row_idx",
-        "expert_counts", "expert_cumsum", "a_codes", "a_scales", "o_rows", "a_amax", "total")]
+        "expert_counts", "expert_cumsum", "a_codes", "a_scales", "o_rows", "o_exp", "a_amax",
+        "total")]
 
 
 _lib_handle = None

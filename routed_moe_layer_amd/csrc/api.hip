@@ -109,6 +109,7 @@ Layout make_layout(const moe_dims_t& d, int64_t T) {
   L.pub.a_codes = c.take(R * I / 2);
   L.pub.a_scales = c.take(R * I / 16);
   L.pub.o_rows = c.take(R * H * 2);
+  L.pub.o_exp = c.take(R * (H / 32));
   L.pub.a_amax = c.take(E * 4);
   L.pub.total = c.off;
   return L;
@@ -384,6 +385,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   a.a_scales = ws + L.pub.a_scales;
   a.a_amax = reinterpret_cast<float*>(ws + L.pub.a_amax);
   a.o_rows = reinterpret_cast<uint16_t*>(ws + L.pub.o_rows);
+  a.o_exp = reinterpret_cast<int8_t*>(ws + L.pub.o_exp);
   a.route_weights = route_weights;
   a.out = out;
 

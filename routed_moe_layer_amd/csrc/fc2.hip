@@ -3,12 +3,13 @@
 // "Cake SiTU backend" (intro; section "Prepared weights and scales"):
 //   o[r, h] = alpha2[e] * sum_i ahat[r, i] * w2hat[e, h, i],  i < I
 // with ahat the requantized SiTU output (NVFP4, decoded exactly to f16) and w2hat the FC2
-// weights; the result is stored as BF16 rows for the finalization.
+// weights; the result is stored as f16 rows with per-32-column exponents (store_out_block)
+// for the finalization.
 //
 // FC2's reduction is short (I = 384 at the page's shape), so a workgroup decodes its token
 // tile's full K range into LDS once, with a single barrier, and then sweeps a group of
 // weight slabs over it: no further barriers, the weight fragments of the next (slab,
-// chunk) stream into registers two steps ahead, and each slab's BF16 rows are stored as
+// chunk) stream into registers two steps ahead, and each slab's output rows are stored as
 // soon as its K loop ends.  Each wave owns WRG 16-row MFMA groups of every slab.
 #include <type_traits>
 
@@ -46,22 +47,18 @@ __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int l
 // The slabs [slab0, slab0 + nslabs) of one token tile; NCH = Ip/128 chunks per slab.
 // Steps q = (slab, chunk) run in order; step q decodes its register set, refills it with
 // step q+2 (two sets alternate, so no register copies of in-flight loads), runs the MFMAs
-// over the LDS-resident token tile and, after a slab's last chunk, stores the slab's BF16
-// rows.  Two slabs per loop trip keep the chunk index, the register set and the epilogue
-// compile-time; a slab's first K-step starts from a zero accumulator.
-// The output of one wave for one 16-token block and one slab, 16 rows x 16*WRG columns of
-// BF16, passes through a per-wave LDS buffer (rows padded by 8 elements) so that the
-// global stores are whole 16-byte pieces of consecutive columns: one store instruction
-// then covers 64/(2*WRG) token rows with 32*WRG contiguous bytes each, instead of 16 rows
-// with 32 bytes each in the MFMA output layout (the rows are scattered over the FC2
-// output, so fewer, longer runs per instruction cut the memory transactions 4x at WRG 4).
-template <int WRG>
-constexpr int fc2_out_stride() { return 16 * WRG + 8; }
-
+// over the LDS-resident token tile and, after a slab's last chunk, stores the slab's
+// output rows.  Two slabs per loop trip keep the chunk index, the register set and the
+// epilogue compile-time; a slab's first K-step starts from a zero accumulator.
+// The output of one wave for one 16-token block and one slab passes through a per-wave LDS
+// buffer (store_out_block): each lane then holds consecutive columns of one token row, so
+// the 32-column segments' exponents need no more than two lane exchanges and the global
+// stores are whole 16-byte pieces of consecutive columns (the rows are scattered over the
+// FC2 output, so longer runs per store instruction cut the memory transactions).
 template <int NW, int WRG, int BN, int NCBA, int NCH>
 __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
                                          int nslabs, const _Float16* __restrict__ s_tok,
-                                         uint16_t* __restrict__ s_out) {
+                                         float* __restrict__ s_out) {
   constexpr int kSlabGroups = NW * WRG;                 // 16-row groups per slab
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int e = td.expert;
@@ -76,7 +73,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
     const int n = min(cb * 16 + (lane & 15), td.nrows - 1);
     flat_cb[cb] = a.sorted_row_idx[td.row_start + n];
   }
-  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
+  float* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
   f32x4 acc[WRG][NCBA];
 
   auto decode = [&](const W2Regs<WRG>& cur, const int s, f16x8 (&wf)[WRG]) {
@@ -128,31 +125,13 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
     }
     if (c == NCH - 1) {
       const int G0 = j * kSlabGroups + w * WRG;
-      constexpr int kStride = fc2_out_stride<WRG>();
-      constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
-      constexpr int kRowsPerPass = 64 / kPieces;
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        // the MFMA layout (4 columns 16r + 4g.. of block row lane % 16) into LDS
+        f32x4 blk[WRG];
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) {
-          const f32x4 o = acc[r][cb];
-          u32x2 v;
-          v[0] = pack_bf16x2(o[0] * al, o[1] * al);
-          v[1] = pack_bf16x2(o[2] * al, o[3] * al);
-          *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-        // back as whole pieces of rows (the wave's LDS operations complete in order)
-#pragma unroll
-        for (int pass = 0; pass < 16 / kRowsPerPass; ++pass) {
-          const int row = pass * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
-          const u32x4 q = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
-          const int64_t flat = __shfl(flat_cb[cb], row);
-          if (cb * 16 + row < td.nrows)
-            *reinterpret_cast<u32x4*>(a.o_rows + flat * a.H + 16 * G0 + 8 * piece) = q;
-        }
-        __builtin_amdgcn_wave_barrier();
+        for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
+        store_out_block<WRG>(blk, al, wave_out, lane, flat_cb[cb], td.nrows - cb * 16, a.o_rows,
+                             a.o_exp, a.H, 16 * G0);
       }
       // the next slab's MFMAs (fresh accumulators) stay after these stores, so the two
       // accumulator sets are never live together
@@ -181,7 +160,7 @@ template <int NW, int WRG, int BN, int SPW, int SPLIT>
 __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   __shared__ _Float16 s_tok[BN * kFc2LdsRow];
   __shared__ int64_t s_row[BN];
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * fc2_out_stride<WRG>()];
+  __shared__ __attribute__((aligned(16))) float s_out[NW * 16 * out_lds_stride<WRG>()];
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
   const int ntiles = a.num_tiles[big];
   const int n_slabs = a.H / (NW * WRG * 16);
@@ -270,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
   constexpr int kThreads = NW * 64;
   static_assert(kFc2StationaryGrid % kXcds == 0, "whole XCD strides");
   __shared__ __attribute__((aligned(16))) _Float16 s_tok[kFc2PassRows * kFc2LdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * fc2_out_stride<WRG>()];
+  __shared__ __attribute__((aligned(16))) float s_out[NW * 16 * out_lds_stride<WRG>()];
 
   const int n_slabs = a.H / (kSlabGroups * 16);
   const int n_runs = a.num_tiles[2];
@@ -278,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
   const int code_bytes = a.I / 2, scale_cols = a.I / 16;
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
-  uint16_t* wave_out = s_out + w * 16 * fc2_out_stride<WRG>();
+  float* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
 
   // Token rows [p0, p0 + nr) of the run (rows past nr repeat the last one; they are not
   // stored).  Four threads per row, each NCH 16-byte pieces of codes (32 values) and the
@@ -327,13 +306,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
       for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
 
     const float al = a.alpha2[e];
-    uint16_t* out_cols = a.o_rows + 16 * (slab * kSlabGroups + w * WRG);
+    const int col0 = 16 * (slab * kSlabGroups + w * WRG);
     int32_t flat[kFc2PassRows / 16];
     int p0 = rd.row_start;
     int nr = min(kFc2PassRows, row_end - p0);
 
     // One pass over NCB 16-token blocks: all K-steps from the resident weights, then the
-    // BF16 rows (stored at their flat ids, through the per-wave LDS transpose).
+    // output rows (stored at their flat ids through the per-wave LDS staging).
     auto pass = [&](auto ncb_c) {
       constexpr int NCB = decltype(ncb_c)::value;
       f32x4 acc[WRG][NCB];
@@ -364,29 +343,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
           __builtin_amdgcn_sched_barrier(0);   // bounds the live decoded weights to one K-step
         }
       }
-      constexpr int kStride = fc2_out_stride<WRG>();
-      constexpr int kPieces = 2 * WRG;                  // 16-byte pieces per row
-      constexpr int kRowsPerPass = 64 / kPieces;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 blk[WRG];
 #pragma unroll
-        for (int r = 0; r < WRG; ++r) {
-          const f32x4 o = acc[r][cb];
-          u32x2 v;
-          v[0] = pack_bf16x2(o[0] * al, o[1] * al);
-          v[1] = pack_bf16x2(o[2] * al, o[3] * al);
-          *reinterpret_cast<u32x2*>(wave_out + (lane & 15) * kStride + 16 * r + 4 * g) = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int q = 0; q < 16 / kRowsPerPass; ++q) {
-          const int row = q * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
-          const u32x4 val = *reinterpret_cast<const u32x4*>(wave_out + row * kStride + 8 * piece);
-          const int64_t f = __shfl(flat[cb], row);
-          if (cb * 16 + row < nr)
-            *reinterpret_cast<u32x4*>(out_cols + f * a.H + 8 * piece) = val;
-        }
-        __builtin_amdgcn_wave_barrier();
+        for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
+        store_out_block<WRG>(blk, al, wave_out, lane, flat[cb], nr - cb * 16, a.o_rows, a.o_exp,
+                             a.H, col0);
       }
     };
 

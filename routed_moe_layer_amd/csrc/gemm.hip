@@ -25,7 +25,8 @@
 //     as MFMA operands (one barrier per chunk).
 // The FC1 epilogue fuses alpha1, SiTU, the group-16 requantization (two consecutive MFMA
 // row groups hold the gate/up pairs of 16 intermediate channels = one NVFP4 group) and the
-// per-expert amax statistic; the FC2 epilogue applies alpha2 and stores BF16 rows.
+// per-expert amax statistic; the FC2 epilogue applies alpha2 and stores the rows as f16
+// with per-32-column exponents (store_out_block).
 #include <type_traits>
 
 #include "common.h"
@@ -402,23 +403,24 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
     if (lane == 0 && wave_amax > 0.0f)
       atomicMax(reinterpret_cast<unsigned int*>(a.a_amax + e), __float_as_uint(wave_amax));
   } else {
+    // the K loop's token buffers are free once every wave has passed its last chunk; each
+    // wave then stages its output blocks in its own part of them
+    static_assert(sizeof(_Float16) * 2 * BN * Stage::kLdsRow >=
+                      sizeof(float) * NW * 16 * out_lds_stride<WRG>(), "output staging space");
+    __syncthreads();
+    float* lds = reinterpret_cast<float*>(&s_tok[0][0]) + t.w * 16 * out_lds_stride<WRG>();
     const float al = a.alpha2[e];
 #pragma unroll
     for (int cb = 0; cb < NCBA; ++cb) {
-      const int n = cb * 16 + (lane & 15);
-      if (n >= td.nrows) continue;
       // stored at the row's flat id t*k + j (the finalization reads a token's rows as
       // one contiguous run)
-      const int64_t row = a.sorted_row_idx[td.row_start + n];
+      const int n = min(cb * 16 + (lane & 15), td.nrows - 1);
+      const int32_t flat = a.sorted_row_idx[td.row_start + n];
+      f32x4 blk[WRG];
 #pragma unroll
-      for (int r = 0; r < WRG; ++r) {
-        const f32x4 o = acc[r][cb];
-        const int h0 = 16 * (G0 + r) + 4 * g;
-        uint2 v;
-        v.x = pack_bf16x2(o[0] * al, o[1] * al);
-        v.y = pack_bf16x2(o[2] * al, o[3] * al);
-        *reinterpret_cast<uint2*>(a.o_rows + row * a.H + h0) = v;
-      }
+      for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
+      store_out_block<WRG>(blk, al, lds, lane, flat, td.nrows - cb * 16, a.o_rows, a.o_exp,
+                           a.H, 16 * G0);
     }
   }
 }
@@ -492,9 +494,11 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 
 // out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[t*k + j, 8v..8v+7]), j in order, fp32 fused
 // multiply-add; rows whose id was dropped (gather-map entry < 0) are skipped.  FC2 stored
-// the rows in flat id order, so a token's k rows are one contiguous run.  A workgroup
-// covers 8*kFinThreads columns of one token; each thread owns 8 columns and issues the
-// 16-byte loads of up to kFinBatch rows before it accumulates them.
+// the rows in flat id order, so a token's k rows are one contiguous run; a stored value is
+// o * 2^s with s the exponent of its 32-column segment, so it enters the sum with the
+// weight w * 2^-s (exact).  A workgroup covers 8*kFinThreads columns of one token; each
+// thread owns 8 columns and issues the 16-byte loads of up to kFinBatch rows before it
+// accumulates them.
 constexpr int kFinThreads = 512, kFinBatch = 8;
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
@@ -503,9 +507,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
   if (v >= a.H / 8) return;
   const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
+  const int segs = a.H / kOutSeg;
+  const int8_t* __restrict__ exp_t = a.o_exp + t * a.k * segs + v / (kOutSeg / 8);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
     u32x4 d[kFinBatch];
+    int32_t sx[kFinBatch];
     bool ok[kFinBatch];
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
@@ -515,16 +522,19 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
       d[u] = ok[u] ? __builtin_nontemporal_load(
                          reinterpret_cast<const u32x4*>(a.o_rows + (t * a.k + j) * a.H) + v)
                    : u32x4{0u, 0u, 0u, 0u};
+      sx[u] = ok[u] ? exp_t[j * segs] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
       if (!ok[u]) continue;
-      const float wt = bf16_to_f32(w_t[j0 + u]);
+      const float wt = bf16_to_f32(w_t[j0 + u]) *
+                       __uint_as_float(static_cast<uint32_t>(127 - sx[u]) << 23);
       const uint32_t dw[4] = {d[u][0], d[u][1], d[u][2], d[u][3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wt, __uint_as_float(dw[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wt, __uint_as_float(dw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        const f32x2 o = __builtin_convertvector(__builtin_bit_cast(f16x2, dw[i]), f32x2);
+        acc[2 * i] = fmaf(wt, o[0], acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wt, o[1], acc[2 * i + 1]);
       }
     }
   }

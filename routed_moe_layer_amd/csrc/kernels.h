@@ -186,7 +186,8 @@ struct LayerArgs {
   uint8_t* a_codes;            // [T*k, I/2]
   uint8_t* a_scales;           // [T*k, I/16]
   float* a_amax;               // [E]
-  uint16_t* o_rows;            // [T*k, H] bf16, row t*k + j (flat id order)
+  uint16_t* o_rows;            // [T*k, H] f16 O * 2^s, row t*k + j (flat id order)
+  int8_t* o_exp;               // [T*k, H/32] exponent s of each 32-column segment
   const uint16_t* route_weights;
   uint16_t* out;               // [T, H]
 };

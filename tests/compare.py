@@ -7,16 +7,15 @@
     the codes may differ (a block whose E4M3 scale differs counts all 16 of its codes),
     and within blocks of equal scale a differing code is at most one E2M1 step away.
   * The BF16 output must satisfy, per row and element,
-        |out - ref| <= 2e-2 * rms(ref row) + |dy| + ulp(|ref| + |dy|)
-    where ulp is the BF16 grid spacing at the reference (both sides round their own sum
-    to BF16 once, so they may land one BF16 step apart: for an element above ~2.5 rms
-    that step alone exceeds 2e-2 * rms), and dy is the exact linear effect on the output
-    of the intermediate codes that differ (FC2 and finalization are linear in the
-    decoded intermediate):
-        dy[t, h] = sum_j w[t, j] * alpha2[e] * sum_i (ahat_gpu - ahat_ref)[i] * w2hat[e][h, i].
+        |out - ref| <= 2e-2 * rms(ref row) + |dy|
+    where ref is the oracle's output before its final BF16 rounding (float64) and dy is
+    the exact linear effect on the output of the intermediate codes that differ (FC2 and
+    finalization are linear in the decoded intermediate):
+        dy[t, h] = sum_j w[t, j] * alpha2[e] * sum_i (ahat_gpu - ahat_ref)[i] * w2hat[e, h, i].
     For a row with no differing code dy = 0 and this is the plain 2e-2 * rms bound; a
     single one-step code flip can move an output element by more than that, so the bound
-    is widened by exactly the flip's effect (computed from the codes, not from outputs).
+    of such a row is widened by exactly the flip's effect (computed from the codes, never
+    from GPU outputs), and the number of rows that needed it is reported.
 """
 
 import numpy as np
@@ -58,25 +57,35 @@ def flip_effect(gpu_codes_u, gpu_scales, ref_codes_u, ref_scales, w2hat, alpha2_
     return np.float64(alpha2_e) * (w2hat @ (dg - dr))
 
 
-def bf16_ulp(v):
-    """Spacing of the BF16 grid at |v| (8 significant bits)."""
-    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -126))
-    return np.ldexp(1.0, e - 8)
+def check_output(gpu_bits, ref_f64, dy=None):
+    """Assert the output bound against the oracle's unrounded output ref_f64 [n, H].
 
-
-def check_output(gpu_bits, ref_bits, dy=None):
-    """Assert the BF16 output bound; returns the worst ratio err / (2e-2 * rms)."""
+    Returns a dict: ``ratio`` = worst err / (2e-2 * rms) over rows without a differing
+    intermediate code (the plain bound, never widened), ``ratio_all`` = worst
+    err / tol over all rows, ``rows_widened`` = rows whose bound includes a flip's dy.
+    """
     out = oracle.bf16_bits_to_f32(gpu_bits).astype(np.float64)
-    ref = oracle.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    dy = np.zeros_like(ref) if dy is None else np.abs(dy)
+    ref = np.asarray(ref_f64, dtype=np.float64)
+    dy = np.zeros_like(ref) if dy is None else np.abs(np.asarray(dy, dtype=np.float64))
+    widened = np.any(dy > 0, axis=1)
     rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
-    tol = OUT_RTOL * rms + dy + bf16_ulp(np.abs(ref) + dy)
+    base = np.maximum(OUT_RTOL * rms, 1e-300)
+    tol = OUT_RTOL * rms + dy
     err = np.abs(out - ref)
     bad = err > tol
     assert not bad.any(), (
         f"{bad.sum()} output elements out of bound; worst row "
-        f"{np.argmax(bad.sum(1))}, max err/tol {np.max(err / tol):.3g}")
-    return float(np.max(err / np.maximum(OUT_RTOL * rms, 1e-30)))
+        f"{np.argmax(bad.sum(1))}, max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}")
+    plain = err / base
+    ratio = float(np.max(plain[~widened])) if (~widened).any() else 0.0
+    return {"ratio": ratio, "ratio_all": float(np.max(err / np.maximum(tol, 1e-300))),
+            "rows_widened": int(widened.sum()), "rows": int(ref.shape[0])}
+
+
+def fmt(res):
+    return (f"worst err/(2e-2 rms) {res['ratio']:.3f} (rows with a flipped code: "
+            f"{res['rows_widened']}/{res['rows']}, worst err/bound there "
+            f"{res['ratio_all']:.3f})")
 
 
 def check_layer(p, gpu_out, inter, ref):
@@ -108,9 +117,9 @@ def check_layer(p, gpu_out, inter, ref):
         dO = flip_effect(gc[i], inter["a_scales"][i], ref["a_codes"][i], ref["a_scales"][i],
                          w2d, p["alpha2"][e])
         dy[t] += float(oracle.bf16_bits_to_f32(p["rw"][t, j])) * dO
-    ratio = check_output(gpu_out, ref["out"], dy)
+    res = check_output(gpu_out, ref["out_f64"], dy)
     # amax statistic: per expert max |SiTU output| of the expert's rows
     amax_ref = np.zeros(cfg.E, np.float32)
     np.maximum.at(amax_ref, ref["sorted_ids"], np.max(np.abs(ref["a"]), axis=1))
     assert np.allclose(inter["a_amax"], amax_ref, rtol=1e-4, atol=0)
-    return st, ratio
+    return st, res

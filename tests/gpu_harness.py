@@ -69,6 +69,13 @@ def prepare(cfg, w13, w13_sf, w2, w2_sf):
     return prepared
 
 
+def _fc2_rows(vals, exps):
+    """FC2 output rows [R, H] as float64 from the stored f16 values and the exponent s of
+    each 32-column segment (value = stored * 2^-s)."""
+    scale = np.ldexp(1.0, -np.repeat(exps.astype(np.int64), 32, axis=1))
+    return vals.astype(np.float64) * scale
+
+
 class DeviceLayer:
     """The inputs of one moe_forward call resident on the GPU."""
 
@@ -125,6 +132,7 @@ class DeviceLayer:
             "cumsum": take("expert_cumsum", cfg.E, np.int32, (cfg.E,)),
             "a_codes": take("a_codes", R * cfg.I // 2, np.uint8, (R, cfg.I // 2)),
             "a_scales": take("a_scales", R * cfg.I // 16, np.uint8, (R, cfg.I // 16)),
-            "o_rows": take("o_rows", R * cfg.H, np.uint16, (R, cfg.H)),
+            "o_rows": _fc2_rows(take("o_rows", R * cfg.H, np.float16, (R, cfg.H)),
+                                take("o_exp", R * (cfg.H // 32), np.int8, (R, cfg.H // 32))),
             "a_amax": take("a_amax", cfg.E, np.float32, (cfg.E,)),
         }

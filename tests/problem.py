@@ -12,11 +12,12 @@ from moe_inputs import (LayerConfig, draw_layer_tokens, draw_all_expert_weights,
 
 
 def build_layer_problem(cfg: LayerConfig, calib_tokens=None, w13_bits=None, w2_bits=None,
-                        quantize_weights=True):
+                        quantize_weights=True, per_expert_qa=False):
     """Inputs and every scale of a layer workload.
 
     Weight amax calibration is per expert; dX over all tokens; dA from the oracle's
-    calibration pass over ``calib_tokens`` (default: all tokens).
+    calibration pass over ``calib_tokens`` (default: all tokens), one shared value or,
+    with ``per_expert_qa``, one value per expert from that expert's own rows.
     With ``quantize_weights`` the canonical NVFP4 weight storage is made by the oracle.
     """
     x, ids, rw = draw_layer_tokens(cfg)
@@ -32,8 +33,10 @@ def build_layer_problem(cfg: LayerConfig, calib_tokens=None, w13_bits=None, w2_b
         p["w13"], p["w13_sf"] = oracle.quantize_expert_stack(w13_bits, sc["qW13"])
         p["w2"], p["w2_sf"] = oracle.quantize_expert_stack(w2_bits, sc["qW2"])
         tokens = np.arange(cfg.T) if calib_tokens is None else np.asarray(calib_tokens)
-        dA, qA = oracle.calibrate_intermediate(tokens, x, ids, p["w13"], p["w13_sf"], p["w2"],
-                                               p["w2_sf"], p["qX"], alpha1, beta, lam)
+        calib = (oracle.calibrate_intermediate_per_expert if per_expert_qa
+                 else oracle.calibrate_intermediate)
+        dA, qA = calib(tokens, x, ids, p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], p["qX"],
+                       alpha1, beta, lam)
         p["dA"], p["qA"] = dA, qA
         p["alpha2"] = (dA * sc["dW2"]).astype(np.float32)
     return p
@@ -80,7 +83,9 @@ class ExpertStore:
             d13[e], s13[e], d2[e], s2[e] = a[0], b[0], c[0], d[0]
 
         with ThreadPoolExecutor(threads) as ex:
-            list(ex.map(one, experts))
+            for n, _ in enumerate(ex.map(one, experts)):
+                if (n + 1) % 128 == 0:
+                    print(f"    quantized {n + 1}/{len(experts)} experts", flush=True)
         E, H, I = cfg.E, cfg.H, cfg.I
         self.experts = experts
         self.w13 = self._View(d13, (E, 2 * I, H // 2))
@@ -89,28 +94,67 @@ class ExpertStore:
         self.w2_sf = self._View(s2, (E, H, I // 16))
 
 
-def build_full_problem(cfg, w13_bits, w2_bits, sample_tokens, calib_tokens, wscales=None):
+def build_full_problem(cfg, w13_bits, w2_bits, select, wscales=None, per_expert_qa=False):
     """A full-shape workload whose weights live on the CPU as BF16 bits (all experts, for
-    upload to the GPU) and, for the experts the sampled and calibration tokens touch, as
-    oracle-quantized canonical storage.  Scales: per-expert weight amax, global x amax,
-    dA from the oracle's calibration pass over ``calib_tokens``."""
+    upload to the GPU) and, for the experts the checked rows touch, as oracle-quantized
+    canonical storage.  ``select(ids)`` returns (pairs [n, 2] of (token, pick) routed rows
+    whose intermediate and FC2 rows are checked, tokens whose whole output is checked).
+    Scales: per-expert weight amax, global x amax, dA from the oracle's calibration pass
+    over the first 8 checked tokens (shared, or per expert with ``per_expert_qa``)."""
     x, ids, rw = draw_layer_tokens(cfg)
+    pairs, tokens = select(ids)
+    pairs = np.asarray(pairs, np.int64).reshape(-1, 2)
+    tokens = np.asarray(tokens, np.int64)
     dX, qX = oracle.calibrate_tokens(x)
     if wscales is None:
         wscales = oracle.calibrate_weights(w13_bits) + oracle.calibrate_weights(w2_bits)
     dW13, qW13, dW2, qW2 = wscales
     beta, lam = draw_situ_params(cfg)
     alpha1 = (dX * dW13).astype(np.float32)
-    sample_tokens = np.asarray(sample_tokens)
-    calib_tokens = np.asarray(calib_tokens)
-    used = np.unique(np.concatenate([ids[sample_tokens].ravel(), ids[calib_tokens].ravel()]))
+    used = np.unique(np.concatenate([ids[pairs[:, 0], pairs[:, 1]], ids[tokens].ravel()]))
     store = ExpertStore(cfg, qW13, qW2, used)
-    cache = {}
-    dA, qA = oracle.calibrate_intermediate(calib_tokens, x, ids, store.w13, store.w13_sf,
-                                           store.w2, store.w2_sf, qX, alpha1, beta, lam,
-                                           weight_cache=cache)
+    calib = (oracle.calibrate_intermediate_per_expert if per_expert_qa
+             else oracle.calibrate_intermediate)
+    dA, qA = calib(tokens[:8], x, ids, store.w13, store.w13_sf, store.w2, store.w2_sf, qX,
+                   alpha1, beta, lam)
     alpha2 = (dA * dW2).astype(np.float32)
     return dict(cfg=cfg, x=x, ids=ids, rw=rw, beta=beta, lam=lam, qX=np.float32(qX),
                 dX=np.float32(dX), qW13=qW13, qW2=qW2, dW13=dW13, dW2=dW2, alpha1=alpha1,
                 dA=dA, qA=qA, alpha2=alpha2, w13=store.w13, w13_sf=store.w13_sf, w2=store.w2,
-                w2_sf=store.w2_sf, store=store, weight_cache=cache, sample=sample_tokens)
+                w2_sf=store.w2_sf, store=store, pairs=pairs, tokens=tokens)
+
+
+def oracle_pairs(p, pairs, threads=16):
+    """The oracle's FC1 -> SiTU -> requantization -> FC2 of routed rows pairs [(t, j)],
+    evaluated expert by expert (each expert's weights decoded once, experts in parallel
+    threads).  Returns per pair: a_codes [n, I], a_scales [n, I/16], o [n, H] fp32; and the
+    NVFP4 codes and scales of the tokens involved."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = p["cfg"]
+    pairs = np.asarray(pairs, np.int64).reshape(-1, 2)
+    t, j = pairs[:, 0], pairs[:, 1]
+    e_of = np.asarray(p["ids"])[t, j]
+    toks, tok_row = np.unique(t, return_inverse=True)
+    xc, xs = oracle.quantize_nvfp4(oracle.bf16_bits_to_f32(p["x"][toks]), np.float32(p["qX"]))
+    xdec = oracle.dequantize_nvfp4(xc, xs)
+    n, H, I = pairs.shape[0], cfg.H, cfg.I
+    beta = np.full(cfg.E, 4.0, np.float32) if p["beta"] is None else p["beta"]
+    lam = np.full(cfg.E, 25.0, np.float32) if p["lam"] is None else p["lam"]
+    res = {"a_codes": np.zeros((n, I), np.uint8), "a_scales": np.zeros((n, I // 16), np.uint8),
+           "o": np.zeros((n, H), np.float32),
+           "x_codes": xc, "x_scales": xs, "tokens": toks}
+
+    def one(e):
+        sel = np.nonzero(e_of == e)[0]
+        w13d, w2d = oracle.expert_weights_decoded(p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], e)
+        _, _, ac, as_, o = oracle.expert_rows(xdec[tok_row[sel]], w13d, w2d, p["alpha1"][e],
+                                              p["qA"][e], p["alpha2"][e], beta[e], lam[e])
+        return sel, ac, as_, o
+
+    experts = np.unique(e_of)
+    with ThreadPoolExecutor(threads) as ex:
+        for n, (sel, ac, as_, o) in enumerate(ex.map(one, experts)):
+            res["a_codes"][sel], res["a_scales"][sel], res["o"][sel] = ac, as_, o
+            if (n + 1) % 128 == 0:
+                print(f"    oracle rows of {n + 1}/{experts.size} experts", flush=True)
+    return res

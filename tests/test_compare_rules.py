@@ -25,16 +25,30 @@ def test_code_diff_counting():
     assert st["max_step_same_scale"] == 1 and st["n_diff"] == 2
 
 
-def test_output_bound_accepts_one_ulp_and_rejects_more():
-    ref = oracle.f64_to_bf16_bits(np.array([[3.0, -1.0, 0.5, 0.25] * 8]))
-    vals = oracle.bf16_bits_to_f32(ref).astype(np.float64)
-    one_up = oracle.f64_to_bf16_bits(vals + compare.bf16_ulp(vals))
-    compare.check_output(one_up, ref)
-    far = oracle.f64_to_bf16_bits(vals + 0.2 * np.sqrt(np.mean(vals ** 2)))
+def test_output_bound_is_two_percent_of_the_unrounded_row_rms():
+    ref = np.array([[3.0, -1.0, 0.5, 0.25] * 8])
+    rms = np.sqrt(np.mean(ref ** 2))
+    # the BF16 rounding of the reference itself passes (here exact)
+    res = compare.check_output(oracle.f64_to_bf16_bits(ref), ref)
+    assert res["ratio"] == 0.0 and res["rows_widened"] == 0
+    # a deviation just inside 2e-2 * rms passes, one just outside fails: no ulp slack
+    bits = oracle.f64_to_bf16_bits(ref)                        # exact: err = |shift|
+    for frac, ok in ((0.0199, True), (0.0201, False)):
+        moved = ref.copy(); moved[0, 0] -= frac * rms          # reference shifted, rms kept
+        moved_rms = np.sqrt(np.mean(moved ** 2))
+        moved[0, 0] = ref[0, 0] - frac * moved_rms
+        if ok:
+            assert compare.check_output(bits, moved)["ratio"] <= 1.0
+        else:
+            with pytest.raises(AssertionError):
+                compare.check_output(bits, moved)
+    far = oracle.f64_to_bf16_bits(ref + 0.2 * rms)
     with pytest.raises(AssertionError):
         compare.check_output(far, ref)
-    # a large deviation is accepted only when the flip effect dy accounts for it
-    compare.check_output(far, ref, dy=np.full(vals.shape, 0.2 * np.sqrt(np.mean(vals ** 2))))
+    # a large deviation is accepted only when the flip effect dy accounts for it, and the
+    # row is reported as widened
+    res = compare.check_output(far, ref, dy=np.full(ref.shape, 0.2 * rms))
+    assert res["rows_widened"] == 1
 
 
 def test_flip_effect_is_the_fc2_difference():

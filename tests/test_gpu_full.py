@@ -1,8 +1,18 @@
 """GPU parity at the full TP8-local shape (H=3584, I=384, E=896, top-16) for the decode
 (T=16), mid (T=1024, Zipf 1.0) and prefill (T=16384, per-expert SiTU, outliers) batches,
-in the launch configuration the benchmark times.  Routing is compared bit for bit in full;
-the layer output, the input codes and the intermediate codes on sampled tokens that the
-oracle evaluates one by one (first, second, middle, last two)."""
+in the launch configuration the benchmark times.
+
+Routing is compared bit for bit in full.  The oracle then evaluates routed rows chosen by
+their position in the expert-sorted order (the GEMMs' token tiles are runs of 16-row blocks
+of one expert's rows, so these cover every position a row can take in a tile):
+  * every row of a few experts: the most loaded one, up to three whose row count leaves
+    a ragged last 16-row block, a median one and the least loaded one -- their
+    intermediate NVFP4 codes and their FC2 output rows are compared row by row;
+  * the whole output of 64 tokens: those of the first and last row of every 16-row block
+    of the two most loaded experts, then the first and last token (all 16 at T=16), with
+    the input codes of those tokens and the codes and FC2 rows of all their picks.
+The mid and prefill batches take a per-expert qA (each expert calibrated on its own rows
+of the calibration tokens), the decode batch one shared qA."""
 
 import sys
 
@@ -12,11 +22,13 @@ import torch
 
 import oracle
 from moe_inputs import DECODE_16, MID_1024, PREFILL_16K, draw_all_expert_weights
-from tests.problem import build_full_problem, oracle_dense
+from tests.problem import build_full_problem, oracle_pairs
 from tests.gpu_harness import dev, host, quantize_on_gpu, prepare, DeviceLayer
 from tests import compare
 
 pytestmark = pytest.mark.gpu
+
+N_TOKENS = 64
 
 
 def _say(msg):
@@ -48,24 +60,72 @@ def full_weights():
     torch.cuda.synchronize()
 
 
-def _samples(T):
-    return np.unique(np.array([0, 1, T // 2, T - 2, T - 1])) if T > 16 else np.arange(T)
+def selection(cfg):
+    """select(ids) for build_full_problem: (pairs checked row by row, tokens checked)."""
+    def select(ids):
+        T, k, E = cfg.T, cfg.k, cfg.E
+        if T <= N_TOKENS:
+            t, j = np.meshgrid(np.arange(T), np.arange(k), indexing="ij")
+            return np.stack([t.ravel(), j.ravel()], 1), np.arange(T)
+        r = oracle.route(ids, E)
+        counts = r["counts"].astype(np.int64)
+        start = r["cumsum"].astype(np.int64) - counts
+        order = np.argsort(-counts, kind="stable")
+        nz = [int(e) for e in order if counts[e] > 0]
+        chosen = [nz[0]]
+        chosen += [e for e in nz[1:] if counts[e] % 16 and counts[e] > 16][:3]
+        chosen += [e for e in (nz[len(nz) // 2], nz[-1]) if e not in chosen]
+        rows = np.concatenate([np.arange(start[e], start[e] + counts[e]) for e in chosen])
+        tok = []
+        for e in nz[:2]:
+            for b0 in range(0, int(counts[e]), 16):
+                for pos in (b0, min(b0 + 15, int(counts[e]) - 1)):
+                    tok.append(int(r["sorted_row_idx"][start[e] + pos]) // k)
+        tok = list(dict.fromkeys(tok))                   # first occurrences, in order
+        half = N_TOKENS // 2 - 1
+        # as many from each of the two experts' blocks, then the first and last token
+        in_first = set((r["sorted_row_idx"][start[nz[0]]:start[nz[0]] + counts[nz[0]]] // k).tolist())
+        first = [t for t in tok if t in in_first]
+        second = [t for t in tok if t not in in_first]
+        tokens = list(dict.fromkeys(first[:half] + second[:half] + [0, T - 1]))
+        for t in tok:                                    # top up to N_TOKENS
+            if len(tokens) >= N_TOKENS:
+                break
+            if t not in tokens:
+                tokens.append(t)
+        tokens = np.array(tokens[:N_TOKENS])
+        flat = r["sorted_row_idx"][rows].astype(np.int64)
+        tj = np.stack([flat // k, flat % k], 1)
+        t2, j2 = np.meshgrid(tokens, np.arange(k), indexing="ij")
+        tj = np.concatenate([tj, np.stack([t2.ravel(), j2.ravel()], 1)])
+        return np.unique(tj, axis=0), tokens
+    return select
 
 
-@pytest.mark.parametrize("cfg", [DECODE_16, MID_1024, PREFILL_16K], ids=lambda c: c.name)
-def test_full_layer_parity(full_weights, cfg):
+CASES = [(DECODE_16, False), (MID_1024, True), (PREFILL_16K, True)]
+
+
+# the oracle side of one case takes one to two minutes of host time (hundreds of experts)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,per_expert_qa", CASES,
+                         ids=[f"{c.name}{'_qa_per_expert' if q else ''}" for c, q in CASES])
+def test_full_layer_parity(full_weights, cfg, per_expert_qa):
     fw = full_weights
-    sample = _samples(cfg.T)
+    E, H, I, k, T = cfg.E, cfg.H, cfg.I, cfg.k, cfg.T
     _say(f"full layer {cfg.name}: building oracle problem")
-    p = build_full_problem(cfg, fw["w13_bits"], fw["w2_bits"], sample, np.arange(min(8, cfg.T)),
-                           wscales=fw["wscales"])
-    E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.k
+    p = build_full_problem(cfg, fw["w13_bits"], fw["w2_bits"], selection(cfg),
+                           wscales=fw["wscales"], per_expert_qa=per_expert_qa)
+    if per_expert_qa:
+        assert len(np.unique(p["qA"])) > 16
+    pairs, tokens = p["pairs"], p["tokens"]
+    assert tokens.size == min(T, N_TOKENS)
     # the GPU-quantized weights of every expert the oracle touches equal the oracle's
     ex = np.array(p["store"].experts)
-    g13 = host(fw["c13"].view(E, 2 * I, H // 2)[torch.from_numpy(ex).cuda()])
-    g13s = host(fw["s13"].view(E, 2 * I, H // 16)[torch.from_numpy(ex).cuda()])
-    g2 = host(fw["c2"].view(E, H, I // 2)[torch.from_numpy(ex).cuda()])
-    g2s = host(fw["s2"].view(E, H, I // 16)[torch.from_numpy(ex).cuda()])
+    sel = torch.from_numpy(ex).cuda()
+    g13 = host(fw["c13"].view(E, 2 * I, H // 2)[sel])
+    g13s = host(fw["s13"].view(E, 2 * I, H // 16)[sel])
+    g2 = host(fw["c2"].view(E, H, I // 2)[sel])
+    g2s = host(fw["s2"].view(E, H, I // 16)[sel])
     for n, e in enumerate(ex):
         assert np.array_equal(g13[n], p["w13"][e]) and np.array_equal(g13s[n], p["w13_sf"][e])
         assert np.array_equal(g2[n], p["w2"][e]) and np.array_equal(g2s[n], p["w2_sf"][e])
@@ -76,33 +136,45 @@ def test_full_layer_parity(full_weights, cfg):
     inter = L.intermediates()
     # routing: bit-exact in full
     r = oracle.route(p["ids"], E)
-    for key, rk in (("sorted_ids", "sorted_ids"), ("sorted_row_idx", "sorted_row_idx"),
-                    ("expanded_row_idx", "expanded_row_idx"), ("counts", "counts"),
-                    ("cumsum", "cumsum")):
-        assert np.array_equal(inter[key], r[rk]), key
-    # oracle on the sampled tokens
-    _say(f"full layer {cfg.name}: oracle on tokens {sample.tolist()}")
-    ref = oracle_dense(p, sample, weight_cache=p["weight_cache"])
-    assert np.array_equal(inter["x_codes"][sample], oracle.pack_nibbles(ref["x_codes"]))
-    assert np.array_equal(inter["x_scales"][sample], ref["x_scales"])
-    if cfg.T * k < compare.X_DEC_MAX_ROWS:
-        assert np.array_equal(inter["x_dec"][sample].astype(np.float64),
+    for key in ("sorted_ids", "sorted_row_idx", "expanded_row_idx", "counts", "cumsum"):
+        assert np.array_equal(inter[key], r[key]), key
+    _say(f"  oracle on {pairs.shape[0]} routed rows over {ex.size} experts, "
+         f"{tokens.size} whole tokens")
+    ref = oracle_pairs(p, pairs)
+    # input codes of the tokens involved
+    assert np.array_equal(inter["x_codes"][ref["tokens"]], oracle.pack_nibbles(ref["x_codes"]))
+    assert np.array_equal(inter["x_scales"][ref["tokens"]], ref["x_scales"])
+    if T * k < compare.X_DEC_MAX_ROWS:
+        assert np.array_equal(inter["x_dec"][ref["tokens"]].astype(np.float64),
                               oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
-    pos = inter["expanded_row_idx"].reshape(cfg.T, k)[sample]            # [n, k]
-    gc = compare.unpack(inter["a_codes"][pos.ravel()])
-    gs = inter["a_scales"][pos.ravel()]
-    rc = ref["a_codes"].reshape(-1, I)
-    rs = ref["a_scales"].reshape(-1, I // 16)
-    st = compare.code_diff_stats(gc, gs, rc, rs)
+    # intermediate codes, row by row
+    flat = pairs[:, 0] * k + pairs[:, 1]
+    pos = inter["expanded_row_idx"][flat]
+    gc = compare.unpack(inter["a_codes"][pos])
+    gs = inter["a_scales"][pos]
+    st = compare.code_diff_stats(gc, gs, ref["a_codes"], ref["a_scales"])
     _say(f"  intermediate code diffs {st['n_diff']}/{st['n_codes']}")
     assert st["max_step_same_scale"] <= 1, st
     assert st["frac"] <= compare.CODE_DIFF_FRAC, st
-    dy = np.zeros((sample.size, H))
-    for row in st["rows_with_diff"]:
-        n, j = divmod(int(row), k)
-        e = int(p["ids"][sample[n], j])
-        w2d = p["weight_cache"][e][1]
-        dO = compare.flip_effect(gc[row], gs[row], rc[row], rs[row], w2d, p["alpha2"][e])
-        dy[n] += float(oracle.bf16_bits_to_f32(p["rw"][sample[n], j])) * dO
-    ratio = compare.check_output(out[sample], ref["out"], dy)
-    _say(f"  worst err/(2e-2 rms) {ratio:.3f}")
+    dO = np.zeros((pairs.shape[0], H))
+    for i in st["rows_with_diff"]:
+        e = int(p["ids"][pairs[i, 0], pairs[i, 1]])
+        _, w2d = oracle.expert_weights_decoded(p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], e)
+        dO[i] = compare.flip_effect(gc[i], gs[i], ref["a_codes"][i], ref["a_scales"][i], w2d,
+                                    p["alpha2"][e])
+    # FC2 output rows, row by row: f16 storage with per-32-column exponents keeps 11
+    # significant bits of the segment's largest value
+    o_gpu = inter["o_rows"][flat]
+    seg = np.repeat(np.max(np.abs(ref["o"]).reshape(-1, H // 32, 32), axis=2), 32, axis=1)
+    err = np.abs(o_gpu - ref["o"])
+    tol = 2.0 ** -10 * seg + np.abs(dO)
+    assert np.all(err <= tol), (f"{int((err > tol).sum())} FC2 output values off; "
+                                f"worst row {int(np.argmax((err > tol).sum(1)))}")
+    # whole-token outputs against the oracle's unrounded finalization
+    index = {(int(t), int(j)): i for i, (t, j) in enumerate(pairs)}
+    rows_tk = np.array([[index[(int(t), j)] for j in range(k)] for t in tokens])
+    want = oracle.combine(ref["o"][rows_tk], p["rw"][tokens])
+    wts = oracle.bf16_bits_to_f32(p["rw"][tokens]).astype(np.float64)
+    dy = np.einsum("nk,nkh->nh", wts, dO[rows_tk])
+    res = compare.check_output(out[tokens], want, dy)
+    _say(f"  {compare.fmt(res)}")

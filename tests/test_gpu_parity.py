@@ -226,8 +226,8 @@ def test_layer_tiny_parity():
     p = build_layer_problem(TINY)
     ref = oracle_forward(p)
     _, out, inter = _run_layer(p)
-    st, ratio = compare.check_layer(p, out, inter, ref)
-    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, worst err/(2e-2 rms) {ratio:.3f}")
+    st, res = compare.check_layer(p, out, inter, ref)
+    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, {compare.fmt(res)}")
 
 
 def _edge(name, **kw):
@@ -278,13 +278,25 @@ EDGE = [
     # split into 32-row tiles, and no big-tile kernel is launched
     ("small_batch_split_experts", _edge("edge_split", T=90, E=4, k=2, H=256, I=128,
                                         seed_index=47), None),
+    # a qA per expert (each expert's scale from its own rows): the requantization must use
+    # the scale of the row's expert in every kernel instance -- small tiles, big tiles with
+    # 2 and 4 row groups per wave, and the 65536-row kernels
+    ("qa_per_expert_small", _edge("edge_qa_s", T=24, E=16, k=4, seed_index=48), "qa"),
+    ("qa_per_expert_big", _edge("edge_qa_b", T=300, E=4, k=4, H=256, I=128, seed_index=49),
+     "qa"),
+    ("qa_per_expert_mid", _edge("edge_qa_m", T=400, E=8, k=4, H=384, I=128, seed_index=50),
+     "qa"),
+    ("qa_per_expert_many_rows", _edge("edge_qa_many", T=8192, E=64, k=8, H=512, I=256,
+                                      zipf_s=1.0, seed_index=51), "qa"),
 ]
 
 
 @pytest.mark.parametrize("name,cfg,mod", EDGE, ids=[c[0] for c in EDGE])
 def test_layer_edge_cases(name, cfg, mod):
     _say(f"layer edge {name}")
-    p = build_layer_problem(cfg)
+    p = build_layer_problem(cfg, per_expert_qa=(mod == "qa"))
+    if mod == "qa":
+        assert len(np.unique(p["qA"])) == cfg.E
     if mod == "same":
         p["ids"] = p["ids"].copy()
         p["ids"][:, 0] = 5                   # every token's first pick is expert 5
@@ -293,8 +305,8 @@ def test_layer_edge_cases(name, cfg, mod):
         p["ids"][:, 1] = p["ids"][:, 0]
     ref = oracle_forward(p)
     _, out, inter = _run_layer(p)
-    st, ratio = compare.check_layer(p, out, inter, ref)
-    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, worst err/(2e-2 rms) {ratio:.3f}")
+    st, res = compare.check_layer(p, out, inter, ref)
+    _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, {compare.fmt(res)}")
 
 
 def test_layer_determinism_poisoned_workspace_and_reuse():

@@ -50,8 +50,8 @@ def layer():
     batch = host(L.forward().clone(), np.uint16)
     L.check_guards()
     # the batch output is the oracle-checked reference of every streamed run
-    st, ratio = compare.check_layer(p, batch, L.intermediates(), oracle_forward(p))
-    _say(f"batch vs oracle: code diffs {st['n_diff']}/{st['n_codes']}, ratio {ratio:.3f}")
+    st, res = compare.check_layer(p, batch, L.intermediates(), oracle_forward(p))
+    _say(f"batch vs oracle: code diffs {st['n_diff']}/{st['n_codes']}, {compare.fmt(res)}")
     return p, L, batch
 
 

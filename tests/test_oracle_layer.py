@@ -110,7 +110,7 @@ def test_gate_rows_come_before_up_rows():
     g = np.array([1.5, 3, -2, 0.5] * 4); u = np.array([3, 1.5, 0.5, -2] * 4)
     w13d = np.zeros((2 * I, H)); w13d[:I, 0] = g; w13d[I:, 0] = u
     w2d = np.zeros((H, I)); w2d[0, 0] = 1.0
-    h, a, ac, as_, o = olayer._expert_rows(xdec, w13d, w2d, 1.0, 1.0, 1.0, 4.0, 25.0)
+    h, a, ac, as_, o = olayer.expert_rows(xdec, w13d, w2d, 1.0, 1.0, 1.0, 4.0, 25.0)
     assert np.array_equal(a[0], oracle.situ(g.astype(np.float32), u.astype(np.float32)))
     assert not np.array_equal(a[0], oracle.situ(u.astype(np.float32), g.astype(np.float32)))
 
@@ -153,3 +153,39 @@ def test_duplicate_expert_in_a_token_is_two_rows():
     d = oracle_dense(p)
     assert np.array_equal(g["out"], d["out"])
     assert g["counts"].sum() == p["cfg"].T * p["cfg"].k
+
+
+@pytest.mark.parametrize("ntok", [12, 2], ids=["every_expert_seen", "some_experts_unseen"])
+def test_intermediate_calibration_against_dense_brute_force(ntok):
+    """The calibration pass behind qA: a brute force over every (token, pick) pair of the
+    calibration tokens, decoding through torch's float8 type, with a running max of
+    |SiTU output| per expert; the shared and the per-expert scales follow from it."""
+    cfg = dataclasses.replace(TINY, name="calib", T=12, seed_index=70, per_expert_situ=True)
+    p = build_layer_problem(cfg)
+    I, E = cfg.I, cfg.E
+    toks = np.arange(ntok)
+    xc, xs = oracle.quantize_nvfp4(oracle.bf16_bits_to_f32(p["x"][toks]), p["qX"])
+    xdec = _torch_decode(oracle.pack_nibbles(xc), xs)
+    want = np.zeros(E, np.float32)
+    for t in toks:
+        for j in range(cfg.k):
+            e = int(p["ids"][t, j])
+            w = _torch_decode(p["w13"][e], p["w13_sf"][e])
+            h = ((xdec[t] @ w.T).numpy().astype(np.float32) * p["alpha1"][e]).astype(np.float32)
+            a = oracle.situ(h[:I], h[I:], p["beta"][e], p["lam"][e])
+            want[e] = max(want[e], np.float32(np.max(np.abs(a))))
+    args = (toks, p["x"], p["ids"], p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], p["qX"],
+            p["alpha1"], p["beta"], p["lam"])
+    got = oracle.intermediate_amax_per_expert(*args)
+    assert np.array_equal(got, want)
+    assert oracle.intermediate_amax(*args) == want.max()
+    seen = want > 0
+    assert seen.all() == (ntok == 12)
+    dA, qA = oracle.calibrate_intermediate_per_expert(*args)
+    d_shared = np.float32(want.max() / np.float32(2688.0))
+    assert np.array_equal(dA[seen], (want[seen] / np.float32(2688.0)).astype(np.float32))
+    assert np.all(dA[~seen] == d_shared)
+    assert np.array_equal(qA, (np.float32(1.0) / dA).astype(np.float32))
+    assert len(np.unique(dA[seen])) > 1                       # distinct per expert
+    dS, qS = oracle.calibrate_intermediate(*args)
+    assert np.all(dS == d_shared) and np.all(qS == np.float32(1.0) / d_shared)
