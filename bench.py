@@ -7,8 +7,10 @@ TP8-local shape H=3584, I=384, E=896, top-16, with every input already resident 
 
 The headline line reports the prefill batch (T=16384, per-expert SiTU parameters, 0.5%
 outlier channels x30): tokens/s, and the roofline of its dominant kernel (the FC1 grouped
-GEMM, bound by the f16 MFMA).  The decode (T=16) and mid (T=1024, Zipf 1.0) batches are
-reported under "workloads" with their HBM rooflines, and the routing-and-int8-permute
+GEMM, bound by the f16 MFMA).  The decode (T=16), mid (T=1024, Zipf 1.0) batches and the
+band edges T=64 (decode) and T=4096 (prefill) are reported under "workloads" with their
+HBM rooflines, per-step medians and spreads (at least 50 timed steps each) and the same
+step captured into a graph and replayed; and the routing-and-int8-permute
 primitive (moe_route, N=8192, H=7168, E=256, K=8) under "routing_primitive" with its
 routed rows/s and HBM fraction, and two cases of its options (moe_route_v2) under
 "routing_primitive.options", and the layer through the chunk-streamed front end
@@ -16,7 +18,8 @@ routed rows/s and HBM fraction, and two cases of its options (moe_route_v2) unde
 the stages on the launch stream (moe_forward_timed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workloads prefill,decode,mid,route,stream] [--summarize DIR]
+                       [--workloads prefill,decode,mid,decode64,prefill4k,route,stream]
+                       [--summarize DIR]
 """
 
 import argparse
@@ -38,6 +41,7 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16/bf16 MFMA
 FC1_BYTES_PER_EXPERT = 768 * 1792 + 768 * 224          # codes + E4M3 scales
 FC2_BYTES_PER_EXPERT = 3584 * 192 + 3584 * 24
 STAGES = ("quantize_x", "route", "fc1_situ_requant", "fc2", "finalize")
+MIN_SUB_STEPS = 50             # timed steps of every batch but the headline one
 CSRC = os.path.join(ROOT, "routed_moe_layer_amd", "csrc")
 
 
@@ -189,6 +193,9 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     for e in evs:
         events.destroy(e)
     ms_per_step = wall * 1e3 / steps
+    graph = graph_replay_ms(lambda i, stream: rm.moe_forward(
+        dims, T, x, ids[i], rw, prepared, qx, alpha1, qa, alpha2, beta, lam, ws, out,
+        stream=stream), rotations, torch, steps, warmup, events)
     # algorithmic work
     distinct = np.mean([len(np.unique(a)) for a in ids_host])
     weight_bytes = distinct * (FC1_BYTES_PER_EXPERT + FC2_BYTES_PER_EXPERT)
@@ -200,7 +207,12 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     res = {
         "workload": cfg.name, "T": T, "tokens_per_s": T / (ms_per_step * 1e-3),
         "ms_per_step": ms_per_step, "gpu_ms_per_step": float(np.mean(gpu_ms)),
-        "stage_ms": st, "distinct_experts": float(distinct),
+        "steps": steps, "gpu_ms_step_stats": _stats(gpu_ms),
+        "graph_replay_ms_step_stats": graph,
+        "graph_replay_tokens_per_s": T / (graph["median"] * 1e-3),
+        "stage_ms": st, "stage_ms_median": {name: float(np.median(stage_ms[:, j]))
+                                            for j, name in enumerate(STAGES)},
+        "distinct_experts": float(distinct),
         "algorithmic_bytes": float(weight_bytes + act_bytes),
         "hbm_frac_of_step": (weight_bytes + act_bytes) / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "flops": fc1_flops + fc2_flops,
@@ -213,6 +225,44 @@ def layer_workload(cfg, torch, rm, prepared, d13, d2, steps, warmup, events, rot
     keep = dict(x=x, ids=ids_host[0], rw=rw, qx=qx, alpha1=alpha1, qa=qa, alpha2=alpha2,
                 beta=beta, lam=lam)
     return res, keep
+
+
+def _stats(ms):
+    """Median, spread and extremes (ms) of per-step times."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "min": float(a.min()), "max": float(a.max()),
+            "n": int(a.size)}
+
+
+def graph_replay_ms(capture_call, rotations, torch, steps, warmup, events):
+    """Per-step times (ms) of the layer call captured into a graph and replayed ("Cake SiTU
+    backend", "Caller-owned execution": the caller may capture and replay): one graph per
+    input rotation, replayed in turn, each replay bracketed by events on the launch stream."""
+    side = torch.cuda.Stream()
+    graphs = []
+    torch.cuda.synchronize()
+    for i in range(rotations):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            capture_call(i, side)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % rotations].replay()
+    torch.cuda.synchronize()
+    evs = [events.create(2) for _ in range(steps)]
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(steps):
+        events.record(evs[i][0], stream)
+        graphs[i % rotations].replay()
+        events.record(evs[i][1], stream)
+    torch.cuda.synchronize()
+    ms = [events.elapsed_ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        events.destroy(e)
+    del graphs
+    return _stats(ms)
 
 
 # The chunk-streamed front end: (layer workload, tokens per slot, ring slots).
@@ -672,7 +722,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="prefill,decode,mid,route,stream")
+    ap.add_argument("--workloads",
+                    default="prefill,decode,mid,decode64,prefill4k,route,stream")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens of the oracle's bounded CPU sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -690,7 +741,7 @@ def main():
 
     import torch
     import routed_moe_layer_amd as rm
-    from moe_inputs import DECODE_16, MID_1024, PREFILL_16K, ROUTE_8K
+    from moe_inputs import DECODE_16, MID_1024, PREFILL_16K, ROUTE_8K, DECODE_64, PREFILL_4K
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.copy_calibration:
@@ -707,7 +758,8 @@ def main():
     chosen = [w.strip() for w in args.workloads.split(",") if w.strip() and w.strip() != "stream"]
     if any(c != "route" for c in chosen):
         prepared, d13, d2 = build_weights(DECODE_16, torch, rm)
-    cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4)}
+    cfgs = {"prefill": (PREFILL_16K, 1), "decode": (DECODE_16, 8), "mid": (MID_1024, 4),
+            "decode64": (DECODE_64, 4), "prefill4k": (PREFILL_4K, 1)}
     results, keeps = {}, {}
     route_res = None
     if "route" in chosen:
@@ -729,14 +781,19 @@ def main():
             route_res["options"][case] = r
             log(f"  {r['workload']}: {r['us_per_call']:.1f} us/call, {r['routed_rows']} rows, "
                 f"{100 * r['hbm_frac']:.1f}% of HBM peak")
+    head = "prefill" if "prefill" in chosen else (chosen[0] if chosen else None)
     for name in chosen:
         cfg, rot = cfgs[name]
-        log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+        # the headline batch times exactly --steps steps; the others at least 50 (cheap)
+        steps = args.steps if name == head else max(args.steps, MIN_SUB_STEPS)
+        log(f"timing {cfg.name}: warmup {args.warmup}, steps {steps}")
         results[name], keeps[name] = layer_workload(cfg, torch, rm, prepared, d13, d2,
-                                                    args.steps, args.warmup, events, rot)
+                                                    steps, args.warmup, events, rot)
         r = results[name]
-        log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step, stages "
-            + ", ".join(f"{k} {v:.3f}" for k, v in r["stage_ms"].items()))
+        log(f"  {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step "
+            f"(median {r['gpu_ms_step_stats']['median']:.4f}, graph replay median "
+            f"{r['graph_replay_ms_step_stats']['median']:.4f}), stages "
+            + ", ".join(f"{k} {v:.4f}" for k, v in r["stage_ms_median"].items()))
     streamed = {}
     if "stream" in [w.strip() for w in args.workloads.split(",")]:
         for name, (chunk, slots) in STREAM_CASES.items():
@@ -755,7 +812,6 @@ def main():
     if not chosen:                      # routing primitive only
         print(json.dumps({"routing_primitive": route_res}), flush=True)
         return
-    head = "prefill" if "prefill" in results else chosen[0]
     hr = results[head]
     hcfg = cfgs[head][0]
     fc1_ms = hr["fc1"]["ms"]

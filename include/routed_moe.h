@@ -89,8 +89,9 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   o_rows    f16  [T*k, H]   FC2 output O of routed row (t, j) at row t*k + j, alpha2
  *                             applied, stored as O * 2^s with s the exponent of its
  *                             32-column segment (rows of dropped ids are not written)
- *   o_exp     i8   [T*k, H/32] s of each segment: the segment's largest |O| * 2^s lies
- *                             in [2^14, 2^15] (s = 0 for an all-zero segment)
+ *   o_exp     i8   [T, H/32, k] s of segment c of routed row (t, j) at [t, c, j]: the
+ *                             segment's largest |O| * 2^s lies in [2^14, 2^15] (s = 0 for
+ *                             an all-zero segment)
  *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
  *                             (0 for an expert with no rows; a calibration statistic) */
 typedef struct {

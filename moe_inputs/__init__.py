@@ -81,7 +81,17 @@ PREFILL_16K = LayerConfig("layer_T16384_H3584_I384_E896_k16_uniform_situE", T=16
                           outlier_mult=30.0, per_expert_situ=True, seed_index=4,
                           weight_seed_index=2)
 
-LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE_16, MID_1024, PREFILL_16K)}
+# The edges of the two target bands: the largest decode batch (T=64, uniform picks, as the
+# T=16 batch) and the smallest prefill batch (T=4096, as the T=16384 batch).
+DECODE_64 = LayerConfig("layer_T64_H3584_I384_E896_k16_uniform", T=64, H=3584, I=384, E=896,
+                        k=16, w_std=0.02, seed_index=5, weight_seed_index=2)
+PREFILL_4K = LayerConfig("layer_T4096_H3584_I384_E896_k16_uniform_situE", T=4096, H=3584,
+                         I=384, E=896, k=16, w_std=0.02, outlier_frac=0.005,
+                         outlier_mult=30.0, per_expert_situ=True, seed_index=6,
+                         weight_seed_index=2)
+
+LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE_16, MID_1024, PREFILL_16K, DECODE_64,
+                                     PREFILL_4K)}
 
 
 def _rng(seed_index, tag, index=0):

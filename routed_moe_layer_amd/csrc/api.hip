@@ -360,6 +360,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
 
   LayerArgs a{};
   a.H = H; a.I = I; a.Ip = padded_inter(I); a.E = E; a.k = k; a.T = T;
+  a.k_inv = ((uint64_t{1} << 32) + static_cast<uint64_t>(k) - 1) / static_cast<uint64_t>(k);
   a.x_codes = ws + L.pub.x_codes;
   a.x_scales = ws + L.pub.x_scales;
   a.x_dec = reinterpret_cast<const uint16_t*>(ws + L.pub.x_dec);

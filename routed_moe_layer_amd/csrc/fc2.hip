@@ -58,12 +58,12 @@ __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int l
 template <int NW, int WRG, int BN, int NCBA, int NCH>
 __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
                                          int nslabs, const _Float16* __restrict__ s_tok,
-                                         float* __restrict__ s_out) {
+                                         uint16_t* __restrict__ s_out) {
   constexpr int kSlabGroups = NW * WRG;                 // 16-row groups per slab
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int e = td.expert;
   const int last = slab0 + nslabs - 1;
-  const float al = a.alpha2[e];
+  const OutScale osc = out_scale_of(a.alpha2[e]);
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
   // FC2 rows are stored at their flat id t*k + j, so that the finalization reads each
   // token's k rows as one contiguous run; lane l holds the flat id of block row l % 16
@@ -73,7 +73,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
     const int n = min(cb * 16 + (lane & 15), td.nrows - 1);
     flat_cb[cb] = a.sorted_row_idx[td.row_start + n];
   }
-  float* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
+  uint16_t* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
   f32x4 acc[WRG][NCBA];
 
   auto decode = [&](const W2Regs<WRG>& cur, const int s, f16x8 (&wf)[WRG]) {
@@ -130,8 +130,8 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
         f32x4 blk[WRG];
 #pragma unroll
         for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
-        store_out_block<WRG>(blk, al, wave_out, lane, flat_cb[cb], td.nrows - cb * 16, a.o_rows,
-                             a.o_exp, a.H, 16 * G0);
+        store_out_block<WRG>(blk, osc, wave_out, lane, flat_cb[cb], td.nrows - cb * 16, a.o_rows,
+                             a.o_exp, a.H, a.k, a.k_inv, 16 * G0);
       }
       // the next slab's MFMAs (fresh accumulators) stay after these stores, so the two
       // accumulator sets are never live together
@@ -160,7 +160,7 @@ template <int NW, int WRG, int BN, int SPW, int SPLIT>
 __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   __shared__ _Float16 s_tok[BN * kFc2LdsRow];
   __shared__ int64_t s_row[BN];
-  __shared__ __attribute__((aligned(16))) float s_out[NW * 16 * out_lds_stride<WRG>()];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * out_lds_stride<WRG>()];
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
   const int ntiles = a.num_tiles[big];
   const int n_slabs = a.H / (NW * WRG * 16);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
   constexpr int kThreads = NW * 64;
   static_assert(kFc2StationaryGrid % kXcds == 0, "whole XCD strides");
   __shared__ __attribute__((aligned(16))) _Float16 s_tok[kFc2PassRows * kFc2LdsRow];
-  __shared__ __attribute__((aligned(16))) float s_out[NW * 16 * out_lds_stride<WRG>()];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * out_lds_stride<WRG>()];
 
   const int n_slabs = a.H / (kSlabGroups * 16);
   const int n_runs = a.num_tiles[2];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
   const int code_bytes = a.I / 2, scale_cols = a.I / 16;
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
-  float* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
+  uint16_t* wave_out = s_out + w * 16 * out_lds_stride<WRG>();
 
   // Token rows [p0, p0 + nr) of the run (rows past nr repeat the last one; they are not
   // stored).  Four threads per row, each NCH 16-byte pieces of codes (32 values) and the
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
 #pragma unroll
       for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
 
-    const float al = a.alpha2[e];
+    const OutScale osc = out_scale_of(a.alpha2[e]);
     const int col0 = 16 * (slab * kSlabGroups + w * WRG);
     int32_t flat[kFc2PassRows / 16];
     int p0 = rd.row_start;
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
         f32x4 blk[WRG];
 #pragma unroll
         for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
-        store_out_block<WRG>(blk, al, wave_out, lane, flat[cb], nr - cb * 16, a.o_rows, a.o_exp,
-                             a.H, col0);
+        store_out_block<WRG>(blk, osc, wave_out, lane, flat[cb], nr - cb * 16, a.o_rows, a.o_exp,
+                             a.H, a.k, a.k_inv, col0);
       }
     };
 

@@ -405,11 +405,11 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
   } else {
     // the K loop's token buffers are free once every wave has passed its last chunk; each
     // wave then stages its output blocks in its own part of them
-    static_assert(sizeof(_Float16) * 2 * BN * Stage::kLdsRow >=
-                      sizeof(float) * NW * 16 * out_lds_stride<WRG>(), "output staging space");
+    static_assert(2 * BN * Stage::kLdsRow >= NW * 16 * out_lds_stride<WRG>(),
+                  "output staging space");
     __syncthreads();
-    float* lds = reinterpret_cast<float*>(&s_tok[0][0]) + t.w * 16 * out_lds_stride<WRG>();
-    const float al = a.alpha2[e];
+    uint16_t* lds = reinterpret_cast<uint16_t*>(&s_tok[0][0]) + t.w * 16 * out_lds_stride<WRG>();
+    const OutScale osc = out_scale_of(a.alpha2[e]);
 #pragma unroll
     for (int cb = 0; cb < NCBA; ++cb) {
       // stored at the row's flat id t*k + j (the finalization reads a token's rows as
@@ -419,8 +419,8 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
       f32x4 blk[WRG];
 #pragma unroll
       for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
-      store_out_block<WRG>(blk, al, lds, lane, flat, td.nrows - cb * 16, a.o_rows, a.o_exp,
-                           a.H, 16 * G0);
+      store_out_block<WRG>(blk, osc, lds, lane, flat, td.nrows - cb * 16, a.o_rows, a.o_exp,
+                           a.H, a.k, a.k_inv, 16 * G0);
     }
   }
 }
@@ -501,19 +501,26 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 // accumulates them.
 constexpr int kFinThreads = 512, kFinBatch = 8;
 
+// K8: k is a multiple of kFinBatch, so each batch's exponents are one 8-byte load; else
+// one byte load per row (index clamped: every load is unconditional and the loads of a
+// batch stay in flight together).
+template <bool K8>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
   const int64_t t = blockIdx.x / col_blocks;
   const int v = (blockIdx.x % col_blocks) * blockDim.x + threadIdx.x;
   if (v >= a.H / 8) return;
   const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
-  const int segs = a.H / kOutSeg;
-  const int8_t* __restrict__ exp_t = a.o_exp + t * a.k * segs + v / (kOutSeg / 8);
+  // the k exponents of this thread's 32-column segment, in j order
+  const int8_t* __restrict__ exp_v =
+      a.o_exp + (t * (a.H / kOutSeg) + v / (kOutSeg / 8)) * a.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
     u32x4 d[kFinBatch];
     int32_t sx[kFinBatch];
     bool ok[kFinBatch];
+    uint2 e8;
+    if constexpr (K8) e8 = *reinterpret_cast<const uint2*>(exp_v + j0);
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
       const int j = j0 + u;
@@ -522,7 +529,10 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
       d[u] = ok[u] ? __builtin_nontemporal_load(
                          reinterpret_cast<const u32x4*>(a.o_rows + (t * a.k + j) * a.H) + v)
                    : u32x4{0u, 0u, 0u, 0u};
-      sx[u] = ok[u] ? exp_t[j * segs] : 0;
+      if constexpr (K8)
+        sx[u] = static_cast<int8_t>(((u < 4 ? e8.x : e8.y) >> (8 * (u & 3))) & 0xFFu);
+      else
+        sx[u] = exp_v[min(j, a.k - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
@@ -631,8 +641,10 @@ hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
   const int per_block = (vecs + col_blocks - 1) / col_blocks;
   const int threads = (per_block + 63) / 64 * 64;
   const int64_t grid = static_cast<int64_t>(a.T) * col_blocks;
-  if (grid > 0)
-    finalize_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
+  if (grid > 0 && a.k % kFinBatch == 0)
+    finalize_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
+  else if (grid > 0)
+    finalize_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
   return hipGetLastError();
 }
 

@@ -133,6 +133,8 @@ class DeviceLayer:
             "a_codes": take("a_codes", R * cfg.I // 2, np.uint8, (R, cfg.I // 2)),
             "a_scales": take("a_scales", R * cfg.I // 16, np.uint8, (R, cfg.I // 16)),
             "o_rows": _fc2_rows(take("o_rows", R * cfg.H, np.float16, (R, cfg.H)),
-                                take("o_exp", R * (cfg.H // 32), np.int8, (R, cfg.H // 32))),
+                                take("o_exp", R * (cfg.H // 32), np.int8,
+                                     (T, cfg.H // 32, cfg.k)).transpose(0, 2, 1)
+                                .reshape(R, cfg.H // 32)),
             "a_amax": take("a_amax", cfg.E, np.float32, (cfg.E,)),
         }
