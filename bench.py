@@ -373,15 +373,33 @@ def route_workload(cfg, torch, rm, steps, warmup, events):
     ws = torch.empty(rm.moe_route_workspace_size(N, K, E), dtype=torch.uint8, device="cuda")
 
     def call():
-        rm.moe_route(N, H, E, K, x, ids, rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs, sid,
-                     sri, ws)
+        rm.moe_route(rm.MoeDims(H, 0, E, K), N, x, ids, rm.MOE_QUANT_INT8_ROW_DYNAMIC, None, sid,
+                     sri, eri, cs, ex, esc, ws)
 
     gpu_ms, wall_ms = _time_calls(call, torch, steps, warmup, events)
     nbytes = N * H * 2 + R * 4 + R * H + R * 4 + 3 * R * 4 + E * 4
-    return {"workload": cfg.name, "N": N, "routed_rows_per_s": R / (gpu_ms * 1e-3),
-            "ms_per_call": gpu_ms, "wall_ms_per_call": wall_ms,
-            "algorithmic_bytes": float(nbytes),
-            "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
+    res = {"workload": cfg.name, "N": N, "routed_rows_per_s": R / (gpu_ms * 1e-3),
+           "ms_per_call": gpu_ms, "wall_ms_per_call": wall_ms,
+           "algorithmic_bytes": float(nbytes),
+           "hbm_frac": nbytes / (gpu_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)}
+    # the same routing with the layer's NVFP4 quantization of the moved rows (qx from the
+    # tokens' amax); bytes: x once, the ids, expanded codes and scales, three index arrays
+    amax = x.view(torch.bfloat16).float().abs().amax()
+    qx = (2688.0 / torch.where(amax > 0, amax, torch.ones_like(amax))).reshape(1).contiguous()
+    exf = torch.empty((R, H // 2), dtype=torch.uint8, device="cuda")
+    esf = torch.empty((R, H // 16), dtype=torch.uint8, device="cuda")
+
+    def call_fp4():
+        rm.moe_route(rm.MoeDims(H, 0, E, K), N, x, ids, rm.MOE_QUANT_NVFP4_G16, qx, sid, sri, eri,
+                     cs, exf, esf, ws)
+
+    g4, w4 = _time_calls(call_fp4, torch, steps, warmup, events)
+    b4 = N * H * 2 + R * 4 + R * (H // 2 + H // 16) + 3 * R * 4 + E * 4
+    res["nvfp4"] = {"workload": cfg.name.replace("_int8", "_nvfp4"), "ms_per_call": g4,
+                    "wall_ms_per_call": w4, "routed_rows_per_s": R / (g4 * 1e-3),
+                    "algorithmic_bytes": float(b4),
+                    "hbm_frac": b4 / (g4 * 1e-3) / (PEAK_HBM_GBS * 1e9)}
+    return res
 
 
 # The routing page's two named fast cases, through moe_route_v2 on the routing workload's
@@ -768,6 +786,8 @@ def main():
         route_res = route_workload(ROUTE_8K, torch, rm, args.steps, args.warmup, events)
         log(f"  {route_res['routed_rows_per_s']:.3e} routed rows/s, {route_res['ms_per_call']:.3f} ms, "
             f"{100 * route_res['hbm_frac']:.1f}% of HBM peak")
+        r4 = route_res["nvfp4"]
+        log(f"  {r4['workload']}: {r4['ms_per_call']:.3f} ms, {100 * r4['hbm_frac']:.1f}% of HBM peak")
         route_res["topk"] = {}
         for T in (16384, 16):
             r = topk_workload(T, 896, 16, torch, rm, args.steps, args.warmup, events)

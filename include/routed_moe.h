@@ -55,6 +55,19 @@ typedef struct {
 /* Largest token count of one moe_forward call ("Cake SiTU backend", intro: 1..16384). */
 #define MOE_MAX_TOKENS 16384
 
+/* Quantization of the tokens a call moves or computes on:
+ *   MOE_QUANT_NONE             BF16 as given;
+ *   MOE_QUANT_INT8_ROW_DYNAMIC per-row dynamic int8 ("torch_npu.npu_moe_init_routing_v2",
+ *                              section 计算公式 step 4: scale = row_max|x| / 127);
+ *   MOE_QUANT_NVFP4_G16        group-16 NVFP4 with the global encoding scale qx, the
+ *                              layer's input quantization ("Cake SiTU backend", intro; the
+ *                              arithmetic is given at moe_quantize_nvfp4). */
+typedef enum {
+  MOE_QUANT_NONE = 0,
+  MOE_QUANT_INT8_ROW_DYNAMIC = 1,
+  MOE_QUANT_NVFP4_G16 = 2
+} moe_quant_t;
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* moe_status_string(moe_status_t s);
 
@@ -63,9 +76,13 @@ const char* moe_status_string(moe_status_t s);
  * "Caller-owned execution": the size query uses host metadata only).
  * ------------------------------------------------------------------------------------ */
 
-/* Workspace bytes of moe_forward for any T <= max_tokens.  Monotone in max_tokens, so a
- * buffer sized for the maximum serves every smaller call (same section). */
-moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, size_t* bytes /*host*/);
+/* Workspace bytes for every T <= max_tokens of moe_route with quantization q and, when q
+ * is MOE_QUANT_NVFP4_G16 (the layer's quantization), of moe_forward too; the layer's
+ * limits on d and T (<= MOE_MAX_TOKENS) then apply.  moe_route reads only d.hidden,
+ * d.num_experts and d.top_k.  Monotone in max_tokens, so a buffer sized for the maximum
+ * serves every smaller call (same section). */
+moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, moe_quant_t q,
+                                size_t* bytes /*host*/);
 
 /* Bytes of the prepared (re-laid-out) weights written by moe_prepare_weights: the FC1 and
  * FC2 codes and block scales, E * (2I*H/2 + 2I*H/16 + H*Ip/2 + H*Ip/16) with Ip = I
@@ -106,7 +123,8 @@ typedef struct {
 
 moe_status_t moe_workspace_layout(moe_dims_t d, int32_t T, moe_workspace_layout_t* out /*host*/);
 
-/* Workspace bytes of moe_route and moe_route_v2 for num_rows tokens, top_k, num_experts. */
+/* Workspace bytes of moe_route and moe_route_v2 for num_rows tokens, top_k, num_experts
+ * (moe_workspace_size with q other than MOE_QUANT_NVFP4_G16 returns the same). */
 moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t num_experts,
                                       size_t* bytes /*host*/);
 
@@ -141,31 +159,32 @@ moe_status_t moe_prepare_weights(moe_dims_t d, const uint8_t* w13, const uint8_t
 
 /* ------------------------------------------------------------------------------------
  * The routing primitive ("torch_npu.npu_moe_init_routing_v2", section 计算公式, steps
- * 1-5, dropless, full expert range, gather index type 0, cumsum histogram type 0):
- *   sorted_expert_idx, sorted_row_idx = stable keyValueSort(expert_idx, f = t*K + j)
+ * 1-5, dropless, full expert range, gather index type 0, cumsum histogram type 0), with
+ * the token movement quantized as q:
+ *   sorted_expert_ids, sorted_row_idx = stable keyValueSort(expert_ids, f = t*k + j)
  *   expanded_row_idx[sorted_row_idx[i]] = i
  *   expert_cumsum[e] = number of rows with expert <= e          (inclusive)
- *   quant MOE_ROUTE_QUANT_NONE:          expanded_x[i] = x[sorted_row_idx[i] / K]  (BF16)
- *   quant MOE_ROUTE_QUANT_INT8_DYNAMIC:  scale_t = fp32(row_max|x_t| / 127),
+ *   q MOE_QUANT_NONE:             expanded_x[i] = x[sorted_row_idx[i] / k]  (BF16 [T*k, H])
+ *   q MOE_QUANT_INT8_ROW_DYNAMIC: scale_t = fp32(row_max|x_t| / 127),
  *        q_t = clip(round_half_even(fp32(x_t / scale_t)), -127, 127) (0 if scale_t == 0),
- *        expanded_x[i] = q_{sorted_row_idx[i]/K} (int8), expanded_scale[i] = scale_t.
- * Buffers (device): x BF16 [N, H]; expert_idx i32 [N, K] with values in [0, E);
- * expanded_x [N*K, H] (BF16 or int8); expanded_scale f32 [N*K] (INT8 mode; else NULL);
- * expanded_row_idx, sorted_expert_idx, sorted_row_idx i32 [N*K] (the last two may be
- * NULL); expert_cumsum i32 [E].  Limits: 1 <= N, N*K <= 2^24, H % 8 == 0, H <= 65536,
- * 1 <= E <= 4096, 1 <= K <= 64.
+ *        expanded_x[i] = q_{sorted_row_idx[i]/k} (int8 [T*k, H]),
+ *        expanded_sf_or_scale[i] = scale_t (f32 [T*k]);
+ *   q MOE_QUANT_NVFP4_G16:        token t quantized as moe_quantize_nvfp4 with q = *qx,
+ *        expanded_x[i] = its codes (u8 [T*k, H/2]), expanded_sf_or_scale[i] = its E4M3
+ *        block scales (u8 [T*k, H/16]), t = sorted_row_idx[i] / k (one read of each token,
+ *        one quantization, its k rows written).
+ * Buffers (device): x BF16 [T, H]; expert_ids i32 [T, k] with values in [0, E);
+ * qx f32 [1] (NVFP4 only, else may be NULL); expanded_sf_or_scale NULL for MOE_QUANT_NONE;
+ * expanded_row_idx, sorted_expert_ids, sorted_row_idx i32 [T*k] (the last two may be
+ * NULL); expert_cumsum i32 [E].  d.inter is not used.  Limits: 1 <= T, T*k <= 2^24,
+ * H % 8 == 0 (H % 16 == 0 for NVFP4), H <= 65536, 1 <= E <= 4096, 1 <= k <= 64.
+ * workspace: moe_workspace_size(d, T, q) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------------------ */
-typedef enum {
-  MOE_ROUTE_QUANT_NONE = 0,
-  MOE_ROUTE_QUANT_INT8_DYNAMIC = 1
-} moe_route_quant_t;
-
-moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
-                       const uint16_t* x, const int32_t* expert_idx, moe_route_quant_t quant,
-                       void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
-                       int32_t* expert_cumsum, int32_t* sorted_expert_idx,
-                       int32_t* sorted_row_idx, void* workspace, size_t workspace_bytes,
-                       moe_stream_t stream);
+moe_status_t moe_route(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
+                       moe_quant_t q, const float* qx, int32_t* sorted_expert_ids,
+                       int32_t* sorted_row_idx, int32_t* expanded_row_idx,
+                       int32_t* expert_cumsum, void* expanded_x, void* expanded_sf_or_scale,
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * The routing primitive with the options of the same page ("torch_npu.

@@ -21,14 +21,16 @@ __all__ = [
     "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax", "MOE_RING_ROUTE",
     "MOE_RING_LAYOUT",
     "MOE_RING_OK", "MOE_RING_CONSUMER_TIMEOUT", "MOE_RING_PRODUCER_TIMEOUT",
-    "MOE_ROUTE_QUANT_NONE", "MOE_ROUTE_QUANT_INT8_DYNAMIC", "MOE_MAX_TOKENS", "EXPORTED",
+    "MOE_QUANT_NONE", "MOE_QUANT_INT8_ROW_DYNAMIC", "MOE_QUANT_NVFP4_G16", "MOE_MAX_TOKENS",
+    "EXPORTED",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "lib", "libroutedmoe.so")
 
-MOE_ROUTE_QUANT_NONE = 0
-MOE_ROUTE_QUANT_INT8_DYNAMIC = 1
+MOE_QUANT_NONE = 0
+MOE_QUANT_INT8_ROW_DYNAMIC = 1
+MOE_QUANT_NVFP4_G16 = 2
 MOE_MAX_TOKENS = 16384
 MOE_FORWARD_STAGES = 5
 
@@ -107,13 +109,13 @@ def _lib():
         st = ctypes.c_int
         sig = {
             "moe_status_string": (ctypes.c_char_p, [st]),
-            "moe_workspace_size": (st, [MoeDims, I32, ctypes.POINTER(SZ)]),
+            "moe_workspace_size": (st, [MoeDims, I32, ctypes.c_int, ctypes.POINTER(SZ)]),
             "moe_prepared_weights_size": (st, [MoeDims, ctypes.POINTER(SZ)]),
             "moe_workspace_layout": (st, [MoeDims, I32, ctypes.POINTER(_Layout)]),
             "moe_route_workspace_size": (st, [I32, I32, I32, ctypes.POINTER(SZ)]),
             "moe_quantize_nvfp4": (st, [P, I64, I64, I32, P, P, P, P]),
             "moe_prepare_weights": (st, [MoeDims, P, P, P, P, P, SZ, P]),
-            "moe_route": (st, [I32, I32, I32, I32, P, P, ctypes.c_int, P, P, P, P, P, P, P, SZ, P]),
+            "moe_route": (st, [MoeDims, I32, P, P, ctypes.c_int, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_route_v2": (st, [I32, I32, I32, I32, P, P, P, P,
                                   ctypes.POINTER(MoeRouteOptions), P, P, P, P, P, P, SZ, P]),
             "moe_forward": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P]),
@@ -177,9 +179,10 @@ def moe_status_string(status):
     return _lib().moe_status_string(status).decode()
 
 
-def moe_workspace_size(dims, max_tokens):
+def moe_workspace_size(dims, max_tokens, quant=MOE_QUANT_NVFP4_G16):
     n = ctypes.c_size_t()
-    _check("moe_workspace_size", _lib().moe_workspace_size(dims, max_tokens, ctypes.byref(n)))
+    _check("moe_workspace_size",
+           _lib().moe_workspace_size(dims, max_tokens, quant, ctypes.byref(n)))
     return n.value
 
 
@@ -215,14 +218,14 @@ def moe_prepare_weights(dims, w13, w13_sf, w2, w2_sf, prepared, prepared_bytes=N
         _stream(stream)))
 
 
-def moe_route(num_rows, hidden, num_experts, top_k, x, expert_idx, quant, expanded_x,
-              expanded_scale, expanded_row_idx, expert_cumsum, sorted_expert_idx,
-              sorted_row_idx, workspace, workspace_bytes=None, stream=None):
+def moe_route(dims, T, x, expert_ids, quant, qx, sorted_expert_ids, sorted_row_idx,
+              expanded_row_idx, expert_cumsum, expanded_x, expanded_sf_or_scale, workspace,
+              workspace_bytes=None, stream=None):
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check("moe_route", _lib().moe_route(
-        num_rows, hidden, num_experts, top_k, _ptr(x), _ptr(expert_idx), quant, _ptr(expanded_x),
-        _ptr(expanded_scale), _ptr(expanded_row_idx), _ptr(expert_cumsum),
-        _ptr(sorted_expert_idx), _ptr(sorted_row_idx), _ptr(workspace), nb, _stream(stream)))
+        dims, T, _ptr(x), _ptr(expert_ids), quant, _ptr(qx), _ptr(sorted_expert_ids),
+        _ptr(sorted_row_idx), _ptr(expanded_row_idx), _ptr(expert_cumsum), _ptr(expanded_x),
+        _ptr(expanded_sf_or_scale), _ptr(workspace), nb, _stream(stream)))
 
 
 def moe_route_v2(num_rows, hidden, num_experts, top_k, x, expert_idx, options, expanded_x,

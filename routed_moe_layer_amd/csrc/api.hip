@@ -124,6 +124,15 @@ size_t prepared_bytes(const moe_dims_t& d) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Dimensions moe_route uses: hidden (a multiple of 8, of 16 for NVFP4), experts, top-k.
+moe_status_t route_dims_ok(const moe_dims_t& d, moe_quant_t q) {
+  if (d.hidden <= 0 || d.num_experts <= 0 || d.top_k <= 0) return MOE_ERR_INVALID_ARG;
+  if (d.hidden % (q == MOE_QUANT_NVFP4_G16 ? 16 : 8) || d.hidden > 65536)
+    return MOE_ERR_UNSUPPORTED;
+  if (d.num_experts > 4096 || d.top_k > 64) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,12 +148,25 @@ const char* moe_status_string(moe_status_t s) {
   return "unknown status";
 }
 
-moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, size_t* bytes) {
+moe_status_t moe_workspace_size(moe_dims_t d, int32_t max_tokens, moe_quant_t q,
+                                size_t* bytes) {
   if (!bytes) return MOE_ERR_INVALID_ARG;
-  moe_status_t st = check_dims(d);
+  if (q != MOE_QUANT_NONE && q != MOE_QUANT_INT8_ROW_DYNAMIC && q != MOE_QUANT_NVFP4_G16)
+    return MOE_ERR_INVALID_ARG;
+  size_t route = 0;
+  moe_status_t st = route_dims_ok(d, q);
+  if (st != MOE_OK) return st;
+  st = moe_route_workspace_size(max_tokens, d.top_k, d.num_experts, &route);
+  if (st != MOE_OK) return st;
+  if (q != MOE_QUANT_NVFP4_G16) {
+    *bytes = route;
+    return MOE_OK;
+  }
+  // the layer's quantization: moe_forward's workspace, which also serves moe_route
+  st = check_dims(d);
   if (st != MOE_OK) return st;
   if (max_tokens < 1 || max_tokens > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
-  *bytes = make_layout(d, max_tokens).pub.total;
+  *bytes = std::max(route, make_layout(d, max_tokens).pub.total);
   return MOE_OK;
 }
 
@@ -205,46 +227,57 @@ moe_status_t moe_prepare_weights(moe_dims_t d, const uint8_t* w13, const uint8_t
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_route(int32_t num_rows, int32_t hidden, int32_t num_experts, int32_t top_k,
-                       const uint16_t* x, const int32_t* expert_idx, moe_route_quant_t quant,
-                       void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
-                       int32_t* expert_cumsum, int32_t* sorted_expert_idx,
-                       int32_t* sorted_row_idx, void* workspace, size_t workspace_bytes,
-                       moe_stream_t stream) {
-  size_t need = 0;
-  moe_status_t st = moe_route_workspace_size(num_rows, top_k, num_experts, &need);
+moe_status_t moe_route(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
+                       moe_quant_t q, const float* qx, int32_t* sorted_expert_ids,
+                       int32_t* sorted_row_idx, int32_t* expanded_row_idx,
+                       int32_t* expert_cumsum, void* expanded_x, void* expanded_sf_or_scale,
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  if (q != MOE_QUANT_NONE && q != MOE_QUANT_INT8_ROW_DYNAMIC && q != MOE_QUANT_NVFP4_G16)
+    return MOE_ERR_INVALID_ARG;
+  moe_status_t st = route_dims_ok(d, q);
   if (st != MOE_OK) return st;
-  if (hidden < 8 || hidden % 8 || hidden > 65536) return MOE_ERR_UNSUPPORTED;
-  if (quant != MOE_ROUTE_QUANT_NONE && quant != MOE_ROUTE_QUANT_INT8_DYNAMIC)
+  size_t need = 0;
+  st = moe_route_workspace_size(T, d.top_k, d.num_experts, &need);
+  if (st != MOE_OK) return st;
+  const int H = d.hidden, E = d.num_experts, K = d.top_k;
+  if (!x || !expert_ids || !expanded_x || !expanded_row_idx || !expert_cumsum || !workspace)
     return MOE_ERR_INVALID_ARG;
-  if (!x || !expert_idx || !expanded_x || !expanded_row_idx || !expert_cumsum || !workspace)
+  if ((q == MOE_QUANT_INT8_ROW_DYNAMIC || q == MOE_QUANT_NVFP4_G16) && !expanded_sf_or_scale)
     return MOE_ERR_INVALID_ARG;
-  if (quant == MOE_ROUTE_QUANT_INT8_DYNAMIC && !expanded_scale) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(expanded_x, 16) || !aligned(workspace, kAlign))
+  if (q == MOE_QUANT_NVFP4_G16 && !qx) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(expanded_x, 16) || !aligned(workspace, kAlign) ||
+      !aligned(expert_ids, 4) || !aligned(expanded_row_idx, 4))
     return MOE_ERR_INVALID_ARG;
+  if (q == MOE_QUANT_NVFP4_G16 && !aligned(qx, 4)) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const int64_t n = static_cast<int64_t>(num_rows) * top_k;
+  const int64_t n = static_cast<int64_t>(T) * K;
   Carver c;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   RouteBuffers b{};
-  b.tile_hist = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(route_tiles(n)) * num_experts * 4));
-  b.counts = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts) * 4));
-  b.offsets = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(num_experts + 1) * 4));
+  b.tile_hist = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(route_tiles(n)) * E * 4));
+  b.counts = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(E) * 4));
+  b.offsets = reinterpret_cast<int32_t*>(ws + c.take(static_cast<size_t>(E + 1) * 4));
   b.cumsum = expert_cumsum;
-  b.sorted_ids = sorted_expert_idx;
+  b.sorted_ids = sorted_expert_ids;
   b.sorted_row_idx = sorted_row_idx;
   b.expanded_row_idx = expanded_row_idx;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (route_permute_fits_one_workgroup(n, num_experts, num_rows, hidden)) {
-    const PermuteArgs p{x, num_rows, hidden, top_k, static_cast<int>(quant), INT64_MAX,
-                        nullptr, nullptr, nullptr, expanded_x, expanded_scale};
-    return hip_status(launch_route_permute_small(expert_idx, n, num_experts, b, p, s));
+  if (q == MOE_QUANT_NVFP4_G16) {
+    if (launch_route(expert_ids, n, E, b, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_route_permute_nvfp4(
+        x, T, H, K, expanded_row_idx, qx, static_cast<uint8_t*>(expanded_x),
+        static_cast<uint8_t*>(expanded_sf_or_scale), s));
   }
-  hipError_t e = launch_route(expert_idx, n, num_experts, b, s);
+  float* expanded_scale = static_cast<float*>(expanded_sf_or_scale);
+  if (route_permute_fits_one_workgroup(n, E, T, H)) {
+    const PermuteArgs p{x, T, H, K, static_cast<int>(q), INT64_MAX, nullptr, nullptr, nullptr,
+                        expanded_x, expanded_scale};
+    return hip_status(launch_route_permute_small(expert_ids, n, E, b, p, s));
+  }
+  hipError_t e = launch_route(expert_ids, n, E, b, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_route_permute(x, num_rows, hidden, top_k, static_cast<int>(quant), expanded_row_idx,
-                           INT64_MAX, false, nullptr, nullptr, nullptr, expanded_x,
-                           expanded_scale, s);
+  e = launch_route_permute(x, T, H, K, static_cast<int>(q), expanded_row_idx, INT64_MAX, false,
+                           nullptr, nullptr, nullptr, expanded_x, expanded_scale, s);
   return hip_status(e);
 }
 
@@ -523,7 +556,7 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring, int32_t 
   if (static_cast<int64_t>(first_chunk) + num_chunks > chunks) return MOE_ERR_INVALID_ARG;
   if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
   size_t need = 0;
-  st = moe_workspace_size(d, static_cast<int32_t>(C), &need);
+  st = moe_workspace_size(d, static_cast<int32_t>(C), MOE_QUANT_NVFP4_G16, &need);
   if (st != MOE_OK) return st;
   if (!workspace || workspace_bytes < need) return workspace ? MOE_ERR_WORKSPACE_TOO_SMALL
                                                              : MOE_ERR_INVALID_ARG;
@@ -560,7 +593,7 @@ struct SealedLayout {
 static moe_status_t sealed_layout(moe_dims_t d, int32_t tokens, SealedLayout* out) {
   if (tokens < 1 || tokens > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
   size_t layer = 0;
-  moe_status_t st = moe_workspace_size(d, tokens, &layer);
+  moe_status_t st = moe_workspace_size(d, tokens, MOE_QUANT_NVFP4_G16, &layer);
   if (st != MOE_OK) return st;
   Carver c;
   c.take(layer);

@@ -52,9 +52,9 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
 // E2M1 codes of two fp32 values into byte SEL of w (the first value in the low nibble):
 // the nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating at 6 (also for
 // infinities), the sign in bit 3 (-0 and small negatives give 0x8).  gfx950's packed
-// conversion with scale 1 implements exactly this rule: on every non-NaN fp32 input it
-// gives the same code as the piecewise form (rint(2a) on [0,2), 4 + rint(a-2) on [2,4),
-// then 6 up to the tie at 5 and 7 above), checked over all 2^32 bit patterns on the GPU.
+// conversion with scale 1 implements this rule; tests/test_gpu_codec_edges.py pins it
+// against the oracle on every midpoint between two E2M1 magnitudes (both signs) and one
+// and two float steps either side, under block scales from 2^-9 to 2^8.
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
@@ -65,10 +65,12 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
 // code_i = E2M1(fp32(v_i*enc)).  Returns the scale byte; codes packed two per byte,
 // element 2b in the low nibble of byte b (codes_lo: elements 0..7, codes_hi: 8..15).
 // The E4M3 byte rounds to nearest even after the clamp to 448 (subnormals in steps of
-// 2^-9): gfx950's fp32 -> E4M3 conversion does exactly that on [0, 448].  The quotient by
-// 6 is RN(1/6) times amax*q with one FMA correction of the residual; it can differ from the
-// IEEE quotient only where the scale byte is 0 either way.  Both facts were checked on the
-// GPU over every fp32 input (the byte equal to the IEEE quotient's software encode).
+// 2^-9): gfx950's fp32 -> E4M3 conversion does that on [0, 448]; tests/test_gpu_codec_edges.py
+// pins it against the oracle on every midpoint between two E4M3 values (and one float step
+// either side) from the subnormal range to saturation.  The quotient by 6 is RN(1/6) times
+// amax*q with one FMA correction of the residual: over every non-negative finite float it
+// differs from the IEEE quotient only below 2^-100, where the scale byte is 0 either way
+// (tests/c/scale_division.c, run by tests/test_nvfp4_scale_division.py).
 __device__ __forceinline__ uint32_t nvfp4_scale_byte(float amax, float q) {
   constexpr float kSixth = 0.16666667163372040f;      // RN(1/6)
   const float x = amax * q;
@@ -170,6 +172,29 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Group-16 NVFP4 quantization of the 16 BF16 values at src (32-byte aligned) with global
+// encoding scale q: returns the E4M3 scale byte; *codes receives the 8 code bytes (element
+// 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t nvfp4_quantize16(const uint16_t* __restrict__ src, float q,
+                                                     uint2* codes) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+  const uint4 lo = p[0], hi = p[1];
+  const uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(wv[i] << 16);
+    v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  float enc;
+  const uint32_t sb = nvfp4_block_scale(amax, q, &enc);
+  codes->x = pack8_codes(v, enc);
+  codes->y = pack8_codes(v + 8, enc);
+  return sb;
+}
+
 // Group-16 NVFP4 quantization of 16-value block b of BF16 rows (blocks_per_row blocks per
 // row, one encoding scale q[row / rows_per_group] per group of rows): 8 bytes of codes, the
 // E4M3 block scale and, when `decoded` is given, the block's decoded values in f16 (code
@@ -182,23 +207,8 @@ __device__ __forceinline__ void quantize_nvfp4_block(const uint16_t* __restrict_
                                                      uint8_t* __restrict__ scales,
                                                      uint16_t* __restrict__ decoded) {
   const int64_t row = b / blocks_per_row;
-  const float qv = q[row / rows_per_group];
-  const uint4* p = reinterpret_cast<const uint4*>(src + b * kGroup);
-  const uint4 lo = p[0], hi = p[1];
-  const uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  float v[16];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = __uint_as_float(wv[i] << 16);
-    v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
-    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
-  }
-  float enc;
-  const uint32_t sb = nvfp4_block_scale(amax, qv, &enc);
   uint2 out;
-  out.x = pack8_codes(v, enc);
-  out.y = pack8_codes(v + 8, enc);
+  const uint32_t sb = nvfp4_quantize16(src + b * kGroup, q[row / rows_per_group], &out);
   reinterpret_cast<uint2*>(codes)[b] = out;
   scales[b] = static_cast<uint8_t>(sb);
   if (decoded) {

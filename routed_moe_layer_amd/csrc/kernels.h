@@ -129,6 +129,11 @@ hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int 
                                 const float* row_scale,
                                 const float* static_scale, const float* static_offset,
                                 void* expanded_x, float* expanded_scale, hipStream_t stream);
+// NVFP4 token movement: token row t quantized once (group 16, device scalar *qx) and its
+// codes [H/2] and E4M3 scales [H/16] written to rows map[t*K + j] (skipped when negative).
+hipError_t launch_route_permute_nvfp4(const uint16_t* x, int64_t N, int H, int K,
+                                      const int32_t* map, const float* qx, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t stream);
 // Drop/pad: zero the slots of expert e at and past counts[e] (rows of row_bytes bytes,
 // a multiple of 8; scale 0 when expanded_scale is given), for E experts of C slots each.
 hipError_t launch_route_pad_fill(const int32_t* counts, int E, int C, int64_t row_bytes,

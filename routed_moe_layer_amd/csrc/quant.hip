@@ -9,6 +9,8 @@
 //    (section 计算公式, steps 4-5): per-row dynamic int8 quantization (or a BF16 copy),
 //    each token row written to its K expert-sorted positions through the gather map.
 //    One workgroup per token row: the row is read once and written K times.
+//  * route_permute_nvfp4_kernel: the same movement with the layer's group-16 NVFP4
+//    quantization (codes and E4M3 block scales written to each of the K rows).
 #include "common.h"
 #include "kernels.h"
 
@@ -147,6 +149,43 @@ hipError_t launch_route_permute(const uint16_t* x, int64_t N, int H, int K, int 
   route_permute_kernel<<<dim3(static_cast<unsigned>(N)), dim3(kPermThreads), 0, stream>>>(
       x, H, K, quant, map, limit, may_skip, row_scale, static_scale, static_offset, expanded_x,
       expanded_scale);
+  return hipGetLastError();
+}
+
+// Quantized token movement with group-16 NVFP4 ("torch_npu.npu_moe_init_routing_v2",
+// section 计算公式 step 5, with the layer's input quantization of "Cake SiTU backend",
+// intro): token row t is quantized once -- per 16-value block s = E4M3(min(fp32(fp32(amax *
+// qx)/6), 448)), codes E2M1(fp32(v * qx/s)) -- and its codes [H/2] and scales [H/16] are
+// written to its K expert-sorted rows map[t*K + j] (skipped when negative).  One workgroup
+// per token row, one thread per 16-value block: the row's 32-byte reads and every
+// destination's 8-byte code and 1-byte scale writes are contiguous across the threads.
+__global__ __launch_bounds__(kPermThreads) void route_permute_nvfp4_kernel(
+    const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ map,
+    const float* __restrict__ qx, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ int32_t dst[64];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < K) dst[threadIdx.x] = map[t * K + threadIdx.x];
+  __syncthreads();
+  const float q = qx[0];
+  const int nb = H / kGroup;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    uint2 c;
+    const uint32_t sb = nvfp4_quantize16(x + t * H + b * kGroup, q, &c);
+    for (int j = 0; j < K; ++j) {
+      const int64_t r = dst[j];
+      if (r < 0) continue;
+      reinterpret_cast<uint2*>(codes + r * (H / 2))[b] = c;
+      scales[r * nb + b] = static_cast<uint8_t>(sb);
+    }
+  }
+}
+
+hipError_t launch_route_permute_nvfp4(const uint16_t* x, int64_t N, int H, int K,
+                                      const int32_t* map, const float* qx, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  route_permute_nvfp4_kernel<<<dim3(static_cast<unsigned>(N)), dim3(kPermThreads), 0, stream>>>(
+      x, H, K, map, qx, codes, scales);
   return hipGetLastError();
 }
 

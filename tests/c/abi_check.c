@@ -19,8 +19,8 @@ static int failures = 0;
 int main(void) {
   moe_dims_t d = {3584, 384, 896, 16};
   size_t ws16 = 0, ws16k = 0, prep = 0, route = 0;
-  CHECK(moe_workspace_size(d, 16, &ws16) == MOE_OK);
-  CHECK(moe_workspace_size(d, MOE_MAX_TOKENS, &ws16k) == MOE_OK);
+  CHECK(moe_workspace_size(d, 16, MOE_QUANT_NVFP4_G16, &ws16) == MOE_OK);
+  CHECK(moe_workspace_size(d, MOE_MAX_TOKENS, MOE_QUANT_NVFP4_G16, &ws16k) == MOE_OK);
   CHECK(ws16 > 0 && ws16 <= ws16k);
   CHECK(moe_prepared_weights_size(d, &prep) == MOE_OK);
   /* FC1 codes + scales and FC2 codes + scales of 896 experts */
@@ -29,14 +29,22 @@ int main(void) {
   CHECK(moe_workspace_layout(d, 16, &lay) == MOE_OK);
   CHECK(lay.total == ws16 && lay.x_codes < lay.total && lay.o_rows < lay.total);
   CHECK(moe_route_workspace_size(8192, 8, 256, &route) == MOE_OK && route > 0);
+  /* the routing-only workload's dims: moe_route ignores inter */
+  moe_dims_t rd = {7168, 0, 256, 8};
+  size_t rws = 0, rws_fp4 = 0;
+  CHECK(moe_workspace_size(rd, 8192, MOE_QUANT_INT8_ROW_DYNAMIC, &rws) == MOE_OK && rws == route);
+  CHECK(moe_workspace_size(rd, 8192, MOE_QUANT_NVFP4_G16, &rws_fp4) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_route(rd, 8192, (const uint16_t*)0x1000, (const int32_t*)0x2000, MOE_QUANT_NVFP4_G16,
+                  NULL, NULL, NULL, (int32_t*)0x3000, (int32_t*)0x4000, (void*)0x5000,
+                  (void*)0x6000, (void*)0x7000, route, 0) == MOE_ERR_INVALID_ARG); /* no qx */
   moe_ring_layout_t rl;
   CHECK(moe_ring_layout(d, 2, 64, &rl) == MOE_OK && rl.total > rl.counters);
 
   /* validation errors come back as codes, before any device work */
   moe_dims_t bad = {3584, 384, 896, 0};
-  CHECK(moe_workspace_size(bad, 16, &ws16) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_workspace_size(bad, 16, MOE_QUANT_NVFP4_G16, &ws16) == MOE_ERR_INVALID_ARG);
   moe_dims_t odd = {3500, 384, 896, 16};
-  CHECK(moe_workspace_size(odd, 16, &ws16) == MOE_ERR_UNSUPPORTED);
+  CHECK(moe_workspace_size(odd, 16, MOE_QUANT_NVFP4_G16, &ws16) == MOE_ERR_UNSUPPORTED);
   CHECK(moe_forward(d, 16, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                     0, NULL, 0) == MOE_ERR_INVALID_ARG);
   CHECK(moe_topk_softmax(16, 896, 17 * 60, (const float*)0x1000, (int32_t*)0x2000,

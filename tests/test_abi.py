@@ -117,18 +117,42 @@ def test_forward_validation_happens_before_any_hip_call(kw, code):
 
 
 def test_route_validation():
+    d = rm.MoeDims(7168, 0, 256, 8)                   # moe_route ignores inter
     ws = rm.moe_route_workspace_size(8192, 8, 256)
-    base = dict(num_rows=8192, hidden=7168, num_experts=256, top_k=8, x=4096, expert_idx=8192,
-                quant=rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, expanded_x=1 << 20, expanded_scale=1 << 21,
-                expanded_row_idx=1 << 22, expert_cumsum=1 << 23, sorted_expert_idx=None,
-                sorted_row_idx=None, workspace=1 << 24, workspace_bytes=ws, stream=0)
-    for kw, code in ((dict(expanded_scale=None), -1), (dict(quant=5), -1),
-                     (dict(workspace_bytes=ws - 1), -3), (dict(hidden=7), -2),
-                     (dict(num_experts=5000), -2), (dict(num_rows=0), -1)):
+    assert rm.moe_workspace_size(d, 8192, rm.MOE_QUANT_INT8_ROW_DYNAMIC) == ws
+    assert rm.moe_workspace_size(d, 8192, rm.MOE_QUANT_NONE) == ws
+    base = dict(dims=d, T=8192, x=4096, expert_ids=8192, quant=rm.MOE_QUANT_INT8_ROW_DYNAMIC,
+                qx=None, sorted_expert_ids=None, sorted_row_idx=None, expanded_row_idx=1 << 22,
+                expert_cumsum=1 << 23, expanded_x=1 << 20, expanded_sf_or_scale=1 << 21,
+                workspace=1 << 24, workspace_bytes=ws, stream=0)
+    for kw, code in ((dict(expanded_sf_or_scale=None), -1), (dict(quant=5), -1),
+                     (dict(workspace_bytes=ws - 1), -3),
+                     (dict(dims=rm.MoeDims(7, 0, 256, 8)), -2),
+                     (dict(dims=rm.MoeDims(7168, 0, 5000, 8)), -2), (dict(T=0), -1),
+                     # NVFP4 needs the encoding scale, a scale buffer and H % 16 == 0
+                     (dict(quant=rm.MOE_QUANT_NVFP4_G16), -1),
+                     (dict(quant=rm.MOE_QUANT_NVFP4_G16, qx=256, expanded_sf_or_scale=None), -1),
+                     (dict(quant=rm.MOE_QUANT_NVFP4_G16, qx=256,
+                           dims=rm.MoeDims(7160, 0, 256, 8)), -2),
+                     (dict(quant=rm.MOE_QUANT_NVFP4_G16, qx=258), -1)):   # misaligned qx
         a = dict(base); a.update(kw)
         with pytest.raises(rm.MoeError) as ei:
             rm.moe_route(**a)
         assert ei.value.status == code
+
+
+def test_workspace_size_of_the_layer_serves_the_router_in_every_mode():
+    for T in (1, 16, 1024, 16384):
+        n = rm.moe_workspace_size(FULL, T, rm.MOE_QUANT_NVFP4_G16)
+        assert n == rm.moe_workspace_layout(FULL, T)["total"]
+        for q in (rm.MOE_QUANT_NONE, rm.MOE_QUANT_INT8_ROW_DYNAMIC):
+            assert rm.moe_workspace_size(FULL, T, q) <= n
+    # routing-only sizes go past the layer's token limit; the layer's do not
+    assert rm.moe_workspace_size(FULL, 65536, rm.MOE_QUANT_NONE) > 0
+    with pytest.raises(rm.MoeError):
+        rm.moe_workspace_size(FULL, 16385, rm.MOE_QUANT_NVFP4_G16)
+    with pytest.raises(rm.MoeError):
+        rm.moe_workspace_size(FULL, 16, 7)
 
 
 def test_route_v2_validation():

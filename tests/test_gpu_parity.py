@@ -14,7 +14,8 @@ import routed_moe_layer_amd as rm
 from moe_inputs import (TINY, ROUTE_8K, LayerConfig, draw_expert_ids, draw_route_inputs,
                         f32_to_bf16_bits)
 from tests.problem import build_layer_problem, oracle_forward
-from tests.gpu_harness import dev, host, empty_bytes, quantize_on_gpu, prepare, DeviceLayer
+from tests.gpu_harness import (dev, host, empty_bytes, check_guard, quantize_on_gpu, prepare,
+                               DeviceLayer)
 from tests import compare
 
 pytestmark = pytest.mark.gpu
@@ -86,8 +87,8 @@ def _route_on_gpu(ids, E):
     sid = torch.empty(R, dtype=torch.int32, device="cuda")
     sri = torch.empty(R, dtype=torch.int32, device="cuda")
     ws = empty_bytes(rm.moe_route_workspace_size(n, K, E), fill=0xFF)
-    rm.moe_route(n, H, E, K, dev(x), dev(ids.astype(np.int32)), rm.MOE_ROUTE_QUANT_NONE, ex, None,
-                 eri, cs, sid, sri, ws)
+    rm.moe_route(rm.MoeDims(H, 0, E, K), n, dev(x), dev(ids.astype(np.int32)),
+                 rm.MOE_QUANT_NONE, None, sid, sri, eri, cs, ex, None, ws)
     torch.cuda.synchronize()
     return {"expanded_row_idx": host(eri), "cumsum": host(cs), "sorted_ids": host(sid),
             "sorted_row_idx": host(sri)}
@@ -180,8 +181,8 @@ def test_route_int8_full_size_bit_exact():
     sid = torch.empty(R, dtype=torch.int32, device="cuda")
     sri = torch.empty(R, dtype=torch.int32, device="cuda")
     ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
-    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs,
-                 sid, sri, ws)
+    rm.moe_route(rm.MoeDims(H, 0, E, K), N, dev(x), dev(ids), rm.MOE_QUANT_INT8_ROW_DYNAMIC, None,
+                 sid, sri, eri, cs, ex, esc, ws)
     torch.cuda.synchronize()
     want = oracle.route_int8(oracle.bf16_bits_to_f32(x), ids, E)
     assert np.array_equal(host(eri), want["expanded_row_idx"])
@@ -190,6 +191,45 @@ def test_route_int8_full_size_bit_exact():
     assert np.array_equal(host(sri), want["sorted_row_idx"])
     assert np.array_equal(host(esc), want["expanded_scale"])
     assert np.array_equal(host(ex), want["expanded_x"])
+
+
+@pytest.mark.parametrize("case", ["route_N8192_H7168_E256_K8", "layer_T16384_H3584_E896_k16"])
+def test_route_nvfp4_full_size_bit_exact(case):
+    """moe_route with the layer's group-16 NVFP4 quantization: every token quantized once
+    with qX and its codes and E4M3 scales moved to its k expert-sorted rows.  Expected: the
+    oracle's quantize_nvfp4 of each token and its route(), bit for bit."""
+    from moe_inputs import PREFILL_16K, draw_layer_tokens
+    _say(f"route nvfp4 {case}")
+    if case.startswith("route"):
+        x, ids = draw_route_inputs(ROUTE_8K)
+        E = ROUTE_8K.E
+    else:
+        x, ids, _ = draw_layer_tokens(PREFILL_16K)
+        E = PREFILL_16K.E
+    N, H = x.shape
+    K = ids.shape[1]
+    R = N * K
+    _, qX = oracle.calibrate_tokens(x)
+    d = rm.MoeDims(H, 0, E, K)
+    ex = torch.empty((R, H // 2), dtype=torch.uint8, device="cuda")
+    esf = torch.empty((R, H // 16), dtype=torch.uint8, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    cs = torch.empty(E, dtype=torch.int32, device="cuda")
+    sid = torch.empty(R, dtype=torch.int32, device="cuda")
+    sri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = empty_bytes(rm.moe_workspace_size(d, N, rm.MOE_QUANT_NONE), fill=0xFF)
+    rm.moe_route(d, N, dev(x), dev(ids), rm.MOE_QUANT_NVFP4_G16,
+                 dev(np.array([qX], np.float32)), sid, sri, eri, cs, ex, esf, ws)
+    torch.cuda.synchronize()
+    check_guard(ws)
+    r = oracle.route(ids, E)
+    for key, got in (("sorted_ids", sid), ("sorted_row_idx", sri), ("expanded_row_idx", eri),
+                     ("cumsum", cs)):
+        assert np.array_equal(host(got), r[key]), key
+    codes, scales = oracle.quantize_nvfp4(oracle.bf16_bits_to_f32(x), np.float32(qX))
+    tok = r["sorted_row_idx"] // K
+    assert np.array_equal(host(esf), scales[tok])
+    assert np.array_equal(host(ex), oracle.pack_nibbles(codes)[tok])
 
 
 def test_route_bf16_copy_mode():
@@ -202,8 +242,8 @@ def test_route_bf16_copy_mode():
     eri = torch.empty(N * K, dtype=torch.int32, device="cuda")
     cs = torch.empty(E, dtype=torch.int32, device="cuda")
     ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
-    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_NONE, ex, None, eri, cs, None,
-                 None, ws)
+    rm.moe_route(rm.MoeDims(H, 0, E, K), N, dev(x), dev(ids), rm.MOE_QUANT_NONE, None, None,
+                 None, eri, cs, ex, None, ws)
     torch.cuda.synchronize()
     r = oracle.route(ids, E)
     assert np.array_equal(host(eri), r["expanded_row_idx"])

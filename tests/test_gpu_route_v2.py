@@ -208,8 +208,8 @@ def test_route_v2_defaults_equal_moe_route():
     eri = torch.empty(N * K, dtype=torch.int32, device="cuda")
     cs = torch.empty(E, dtype=torch.int32, device="cuda")
     ws = empty_bytes(rm.moe_route_workspace_size(N, K, E))
-    rm.moe_route(N, H, E, K, dev(x), dev(ids), rm.MOE_ROUTE_QUANT_INT8_DYNAMIC, ex, esc, eri, cs,
-                 None, None, ws)
+    rm.moe_route(rm.MoeDims(H, 0, E, K), N, dev(x), dev(ids), rm.MOE_QUANT_INT8_ROW_DYNAMIC, None,
+                 None, None, eri, cs, ex, esc, ws)
     torch.cuda.synchronize()
     assert np.array_equal(got["expanded_x"], host(ex))
     assert np.array_equal(got["expanded_scale"], host(esc))
