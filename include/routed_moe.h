@@ -282,6 +282,26 @@ moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
                                void* const* events);
 
 /* ------------------------------------------------------------------------------------
+ * moe_forward for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation and
+ * arguments without `workspace`, using instead a fixed array of MOE_NOALLOC_SCRATCH_BYTES
+ * in each GPU's global memory that the library holds until the process ends (its device
+ * address is looked up on the first call on a device).  The call itself allocates nothing.
+ * Sizes whose workspace (moe_workspace_size(d, T, MOE_QUANT_NVFP4_G16)) exceeds the array
+ * return MOE_ERR_UNSUPPORTED: at the page's shape that is T > 259.  Every call on one GPU
+ * uses that GPU's one array, so calls on one GPU must not overlap (on different streams
+ * they race); the array keeps the last call's intermediates.
+ * ------------------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+moe_status_t moe_forward_noalloc(moe_dims_t d, int32_t T, const uint16_t* x,
+                                 const int32_t* expert_ids, const uint16_t* route_weights,
+                                 const void* prepared, const float* qx, const float* alpha1,
+                                 const float* qa, const float* alpha2, const float* situ_beta,
+                                 const float* situ_linear_beta, uint16_t* out,
+                                 moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * The step before the layer: top-k expert selection with softmax route weights.  The
  * layer takes expert ids and BF16 route weights as given ("Cake SiTU backend", intro);
  * the pages do not define the gate that makes the router logits, so they are an input:

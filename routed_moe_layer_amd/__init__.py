@@ -18,7 +18,8 @@ __all__ = [
     "MoeRouteOptions", "moe_forward", "moe_forward_timed", "MOE_FORWARD_STAGES",
     "MoeRing", "make_ring", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
     "moe_ring_publish", "moe_forward_streamed", "moe_sealed_workspace_size",
-    "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax", "MOE_RING_ROUTE",
+    "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax", "moe_forward_noalloc",
+    "MOE_NOALLOC_SCRATCH_BYTES", "MOE_RING_ROUTE",
     "MOE_RING_LAYOUT",
     "MOE_RING_OK", "MOE_RING_CONSUMER_TIMEOUT", "MOE_RING_PRODUCER_TIMEOUT",
     "MOE_QUANT_NONE", "MOE_QUANT_INT8_ROW_DYNAMIC", "MOE_QUANT_NVFP4_G16", "MOE_MAX_TOKENS",
@@ -33,6 +34,7 @@ MOE_QUANT_INT8_ROW_DYNAMIC = 1
 MOE_QUANT_NVFP4_G16 = 2
 MOE_MAX_TOKENS = 16384
 MOE_FORWARD_STAGES = 5
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/routed_moe.h declares.
 EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_size",
@@ -40,7 +42,8 @@ EXPORTED = ("moe_status_string", "moe_workspace_size", "moe_prepared_weights_siz
             "moe_prepare_weights", "moe_route", "moe_route_v2", "moe_forward",
             "moe_forward_timed", "moe_ring_layout", "moe_ring_init", "moe_ring_acquire",
             "moe_ring_publish", "moe_forward_streamed", "moe_sealed_workspace_size",
-            "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax")
+            "moe_forward_absorb", "moe_forward_seal", "moe_topk_softmax",
+            "moe_forward_noalloc")
 
 MOE_RING_ROUTE = 0
 MOE_RING_LAYOUT = 1
@@ -133,6 +136,7 @@ def _lib():
             "moe_forward_absorb": (st, [MoeDims, ctypes.POINTER(MoeRing), I32, I32, I32, P,
                                         ctypes.c_uint32, P, SZ, P]),
             "moe_forward_seal": (st, [MoeDims, I32, P, P, P, P, P, P, P, SZ, P, P]),
+            "moe_forward_noalloc": (st, [MoeDims, I32, P, P, P, P, P, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -247,6 +251,14 @@ def moe_forward(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa,
         dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
         _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta),
         _ptr(workspace), nb, _ptr(out), _stream(stream)))
+
+
+def moe_forward_noalloc(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa,
+                        alpha2, situ_beta, situ_linear_beta, out, stream=None):
+    _check("moe_forward_noalloc", _lib().moe_forward_noalloc(
+        dims, T, _ptr(x), _ptr(expert_ids), _ptr(route_weights), _ptr(prepared), _ptr(qx),
+        _ptr(alpha1), _ptr(qa), _ptr(alpha2), _ptr(situ_beta), _ptr(situ_linear_beta), _ptr(out),
+        _stream(stream)))
 
 
 def moe_forward_timed(dims, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,

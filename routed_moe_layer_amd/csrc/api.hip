@@ -3,6 +3,7 @@
 #include "routed_moe.h"
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -685,6 +686,56 @@ moe_status_t moe_forward_seal(moe_dims_t d, int32_t total_tokens, const void* pr
                       reinterpret_cast<const uint16_t*>(ws + SL.weights), prepared, nullptr,
                       alpha1, qa, alpha2, situ_beta, situ_linear_beta, workspace, SL.layer_bytes, out,
                       stream, nullptr, /*quantized=*/true);
+}
+
+}  // extern "C"
+
+// Workspace of moe_forward_noalloc: a fixed array in each GPU's global memory, held for the
+// life of the process.  Host code never uses the array's name as an address (on the host it
+// names a stand-in, not device memory): the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward_noalloc(moe_dims_t d, int32_t T, const uint16_t* x,
+                                 const int32_t* expert_ids, const uint16_t* route_weights,
+                                 const void* prepared, const float* qx, const float* alpha1,
+                                 const float* qa, const float* alpha2, const float* situ_beta,
+                                 const float* situ_linear_beta, uint16_t* out,
+                                 moe_stream_t stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  if (make_layout(d, T).pub.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MOE_OK) return st;
+  // the layer's kernels need no zeroed workspace (every value they read is written
+  // earlier in the same call), so the array's previous contents are harmless
+  return forward_impl(d, T, x, expert_ids, route_weights, prepared, qx, alpha1, qa, alpha2,
+                      situ_beta, situ_linear_beta, ws, MOE_NOALLOC_SCRATCH_BYTES, out, stream,
+                      nullptr);
 }
 
 moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
