@@ -95,8 +95,9 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   x_codes   u8  [T, H/2]    NVFP4 codes of x           x_scales  u8  [T, H/16] E4M3
  *   x_dec     f16 [T, H]      x's NVFP4 values before the global scale (code times block
  *                             scale, exact in f16): the FC1 operand; written only when
- *                             T*k < 65536 (with more routed rows FC1 stages the codes
- *                             and this region is left as it was)
+ *                             T*k < 2 * 128 * (compute units of the device), 65536 on
+ *                             an MI355X (with more routed rows FC1 stages the codes and
+ *                             this region is left as it was)
  *   sorted_ids      i32 [T*k] expert of each sorted row  (keyValueSort keys)
  *   sorted_row_idx  i32 [T*k] flat id t*k+j of each sorted row
  *   expanded_row_idx i32 [T*k] gather map: sorted position of flat id f

@@ -125,6 +125,36 @@ size_t prepared_bytes(const moe_dims_t& d) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Compute units and XCDs of the current device, queried once per device: the persistent
+// grids and the XCD-aware workgroup order follow the device (a partitioned GPU exposes
+// fewer of both than the whole MI355X's 256 CUs in 8 XCDs).
+struct DeviceShape {
+  int cus, xcds;
+};
+std::mutex g_shape_mu;
+DeviceShape g_shape[64] = {};
+
+moe_status_t device_shape(DeviceShape* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_shape_mu);
+  DeviceShape& sh = g_shape[dev];
+  if (sh.cus == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+        xcds <= 0 || xcds > cus)
+      xcds = 1;                   // no XCD count: treat the device as one L2 domain
+    sh.xcds = xcds;
+    sh.cus = cus;
+  }
+  *out = sh;
+  return MOE_OK;
+}
+
 // Dimensions moe_route uses: hidden (a multiple of 8, of 16 for NVFP4), experts, top-k.
 moe_status_t route_dims_ok(const moe_dims_t& d, moe_quant_t q) {
   if (d.hidden <= 0 || d.num_experts <= 0 || d.top_k <= 0) return MOE_ERR_INVALID_ARG;
@@ -393,7 +423,11 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   const int64_t R = static_cast<int64_t>(T) * k;
 
   LayerArgs a{};
+  DeviceShape shape;
+  st = device_shape(&shape);
+  if (st != MOE_OK) return st;
   a.H = H; a.I = I; a.Ip = padded_inter(I); a.E = E; a.k = k; a.T = T;
+  a.cus = shape.cus; a.xcds = shape.xcds;
   a.k_inv = ((uint64_t{1} << 32) + static_cast<uint64_t>(k) - 1) / static_cast<uint64_t>(k);
   a.x_codes = ws + L.pub.x_codes;
   a.x_scales = ws + L.pub.x_scales;
@@ -455,7 +489,7 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
       return MOE_ERR_HIP;
   } else {
     if ((!quantized && launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales,
-                                             layer_writes_x_dec(R) ? x_dec : nullptr,
+                                             layer_writes_x_dec(R, a.cus) ? x_dec : nullptr,
                                              s) != hipSuccess) ||
         !mark(1))
       return MOE_ERR_HIP;
@@ -644,7 +678,10 @@ moe_status_t moe_forward_absorb(moe_dims_t d, const moe_ring_t* ring, int32_t to
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const Layout L = make_layout(d, total_tokens);
   const int H = d.hidden, k = d.top_k;
-  const bool with_dec = layer_writes_x_dec(static_cast<int64_t>(total_tokens) * k);
+  DeviceShape shape;
+  st = device_shape(&shape);
+  if (st != MOE_OK) return st;
+  const bool with_dec = layer_writes_x_dec(static_cast<int64_t>(total_tokens) * k, shape.cus);
   for (int64_t n = first_chunk; n < first_chunk + num_chunks; ++n) {
     const int64_t slot = n % S;
     const int32_t valid = static_cast<int32_t>(std::min<int64_t>(C, total_tokens - n * C));

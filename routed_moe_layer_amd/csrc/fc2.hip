@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   const int n_slabs = a.H / (NW * WRG * 16);
   const int n_groups = (n_slabs + SPW - 1) / SPW;
   int ts, grp;
-  map_workgroup(blockIdx.x, n_groups, &ts, &grp);
+  map_workgroup(blockIdx.x, n_groups, a.xcds, &ts, &grp);
   const int tt = ts / SPLIT, part = ts % SPLIT;
   if (tt >= ntiles) return;
   TileDesc td = tiles[tt];
@@ -237,23 +237,27 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
 // expert's weights are thus read once per run rather than once per 64-row sub-tile.
 // The kernel is persistent (two workgroups per CU, each taking items at a fixed stride), so
 // the grid never holds workgroups with no work; the items of run r go to the workgroups
-// of XCD r % 8, the slabs of one run to consecutive workgroups there, so the run's token
+// of XCD r % xcds, the slabs of one run to consecutive workgroups there, so the run's token
 // rows are fetched from HBM once and reread by the other slabs from that XCD's L2.
 constexpr int kFc2PassRows = 64;
-constexpr int kFc2StationaryGrid = 2 * 256;     // two workgroups on each of 256 CUs
 constexpr int kFc2StationaryRows = 2 * kFc2PassRows;
+// Two workgroups on each compute unit, a whole number per XCD.
+inline int fc2_stationary_grid(const LayerArgs& a) {
+  return static_cast<int>(round_up(2 * static_cast<int64_t>(a.cus), a.xcds));
+}
 
 template <int NW, int WRG, int NCH>
 __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a) {
   constexpr int kSlabGroups = NW * WRG;
   constexpr int kThreads = NW * 64;
-  static_assert(kFc2StationaryGrid % kXcds == 0, "whole XCD strides");
+
   __shared__ __attribute__((aligned(16))) _Float16 s_tok[kFc2PassRows * kFc2LdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_out[NW * 16 * out_lds_stride<WRG>()];
 
   const int n_slabs = a.H / (kSlabGroups * 16);
   const int n_runs = a.num_tiles[2];
-  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const int xcds = a.xcds;                       // gridDim.x is a multiple of it
+  const int xcd = blockIdx.x % xcds, per_xcd = gridDim.x / xcds;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
   const int code_bytes = a.I / 2, scale_cols = a.I / 16;
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
@@ -288,8 +292,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
     }
   };
 
-  for (int k = blockIdx.x / kXcds;; k += per_xcd) {
-    const int run = xcd + kXcds * (k / n_slabs);
+  for (int k = blockIdx.x / xcds;; k += per_xcd) {
+    const int run = xcd + xcds * (k / n_slabs);
     if (run >= n_runs) break;
     const int slab = k - (k / n_slabs) * n_slabs;
     const TileDesc rd = a.runs[run];
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
 template <int NW, int WRG, int NCH>
 static void launch_fc2_stationary(const LayerArgs& a, hipStream_t stream) {
   fc2_stationary_kernel<NW, WRG, NCH>
-      <<<dim3(kFc2StationaryGrid), dim3(NW * 64), 0, stream>>>(a);
+      <<<dim3(static_cast<unsigned>(fc2_stationary_grid(a))), dim3(NW * 64), 0, stream>>>(a);
 }
 
 template <int NW, int WRG, int BN, int SPW, int SPLIT = 1>
@@ -395,7 +399,7 @@ static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
   const int n_slabs = a.H / (NW * WRG * 16);
   const int n_groups = (n_slabs + SPW - 1) / SPW;
   const int64_t grid =
-      round_up(round_up(max_tiles * SPLIT, kTileGroup) * n_groups, kXcds * kXcdRun);
+      round_up(round_up(max_tiles * SPLIT, kTileGroup) * n_groups, a.xcds * kXcdRun);
   if (grid > 0)
     fc2_kernel<NW, WRG, BN, SPW, SPLIT>
         <<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a, big);

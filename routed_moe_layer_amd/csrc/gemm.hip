@@ -441,7 +441,7 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const int n_wt = rows_total / C::kWgRows;
   int tt, wt;
-  map_workgroup(blockIdx.x, n_wt, &tt, &wt);
+  map_workgroup(blockIdx.x, n_wt, a.xcds, &tt, &wt);
   if (tt >= ntiles) return;
   TileCtx t;
   t.td = tiles[tt];
@@ -560,8 +560,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 // Variants: small tiles (up to 32 tokens) run 4 waves x 4 groups (256-row slabs) in FC1
 // and 4 waves x 2 groups (128-row slabs) in FC2 or when the rows do not divide, and stage
 // FC1's tokens as f16 rows.  Big tiles (up to kBigRows tokens) run 4 waves x 2
-// groups, FC1 with f16 rows; with at least kManyRows routed rows (about two big tiles
-// per CU) FC1's big tiles run 4 waves x 4 groups instead (half the LDS operand reads per
+// groups, FC1 with f16 rows; with at least two big tiles per CU of routed rows
+// (many_rows) FC1's big tiles run 4 waves x 4 groups instead (half the LDS operand reads per
 // MFMA; the tokens are staged as codes, a quarter of the f16 rows' bytes: each token row is
 // fetched once per slab, so f16 rows would double the kernel's memory traffic).
 // A slab that does not divide the rows falls back to 128-row slabs.
@@ -576,7 +576,7 @@ static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipSt
   using C = GemmCfg<MODE, NW, WRG, BN>;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const int64_t grid = round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows),
-                                kXcds * kXcdRun);
+                                a.xcds * kXcdRun);
   if (grid > 0)
     grouped_gemm_kernel<MODE, NW, WRG, BN, WPE, ROWS>
         <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
@@ -586,7 +586,7 @@ template <int MODE>
 static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   constexpr bool kRows = MODE == 0;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
-  const bool many = static_cast<int64_t>(a.T) * a.k >= kManyRows;
+  const bool many = many_rows(static_cast<int64_t>(a.T) * a.k, a.cus);
   const bool small_wide =
       MODE == 0 && rows_total % GemmCfg<MODE, 4, kFc1SmallWRG, kSmallRows>::kWgRows == 0;
   if (kRows && many) {
@@ -606,7 +606,7 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  // (from kManyRows on there is no f16 copy of x: FC1's fallback slabs stage codes too)
+  // (with many rows there is no f16 copy of x: FC1's fallback slabs stage codes too)
   const bool big_slabs = rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
   if (kRows && many) {
     if (big_slabs) launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
@@ -626,7 +626,7 @@ hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
   if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows) return hipGetLastError();
   // The resident kernel gives each big tile one workgroup; below about two big tiles per
   // CU that leaves the chip idle, and the grouped kernel (tiles x row slabs) is faster.
-  if (static_cast<int64_t>(a.T) * a.k >= kManyRows) launch_fc2_resident_big(a, stream);
+  if (many_rows(static_cast<int64_t>(a.T) * a.k, a.cus)) launch_fc2_resident_big(a, stream);
   else if (a.H % GemmCfg<1, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
     launch_variant<1, kBigNW, kBigWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
   else

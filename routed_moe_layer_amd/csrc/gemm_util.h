@@ -7,17 +7,18 @@
 
 namespace rmoe {
 
-// Workgroup -> (token tile, weight slab).  Workgroups are dealt to the 8 XCDs round-robin
-// by id; kXcdRun consecutive logical ids are kept on one XCD (and in flight together),
-// and logical ids run over kTileGroup consecutive token tiles of one slab before moving to
-// the next slab.  The token tiles of an expert are adjacent in the work list, so the
-// workgroups that read the same weight slab share that XCD's L2, and a group of token
-// tiles is reread across slabs while it is still cached.
-constexpr int kXcds = 8, kXcdRun = 4, kTileGroup = 4;
+// Workgroup -> (token tile, weight slab).  Workgroups are dealt to the device's XCDs
+// round-robin by id (xcds of them; 8 on an MI355X in its single-partition mode); kXcdRun
+// consecutive logical ids are kept on one XCD (and in flight together), and logical ids
+// run over kTileGroup consecutive token tiles of one slab before moving to the next slab.
+// The token tiles of an expert are adjacent in the work list, so the workgroups that read
+// the same weight slab share that XCD's L2, and a group of token tiles is reread across
+// slabs while it is still cached.  Grids are whole multiples of xcds * kXcdRun.
+constexpr int kXcdRun = 4, kTileGroup = 4;
 
-__device__ __forceinline__ void map_workgroup(int b, int n_wt, int* tt, int* wt) {
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int L = ((slot / kXcdRun) * kXcds + xcd) * kXcdRun + slot % kXcdRun;
+__device__ __forceinline__ void map_workgroup(int b, int n_wt, int xcds, int* tt, int* wt) {
+  const int xcd = b % xcds, slot = b / xcds;
+  const int L = ((slot / kXcdRun) * xcds + xcd) * kXcdRun + slot % kXcdRun;
   const int per_group = n_wt * kTileGroup;
   *tt = (L / per_group) * kTileGroup + L % kTileGroup;
   *wt = (L / kTileGroup) % n_wt;

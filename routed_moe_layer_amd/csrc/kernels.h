@@ -32,10 +32,11 @@ constexpr int kBigTileRows = 112;
 // FC2 for many routed rows works on runs of up to kRunTiles consecutive big tiles of one
 // expert (a contiguous range of its sorted rows).
 constexpr int kRunTiles = 4;
-// From kManyRows routed rows on (about two big tiles per CU), FC1 stages every token tile
-// as NVFP4 codes and the layer does not write the f16 copy of x (x_dec).
-constexpr int64_t kManyRows = 2 * 256 * kBigRows;
-inline bool layer_writes_x_dec(int64_t R) { return R < kManyRows; }
+// From two big tiles per compute unit on (2 * cus * kBigRows routed rows, 65536 on the
+// 256-CU MI355X), FC1 stages every token tile as NVFP4 codes and the layer does not write
+// the f16 copy of x (x_dec).
+inline bool many_rows(int64_t R, int cus) { return R >= int64_t{2} * cus * kBigRows; }
+inline bool layer_writes_x_dec(int64_t R, int cus) { return !many_rows(R, cus); }
 
 inline int route_tiles(int64_t n) { return static_cast<int>((n + kRouteTile - 1) / kRouteTile); }
 inline int bits_for(int E) { int b = 1; while ((1 << b) < E) ++b; return b; }
@@ -169,6 +170,7 @@ hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
 
 struct LayerArgs {
   int H, I, Ip, E, k, T;
+  int cus, xcds;               // compute units and XCDs (L2 domains) of the device
   uint64_t k_inv;              // ceil(2^32 / k): t = (f * k_inv) >> 32 for flat ids f < 2^26
   const uint8_t* x_codes;      // [T, H/2]
   const uint8_t* x_scales;     // [T, H/16]

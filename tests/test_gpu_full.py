@@ -144,7 +144,7 @@ def test_full_layer_parity(full_weights, cfg, per_expert_qa):
     # input codes of the tokens involved
     assert np.array_equal(inter["x_codes"][ref["tokens"]], oracle.pack_nibbles(ref["x_codes"]))
     assert np.array_equal(inter["x_scales"][ref["tokens"]], ref["x_scales"])
-    if T * k < compare.X_DEC_MAX_ROWS:
+    if T * k < compare.x_dec_max_rows():
         assert np.array_equal(inter["x_dec"][ref["tokens"]].astype(np.float64),
                               oracle.dequantize_nvfp4(ref["x_codes"], ref["x_scales"]))
     # intermediate codes, row by row
