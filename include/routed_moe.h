@@ -178,7 +178,8 @@ moe_status_t moe_prepare_weights(moe_dims_t d, const uint8_t* w13, const uint8_t
  * qx f32 [1] (NVFP4 only, else may be NULL); expanded_sf_or_scale NULL for MOE_QUANT_NONE;
  * expanded_row_idx, sorted_expert_ids, sorted_row_idx i32 [T*k] (the last two may be
  * NULL); expert_cumsum i32 [E].  d.inter is not used.  Limits: 1 <= T, T*k <= 2^24,
- * H % 8 == 0 (H % 16 == 0 for NVFP4), H <= 65536, 1 <= E <= 4096, 1 <= k <= 64.
+ * H % 8 == 0 (H % 16 == 0 for NVFP4), H <= 65536, 1 <= E <= 10240 (the page's expert_num
+ * limit), 1 <= k <= 64.
  * workspace: moe_workspace_size(d, T, q) bytes, 256-byte aligned.
  * ------------------------------------------------------------------------------------ */
 moe_status_t moe_route(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t* expert_ids,
@@ -217,8 +218,9 @@ moe_status_t moe_route(moe_dims_t d, int32_t T, const uint16_t* x, const int32_t
  * the valid ones are left untouched except drop/pad's zero slots); expanded_row_idx i32
  * [N*K]; expert_tokens i32 as above or NULL; expanded_scale f32 [rows of expanded_x] or
  * NULL; available_idx_num i32 [1] or NULL.  workspace: moe_route_workspace_size() bytes.
- * Limits as moe_route (num_experts <= 4096 where the page allows 10240).  The
- * smoothing-scale variant of the dynamic mode is not offered.
+ * Limits as moe_route: num_experts <= 10240, and <= 5120 with the key_value histogram
+ * (the page's expert_num limits).  The smoothing-scale variant of the dynamic mode is
+ * not offered.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t expert_start;
@@ -345,8 +347,11 @@ moe_status_t moe_topk_softmax(int32_t T, int32_t num_experts, int32_t top_k,
  *
  * Progress: every wait is a one-workgroup kernel bounded by timeout_us (0 = 1 s).  When
  * a wait expires it records MOE_RING_CONSUMER_TIMEOUT or MOE_RING_PRODUCER_TIMEOUT in the
- * ring's status word (the first failure is kept) and returns; the work after it then runs
- * on whatever the slot holds, and the ring must be re-initialized.  The rule for progress:
+ * ring's status word (the first failure is kept) and returns.  While the status word holds
+ * a failure, the consumer takes no expert id from a slot: every chunk it consumes or
+ * absorbs has all its ids dropped, so its output rows are zero (a defined value, never
+ * computed from stale slot data), and the slot is still published as consumed.  The ring
+ * must then be re-initialized.  The rule for progress:
  * enqueue every publish before the waits that need it (in host enqueue order, across
  * streams), for example all chunks produced into a ring of at least as many slots and
  * then consumed, or produce and consume alternating per chunk.  Then any placement of the

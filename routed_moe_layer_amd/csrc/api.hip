@@ -13,6 +13,10 @@ namespace {
 using namespace rmoe;
 
 constexpr size_t kAlign = 256;
+// The routing primitive's expert-count limits ("torch_npu.npu_moe_init_routing_v2",
+// parameter expert_num: at most 10240, at most 5120 with the key_value histogram); the
+// whole layer takes at most 4096 experts.
+constexpr int kRouteMaxExperts = 10240, kRouteMaxExpertsKeyValue = 5120;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -160,7 +164,7 @@ moe_status_t route_dims_ok(const moe_dims_t& d, moe_quant_t q) {
   if (d.hidden <= 0 || d.num_experts <= 0 || d.top_k <= 0) return MOE_ERR_INVALID_ARG;
   if (d.hidden % (q == MOE_QUANT_NVFP4_G16 ? 16 : 8) || d.hidden > 65536)
     return MOE_ERR_UNSUPPORTED;
-  if (d.num_experts > 4096 || d.top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (d.num_experts > kRouteMaxExperts || d.top_k > 64) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -221,7 +225,7 @@ moe_status_t moe_workspace_layout(moe_dims_t d, int32_t T, moe_workspace_layout_
 moe_status_t moe_route_workspace_size(int32_t num_rows, int32_t top_k, int32_t num_experts,
                                       size_t* bytes) {
   if (!bytes || num_rows < 1 || top_k < 1 || num_experts < 1) return MOE_ERR_INVALID_ARG;
-  if (top_k > 64 || num_experts > 4096) return MOE_ERR_UNSUPPORTED;
+  if (top_k > 64 || num_experts > kRouteMaxExperts) return MOE_ERR_UNSUPPORTED;
   const int64_t n = static_cast<int64_t>(num_rows) * top_k;
   if (n > (int64_t{1} << 24)) return MOE_ERR_UNSUPPORTED;
   Carver c;
@@ -329,6 +333,8 @@ moe_status_t moe_route_v2(int32_t num_rows, int32_t hidden, int32_t num_experts,
   if (start < 0 || end <= start || end > num_experts) return MOE_ERR_INVALID_ARG;
   if (o.row_idx_type != 0 && o.row_idx_type != 1) return MOE_ERR_INVALID_ARG;
   if (o.expert_tokens_num_type < 0 || o.expert_tokens_num_type > 2) return MOE_ERR_INVALID_ARG;
+  if (o.expert_tokens_num_type == 2 && num_experts > kRouteMaxExpertsKeyValue)
+    return MOE_ERR_UNSUPPORTED;
   if (o.quant_mode < -1 || o.quant_mode > 1) return MOE_ERR_INVALID_ARG;
   if (o.drop_pad_mode != 0 && o.drop_pad_mode != 1) return MOE_ERR_INVALID_ARG;
   const int64_t n = static_cast<int64_t>(num_rows) * top_k;
@@ -610,7 +616,15 @@ moe_status_t moe_forward_streamed(moe_dims_t d, const moe_ring_t* ring, int32_t 
     const uint16_t* x = reinterpret_cast<const uint16_t*>(base + L.x) + slot * C * H;
     const int32_t* ids = reinterpret_cast<const int32_t*>(base + L.expert_ids) + slot * C * k;
     const uint16_t* w = reinterpret_cast<const uint16_t*>(base + L.route_weights) + slot * C * k;
-    st = forward_impl(d, valid, x, ids, w, prepared, qx, alpha1, qa, alpha2, situ_beta,
+    // The chunk's ids go through the workspace's FC2-row area (the router reads them there
+    // before FC2 writes that area): after a failed wait they are all dropped, so the chunk
+    // computes nothing from the slot and its output rows are zero.
+    int32_t* ids_ws = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                                 make_layout(d, valid).pub.o_rows);
+    if (launch_slot_ids(ids_ws, ids, static_cast<int64_t>(valid) * k, ring_status(ring, L),
+                        s) != hipSuccess)
+      return MOE_ERR_HIP;
+    st = forward_impl(d, valid, x, ids_ws, w, prepared, qx, alpha1, qa, alpha2, situ_beta,
                       situ_linear_beta, workspace, workspace_bytes, out + n * C * H, stream,
                       nullptr);
     if (st != MOE_OK) return st;
@@ -699,8 +713,9 @@ moe_status_t moe_forward_absorb(moe_dims_t d, const moe_ring_t* ring, int32_t to
     if (launch_quantize_nvfp4(x, 1, valid, H, qx, ws + L.pub.x_codes + t0 * (H / 2),
                               ws + L.pub.x_scales + t0 * (H / kGroup), dec, s) != hipSuccess)
       return MOE_ERR_HIP;
-    if (launch_slot_copy(ws + SL.ids + t0 * k * 4, ids, static_cast<int64_t>(valid) * k * 4,
-                         s) != hipSuccess ||
+    // (after a failed wait the ids are all dropped: the chunk's output rows are zero)
+    if (launch_slot_ids(reinterpret_cast<int32_t*>(ws + SL.ids) + t0 * k, ids,
+                        static_cast<int64_t>(valid) * k, ring_status(ring, RL), s) != hipSuccess ||
         launch_slot_copy(ws + SL.weights + t0 * k * 2, w, static_cast<int64_t>(valid) * k * 2,
                          s) != hipSuccess)
       return MOE_ERR_HIP;

@@ -158,6 +158,9 @@ hipError_t launch_ring_wait(const uint32_t* a, const uint32_t* b, const uint32_t
 hipError_t launch_ring_publish(uint32_t* gen, uint32_t* seq, hipStream_t stream);
 // Device copy of `bytes` (even) bytes on `stream`, 2-byte aligned pointers.
 hipError_t launch_slot_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+// Copy of n expert ids, or n times -1 when *status (the ring's status word) is nonzero.
+hipError_t launch_slot_ids(int32_t* dst, const int32_t* src, int64_t n, const uint32_t* status,
+                           hipStream_t stream);
 
 // Top-k expert selection with softmax weights over the picks (topk.hip): logits f32
 // [T, E] (E <= 4096), k <= 64 -> ids i32 [T, k], BF16 weights [T, k].

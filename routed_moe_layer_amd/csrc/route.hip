@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 
 // The three per-expert quantities the expert scans need, packed into one 64-bit value so
 // that one block scan serves all three: rows (26 bits; at most 2^24 ids per call), small
-// tiles or nonzero experts (19 bits; at most 4096), big tiles (19 bits; at most
-// 2^20 / kBigRows + 4096 for the layer's 2^20 routed rows).
+// tiles or nonzero experts (19 bits; at most 10240 experts), big tiles (19 bits; at most
+// 2^20 / kBigRows + 4096 for the layer's 2^20 routed rows over at most 4096 experts).
 constexpr int kRowBits = 26, kTileBits = 19;
 __device__ __forceinline__ uint64_t pack_counts(int cnt, int n_small, int n_big) {
   return static_cast<uint64_t>(cnt) | (static_cast<uint64_t>(n_small) << kRowBits) |
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteBuffers b, int nt
   if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; carry[2] = 0; carry[3] = 0; }
   __syncthreads();
   int32_t* __restrict__ tile_hist = b.tile_hist;
-  // Experts are handled in rounds of 1024 (E <= 4096).
+  // Experts are handled in rounds of 1024.
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x;
     int cnt = 0;
@@ -335,6 +335,38 @@ __device__ __forceinline__ void fill_tail(const RouteBuffers& b, int64_t f, int6
   if (f < n && f >= total) {
     if (b.sorted_ids) b.sorted_ids[f] = -1;
     if (b.sorted_row_idx) b.sorted_row_idx[f] = -1;
+  }
+}
+
+// Many experts (per-wave histograms of more than kScatterWaveHistMaxE experts would not fit
+// in LDS): the tile's waves rank their ids in turn against one running histogram of the
+// tile ([E] in LDS), so each rank already counts the earlier waves' ids of its expert.
+constexpr int kScatterWaveHistMaxE = 4096;
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_seq_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
+  extern __shared__ int32_t hist[];                // [E]
+  const int nw = kRouteThreads / kWave;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t wave_base = static_cast<int64_t>(blockIdx.x) * kRouteTile + w * (kRouteTile / nw);
+  int key[kIdsPerThread];
+  int rank[kIdsPerThread];
+  for (int turn = 0; turn < nw; ++turn) {
+    if (w == turn)
+      rank_wave_ids(ids, n, E, nbits, b.e_base, wave_base, lane, hist, b.expanded_row_idx, key,
+                    rank);
+    __syncthreads();
+  }
+  const int32_t* th = b.tile_hist + static_cast<int64_t>(blockIdx.x) * E;
+  const int total = b.offsets[E];
+  for (int r = 0; r < kIdsPerThread; ++r) {
+    const int64_t f = wave_base + r * kWave + lane;
+    fill_tail(b, f, n, total);
+    const int e = key[r];
+    if (e < 0) continue;
+    place_id(b, e, f, b.offsets[e], th[e] + rank[r]);
   }
 }
 
@@ -581,9 +613,13 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
     route_colscan_kernel<<<dim3((E + kScanExperts - 1) / kScanExperts),
                            dim3(kScanExperts * kScanWaves), 0, stream>>>(b, nt, E);
   route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(b, nt, E, counted);
-  route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
-                         (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
-      ids, n, E, bits_for(E), b);
+  if (E <= kScatterWaveHistMaxE)
+    route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
+                           (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
+        ids, n, E, bits_for(E), b);
+  else
+    route_scatter_seq_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
+        ids, n, E, bits_for(E), b);
   return hipGetLastError();
 }
 

@@ -75,6 +75,28 @@ __global__ __launch_bounds__(256) void slot_copy_kernel(uint16_t* __restrict__ d
     dst[i] = src[i];
 }
 
+// Copy of a slot's expert ids into the consumer's own buffer -- or, when the ring's status
+// word records a failure (an expired wait: the slot may hold stale or half-written data),
+// -1 for every id, so that the layer drops the chunk's rows and its output rows are zero.
+__global__ __launch_bounds__(256) void slot_ids_kernel(int32_t* __restrict__ dst,
+                                                       const int32_t* __restrict__ src,
+                                                       int64_t n, const uint32_t* status) {
+  const bool failed = load_acquire(status) != 0u;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride)
+    dst[i] = failed ? -1 : src[i];
+}
+
+hipError_t launch_slot_ids(int32_t* dst, const int32_t* src, int64_t n, const uint32_t* status,
+                           hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((n + 255) / 256, 1024);
+  slot_ids_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream>>>(dst, src, n,
+                                                                               status);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
   const int64_t n = bytes / 2;
   if (n <= 0) return hipSuccess;

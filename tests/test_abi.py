@@ -128,7 +128,7 @@ def test_route_validation():
     for kw, code in ((dict(expanded_sf_or_scale=None), -1), (dict(quant=5), -1),
                      (dict(workspace_bytes=ws - 1), -3),
                      (dict(dims=rm.MoeDims(7, 0, 256, 8)), -2),
-                     (dict(dims=rm.MoeDims(7168, 0, 5000, 8)), -2), (dict(T=0), -1),
+                     (dict(dims=rm.MoeDims(7168, 0, 10241, 8)), -2), (dict(T=0), -1),
                      # NVFP4 needs the encoding scale, a scale buffer and H % 16 == 0
                      (dict(quant=rm.MOE_QUANT_NVFP4_G16), -1),
                      (dict(quant=rm.MOE_QUANT_NVFP4_G16, qx=256, expanded_sf_or_scale=None), -1),
@@ -183,6 +183,9 @@ def test_route_v2_validation():
         (dict(options=O(), hidden=12), -2),
         (dict(options=O(), x=4098), -1),
         (dict(options=O(), expanded_row_idx=None), -1),
+        # the page's expert_num limits: 10240, and 5120 with the key_value histogram
+        (dict(options=O(), num_experts=10241), -2),
+        (dict(options=O(expert_tokens_num_type=2), num_experts=5121), -2),
     ]
     for kw, code in cases:
         a = dict(base); a.update(kw)
@@ -244,3 +247,14 @@ def test_plain_c_program_uses_the_abi(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "ok"
+
+
+def test_routing_takes_the_pages_expert_counts():
+    for E in (4097, 5120, 10240):
+        assert rm.moe_route_workspace_size(64, 8, E) > 0
+    d = rm.MoeDims(256, 0, 10240, 8)
+    assert rm.moe_workspace_size(d, 64, rm.MOE_QUANT_NONE) == rm.moe_route_workspace_size(64, 8, 10240)
+    with pytest.raises(rm.MoeError):
+        rm.moe_route_workspace_size(64, 8, 10241)
+    with pytest.raises(rm.MoeError):                   # the layer stays at 4096 experts
+        rm.moe_workspace_size(rm.MoeDims(256, 64, 4097, 8), 16)

@@ -168,6 +168,17 @@ V2_CASES = [
      dict(drop_pad_mode=1, expert_capacity=2, quant_mode=0), False),
     ("few_tokens_range_scatter_row_scale", 5, 4, 16, 72, 0.0,
      dict(quant_mode=-1, expert_start=3, expert_end=11, row_idx_type=1, active_num=9), True),
+    # the page's expert_num limits: 10240 experts (the scatter ranks its waves in turn
+    # against one running histogram above 4096), 5120 with the key_value histogram
+    ("experts_10240_dynamic", 3000, 8, 10240, 64, 0.7, dict(quant_mode=1), False),
+    ("experts_10240_range_scatter_count", 2000, 8, 10240, 64, 0.3,
+     dict(expert_start=100, expert_end=9000, row_idx_type=1, expert_tokens_num_type=1,
+          quant_mode=-1), False),
+    ("experts_10240_droppad", 1500, 8, 10240, 64, 1.2,
+     dict(drop_pad_mode=1, expert_capacity=3, quant_mode=0), False),
+    ("experts_5120_kv", 3000, 8, 5120, 64, 0.5,
+     dict(expert_tokens_num_type=2, quant_mode=1), False),
+    ("experts_10240_one_tile", 40, 8, 10240, 64, 0.0, dict(quant_mode=1), False),
 ]
 
 

@@ -327,6 +327,23 @@ def test_wait_timeouts_set_status_and_return(layer):
     R.produce(0, CFG.T, parts=("route",))          # the layout part is never published
     R.consume(CFG.T, 0, 1, timeout_us=2000)
     assert R.status() == rm.MOE_RING_CONSUMER_TIMEOUT
+    # the expired chunk computed nothing from the slot: its output rows are zero, the rows
+    # of the chunks never consumed keep their fill value
+    out = host(R.out, np.uint16)
+    assert np.all(out[:16] == 0) and np.all(out[16:] == 0xFFFF)
+    # so is a chunk consumed later while the failure stands, even with its data published
+    R.out.fill_(-1)
+    R.produce(0, CFG.T, parts=("layout",))
+    R.consume(CFG.T, 0, 1, timeout_us=2000)
+    assert np.all(host(R.out, np.uint16)[:16] == 0)
+    # the sealed front end likewise drops an expired chunk's ids
+    rm.moe_ring_init(L.dims, R.ring)
+    R.produce(0, CFG.T, parts=("route",))
+    R.absorb(CFG.T, 0, 1, timeout_us=2000)
+    assert R.status() == rm.MOE_RING_CONSUMER_TIMEOUT
+    torch.cuda.synchronize()
+    ids_tail = R.sws[rm.moe_workspace_size(L.dims, CFG.T):].view(torch.int32)[:16 * CFG.k]
+    assert bool((ids_tail == -1).all())
     rm.moe_ring_init(L.dims, R.ring)
     assert R.status() == rm.MOE_RING_OK
     R.produce(0, CFG.T, parts=("route",))
