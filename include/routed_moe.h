@@ -105,11 +105,12 @@ moe_status_t moe_prepared_weights_size(moe_dims_t d, size_t* bytes /*host*/);
  *   a_codes   u8  [T*k, I/2]  requantized SiTU output, sorted row order
  *   a_scales  u8  [T*k, I/16]
  *   o_rows    f16  [T*k, H]   FC2 output O of routed row (t, j) at row t*k + j, alpha2
- *                             applied, stored as O * 2^s with s the exponent of its
- *                             32-column segment (rows of dropped ids are not written)
- *   o_exp     i8   [T, H/32, k] s of segment c of routed row (t, j) at [t, c, j]: the
- *                             segment's largest |O| * 2^s lies in [2^14, 2^15] (s = 0 for
- *                             an all-zero segment)
+ *                             applied, stored as O * 2^s (rows of dropped ids are not
+ *                             written)
+ *   o_exp     i8   [T*k]      s of routed row t*k + j: one exponent per expert e, from a
+ *                             bound (|FC2 sum| <= I * 2688^2): with E the fp32 biased
+ *                             exponent of |alpha2[e]| * I * 2688^2, s = clamp(141 - E,
+ *                             -126, 126), so every |O| * 2^s is below 2^15
  *   a_amax    f32 [E]         max |SiTU output| of each expert's rows in this call
  *                             (0 for an expert with no rows; a calibration statistic) */
 typedef struct {
@@ -291,7 +292,7 @@ moe_status_t moe_forward_timed(moe_dims_t d, int32_t T, const uint16_t* x,
  * in each GPU's global memory that the library holds until the process ends (its device
  * address is looked up on the first call on a device).  The call itself allocates nothing.
  * Sizes whose workspace (moe_workspace_size(d, T, MOE_QUANT_NVFP4_G16)) exceeds the array
- * return MOE_ERR_UNSUPPORTED: at the page's shape that is T > 259.  Every call on one GPU
+ * return MOE_ERR_UNSUPPORTED: at the page's shape that is T > 262.  Every call on one GPU
  * uses that GPU's one array, so calls on one GPU must not overlap (on different streams
  * they race); the array keeps the last call's intermediates.
  * ------------------------------------------------------------------------------------ */

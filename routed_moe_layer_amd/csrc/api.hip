@@ -114,7 +114,7 @@ Layout make_layout(const moe_dims_t& d, int64_t T) {
   L.pub.a_codes = c.take(R * I / 2);
   L.pub.a_scales = c.take(R * I / 16);
   L.pub.o_rows = c.take(R * H * 2);
-  L.pub.o_exp = c.take(R * (H / 32));
+  L.pub.o_exp = c.take(R);
   L.pub.a_amax = c.take(E * 4);
   L.pub.total = c.off;
   return L;
@@ -434,7 +434,6 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   if (st != MOE_OK) return st;
   a.H = H; a.I = I; a.Ip = padded_inter(I); a.E = E; a.k = k; a.T = T;
   a.cus = shape.cus; a.xcds = shape.xcds;
-  a.k_inv = ((uint64_t{1} << 32) + static_cast<uint64_t>(k) - 1) / static_cast<uint64_t>(k);
   a.x_codes = ws + L.pub.x_codes;
   a.x_scales = ws + L.pub.x_scales;
   a.x_dec = reinterpret_cast<const uint16_t*>(ws + L.pub.x_dec);

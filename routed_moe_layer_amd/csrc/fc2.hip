@@ -3,8 +3,8 @@
 // "Cake SiTU backend" (intro; section "Prepared weights and scales"):
 //   o[r, h] = alpha2[e] * sum_i ahat[r, i] * w2hat[e, h, i],  i < I
 // with ahat the requantized SiTU output (NVFP4, decoded exactly to f16) and w2hat the FC2
-// weights; the result is stored as f16 rows with per-32-column exponents (store_out_block)
-// for the finalization.
+// weights; the result is stored as f16 rows scaled by a power of two per expert
+// (store_out_block) for the finalization.
 //
 // FC2's reduction is short (I = 384 at the page's shape), so a workgroup decodes its token
 // tile's full K range into LDS once, with a single barrier, and then sweeps a group of
@@ -52,9 +52,9 @@ __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int l
 // epilogue compile-time; a slab's first K-step starts from a zero accumulator.
 // The output of one wave for one 16-token block and one slab passes through a per-wave LDS
 // buffer (store_out_block): each lane then holds consecutive columns of one token row, so
-// the 32-column segments' exponents need no more than two lane exchanges and the global
-// stores are whole 16-byte pieces of consecutive columns (the rows are scattered over the
-// FC2 output, so longer runs per store instruction cut the memory transactions).
+// the global stores are whole 16-byte pieces of consecutive columns (the rows are
+// scattered over the FC2 output, so longer runs per store instruction cut the memory
+// transactions).
 template <int NW, int WRG, int BN, int NCBA, int NCH>
 __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td, int slab0,
                                          int nslabs, const _Float16* __restrict__ s_tok,
@@ -63,7 +63,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int e = td.expert;
   const int last = slab0 + nslabs - 1;
-  const OutScale osc = out_scale_of(a.alpha2[e]);
+  const OutScale osc = out_scale(a.alpha2[e], a.I);
   const _Float16* xrow = s_tok + (lane & 15) * kFc2LdsRow + 8 * g;
   // FC2 rows are stored at their flat id t*k + j, so that the finalization reads each
   // token's k rows as one contiguous run; lane l holds the flat id of block row l % 16
@@ -131,7 +131,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
 #pragma unroll
         for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
         store_out_block<WRG>(blk, osc, wave_out, lane, flat_cb[cb], td.nrows - cb * 16, a.o_rows,
-                             a.o_exp, a.H, a.k, a.k_inv, 16 * G0);
+                             a.o_exp, a.H, 16 * G0);
       }
       // the next slab's MFMAs (fresh accumulators) stay after these stores, so the two
       // accumulator sets are never live together
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
 #pragma unroll
       for (int r = 0; r < WRG; ++r) scales4_f16(wr[c].s[r], &wsc[c][r][0], &wsc[c][r][1]);
 
-    const OutScale osc = out_scale_of(a.alpha2[e]);
+    const OutScale osc = out_scale(a.alpha2[e], a.I);
     const int col0 = 16 * (slab * kSlabGroups + w * WRG);
     int32_t flat[kFc2PassRows / 16];
     int p0 = rd.row_start;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
 #pragma unroll
         for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
         store_out_block<WRG>(blk, osc, wave_out, lane, flat[cb], nr - cb * 16, a.o_rows, a.o_exp,
-                             a.H, a.k, a.k_inv, col0);
+                             a.H, col0);
       }
     };
 

@@ -26,7 +26,7 @@
 // The FC1 epilogue fuses alpha1, SiTU, the group-16 requantization (two consecutive MFMA
 // row groups hold the gate/up pairs of 16 intermediate channels = one NVFP4 group) and the
 // per-expert amax statistic; the FC2 epilogue applies alpha2 and stores the rows as f16
-// with per-32-column exponents (store_out_block).
+// scaled by a power of two per expert (store_out_block).
 #include <type_traits>
 
 #include "common.h"
@@ -409,7 +409,7 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
                   "output staging space");
     __syncthreads();
     uint16_t* lds = reinterpret_cast<uint16_t*>(&s_tok[0][0]) + t.w * 16 * out_lds_stride<WRG>();
-    const OutScale osc = out_scale_of(a.alpha2[e]);
+    const OutScale osc = out_scale(a.alpha2[e], a.I);
 #pragma unroll
     for (int cb = 0; cb < NCBA; ++cb) {
       // stored at the row's flat id t*k + j (the finalization reads a token's rows as
@@ -420,7 +420,7 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
 #pragma unroll
       for (int r = 0; r < WRG; ++r) blk[r] = acc[r][cb];
       store_out_block<WRG>(blk, osc, lds, lane, flat, td.nrows - cb * 16, a.o_rows, a.o_exp,
-                           a.H, a.k, a.k_inv, 16 * G0);
+                           a.H, 16 * G0);
     }
   }
 }
@@ -495,7 +495,7 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 // out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[t*k + j, 8v..8v+7]), j in order, fp32 fused
 // multiply-add; rows whose id was dropped (gather-map entry < 0) are skipped.  FC2 stored
 // the rows in flat id order, so a token's k rows are one contiguous run; a stored value is
-// o * 2^s with s the exponent of its 32-column segment, so it enters the sum with the
+// o * 2^s with s the exponent of its row (its expert's), so it enters the sum with the
 // weight w * 2^-s (exact).  A workgroup covers 8*kFinThreads columns of one token; each
 // thread owns 8 columns and issues the 16-byte loads of up to kFinBatch rows before it
 // accumulates them.
@@ -511,9 +511,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
   if (v >= a.H / 8) return;
   const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
-  // the k exponents of this thread's 32-column segment, in j order
-  const int8_t* __restrict__ exp_v =
-      a.o_exp + (t * (a.H / kOutSeg) + v / (kOutSeg / 8)) * a.k;
+  // the token's k row exponents, in j order
+  const int8_t* __restrict__ exp_v = a.o_exp + t * a.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
     u32x4 d[kFinBatch];

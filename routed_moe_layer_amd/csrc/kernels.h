@@ -174,7 +174,6 @@ hipError_t launch_prepare_weights(int H, int I, int E, const uint8_t* w13,
 struct LayerArgs {
   int H, I, Ip, E, k, T;
   int cus, xcds;               // compute units and XCDs (L2 domains) of the device
-  uint64_t k_inv;              // ceil(2^32 / k): t = (f * k_inv) >> 32 for flat ids f < 2^26
   const uint8_t* x_codes;      // [T, H/2]
   const uint8_t* x_scales;     // [T, H/16]
   const uint16_t* x_dec;       // [T, H] f16: code times block scale
@@ -198,7 +197,7 @@ struct LayerArgs {
   uint8_t* a_scales;           // [T*k, I/16]
   float* a_amax;               // [E]
   uint16_t* o_rows;            // [T*k, H] f16 O * 2^s, row t*k + j (flat id order)
-  int8_t* o_exp;               // [T, H/32, k] exponent s of each 32-column segment
+  int8_t* o_exp;               // [T*k] exponent s of each FC2 output row (its expert's)
   const uint16_t* route_weights;
   uint16_t* out;               // [T, H]
 };

@@ -91,6 +91,15 @@ def fmt(res):
             f"{res['ratio_all']:.3f})")
 
 
+def out_exponents(alpha2, I):
+    """The FC2 row exponent of each expert: s = clamp(141 - E, -126, 126) with E the fp32
+    biased exponent of |alpha2| * I * 2688^2 (the bound on an FC2 sum of I products of two
+    decoded NVFP4 values), so that every stored value O * 2^s is below 2^15."""
+    b = np.abs(np.asarray(alpha2, np.float32)) * (np.float32(I) * np.float32(2688 * 2688))
+    e = (b.astype(np.float32).view(np.uint32) >> 23) & 0xFF
+    return np.clip(141 - e.astype(np.int64), -126, 126)
+
+
 def check_layer(p, gpu_out, inter, ref):
     """All parity checks of one moe_forward call against the grouped oracle (see above)."""
     cfg = p["cfg"]
@@ -121,6 +130,10 @@ def check_layer(p, gpu_out, inter, ref):
                          w2d, p["alpha2"][e])
         dy[t] += float(oracle.bf16_bits_to_f32(p["rw"][t, j])) * dO
     res = check_output(gpu_out, ref["out_f64"], dy)
+    # FC2 row exponents: the expert's, for every row of an in-range id
+    f, e = ref["sorted_row_idx"], ref["sorted_ids"]
+    ok = f >= 0
+    assert np.array_equal(inter["o_exp"][f[ok]], out_exponents(p["alpha2"], cfg.I)[e[ok]])
     # amax statistic: per expert max |SiTU output| of the expert's rows
     amax_ref = np.zeros(cfg.E, np.float32)
     np.maximum.at(amax_ref, ref["sorted_ids"], np.max(np.abs(ref["a"]), axis=1))

@@ -71,9 +71,8 @@ def prepare(cfg, w13, w13_sf, w2, w2_sf):
 
 def _fc2_rows(vals, exps):
     """FC2 output rows [R, H] as float64 from the stored f16 values and the exponent s of
-    each 32-column segment (value = stored * 2^-s)."""
-    scale = np.ldexp(1.0, -np.repeat(exps.astype(np.int64), 32, axis=1))
-    return vals.astype(np.float64) * scale
+    each row (value = stored * 2^-s)."""
+    return vals.astype(np.float64) * np.ldexp(1.0, -exps.astype(np.int64))[:, None]
 
 
 class DeviceLayer:
@@ -133,8 +132,7 @@ class DeviceLayer:
             "a_codes": take("a_codes", R * cfg.I // 2, np.uint8, (R, cfg.I // 2)),
             "a_scales": take("a_scales", R * cfg.I // 16, np.uint8, (R, cfg.I // 16)),
             "o_rows": _fc2_rows(take("o_rows", R * cfg.H, np.float16, (R, cfg.H)),
-                                take("o_exp", R * (cfg.H // 32), np.int8,
-                                     (T, cfg.H // 32, cfg.k)).transpose(0, 2, 1)
-                                .reshape(R, cfg.H // 32)),
+                                take("o_exp", R, np.int8, (R,))),
+            "o_exp": take("o_exp", R, np.int8, (R,)).copy(),
             "a_amax": take("a_amax", cfg.E, np.float32, (cfg.E,)),
         }

@@ -55,9 +55,9 @@ def test_noalloc_equals_moe_forward_on_two_calls_the_second_smaller():
 
 def test_noalloc_rejects_batches_beyond_its_array():
     d = rm.MoeDims(3584, 384, 896, 16)
-    assert rm.moe_workspace_size(d, 259) <= rm.MOE_NOALLOC_SCRATCH_BYTES
-    assert rm.moe_workspace_size(d, 260) > rm.MOE_NOALLOC_SCRATCH_BYTES
+    assert rm.moe_workspace_size(d, 262) <= rm.MOE_NOALLOC_SCRATCH_BYTES
+    assert rm.moe_workspace_size(d, 263) > rm.MOE_NOALLOC_SCRATCH_BYTES
     with pytest.raises(rm.MoeError) as ei:
-        rm.moe_forward_noalloc(d, 260, 4096, 8192, 8192, 1 << 20, 256, 512, 768, 1024, None,
+        rm.moe_forward_noalloc(d, 263, 4096, 8192, 8192, 1 << 20, 256, 512, 768, 1024, None,
                                None, 1 << 22, stream=0)
     assert ei.value.status == -2                       # unsupported: before any GPU work
