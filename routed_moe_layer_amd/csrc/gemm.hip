@@ -497,46 +497,49 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 // the rows in flat id order, so a token's k rows are one contiguous run; a stored value is
 // o * 2^s with s the exponent of its row (its expert's), so it enters the sum with the
 // weight w * 2^-s (exact).  A workgroup covers 8*kFinThreads columns of one token; each
-// thread owns 8 columns and issues the 16-byte loads of up to kFinBatch rows before it
-// accumulates them.
-constexpr int kFinThreads = 512, kFinBatch = 8;
+// thread owns 8 columns and issues the 16-byte loads of NB rows at a time before it
+// accumulates them.  The row loads do not wait for the gather map: every row t*k + j lies
+// in the FC2 output, and a dropped row's (unwritten) values are loaded but not used, so
+// the map, weight, exponent and row loads of a batch are in flight together.
+constexpr int kFinThreads = 512;
 
-// K8: k is a multiple of kFinBatch, so each batch's exponents are one 8-byte load; else
-// one byte load per row (index clamped: every load is unconditional and the loads of a
-// batch stay in flight together).
-template <bool K8>
+// VEC: k is a multiple of NB, so a batch's exponents are one NB-byte load; else one byte
+// load per row (index clamped: every load is unconditional).
+template <int NB, bool VEC>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int col_blocks) {
   const int64_t t = blockIdx.x / col_blocks;
   const int v = (blockIdx.x % col_blocks) * blockDim.x + threadIdx.x;
   if (v >= a.H / 8) return;
   const int32_t* __restrict__ pos_t = a.expanded_row_idx + t * a.k;
   const uint16_t* __restrict__ w_t = a.route_weights + t * a.k;
-  // the token's k row exponents, in j order
-  const int8_t* __restrict__ exp_v = a.o_exp + t * a.k;
+  const int8_t* __restrict__ exp_t = a.o_exp + t * a.k;     // the token's k row exponents
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < a.k; j0 += kFinBatch) {
-    u32x4 d[kFinBatch];
-    int32_t sx[kFinBatch];
-    bool ok[kFinBatch];
-    uint2 e8;
-    if constexpr (K8) e8 = *reinterpret_cast<const uint2*>(exp_v + j0);
-#pragma unroll
-    for (int u = 0; u < kFinBatch; ++u) {
-      const int j = j0 + u;
-      ok[u] = j < a.k && pos_t[j] >= 0;         // < 0: dropped (expert id out of range)
-      // read once, never again: nontemporal, so the rows do not displace cached data
-      d[u] = ok[u] ? __builtin_nontemporal_load(
-                         reinterpret_cast<const u32x4*>(a.o_rows + (t * a.k + j) * a.H) + v)
-                   : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (K8)
-        sx[u] = static_cast<int8_t>(((u < 4 ? e8.x : e8.y) >> (8 * (u & 3))) & 0xFFu);
-      else
-        sx[u] = exp_v[min(j, a.k - 1)];
+  for (int j0 = 0; j0 < a.k; j0 += NB) {
+    u32x4 d[NB];
+    int32_t sx[NB];
+    bool ok[NB];
+    uint32_t e4[NB / 4 > 0 ? NB / 4 : 1];
+    if constexpr (VEC && NB == 16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(exp_t + j0);
+      e4[0] = q.x; e4[1] = q.y; e4[2] = q.z; e4[3] = q.w;
+    } else if constexpr (VEC && NB == 8) {
+      const uint2 q = *reinterpret_cast<const uint2*>(exp_t + j0);
+      e4[0] = q.x; e4[1] = q.y;
     }
 #pragma unroll
-    for (int u = 0; u < kFinBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u, jc = min(j, a.k - 1);
+      ok[u] = j < a.k && pos_t[jc] >= 0;        // < 0: dropped (expert id out of range)
+      // read once, never again: nontemporal, so the rows do not displace cached data
+      d[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(a.o_rows + (t * a.k + jc) * a.H) + v);
+      if constexpr (VEC) sx[u] = static_cast<int8_t>((e4[u / 4] >> (8 * (u & 3))) & 0xFFu);
+      else sx[u] = exp_t[jc];
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
       if (!ok[u]) continue;
-      const float wt = bf16_to_f32(w_t[j0 + u]) *
+      const float wt = bf16_to_f32(w_t[min(j0 + u, a.k - 1)]) *
                        __uint_as_float(static_cast<uint32_t>(127 - sx[u]) << 23);
       const uint32_t dw[4] = {d[u][0], d[u][1], d[u][2], d[u][3]};
 #pragma unroll
@@ -640,10 +643,12 @@ hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
   const int per_block = (vecs + col_blocks - 1) / col_blocks;
   const int threads = (per_block + 63) / 64 * 64;
   const int64_t grid = static_cast<int64_t>(a.T) * col_blocks;
-  if (grid > 0 && a.k % kFinBatch == 0)
-    finalize_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
-  else if (grid > 0)
-    finalize_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream>>>(a, col_blocks);
+  const dim3 g(static_cast<unsigned>(grid)), b(threads);
+  if (grid == 0) return hipSuccess;
+  if (a.k % 16 == 0) finalize_kernel<16, true><<<g, b, 0, stream>>>(a, col_blocks);
+  else if (a.k % 8 == 0) finalize_kernel<8, true><<<g, b, 0, stream>>>(a, col_blocks);
+  else if (a.k > 8) finalize_kernel<16, false><<<g, b, 0, stream>>>(a, col_blocks);
+  else finalize_kernel<8, false><<<g, b, 0, stream>>>(a, col_blocks);
   return hipGetLastError();
 }
 

@@ -297,9 +297,17 @@ __device__ __forceinline__ void rank_wave_ids(const int32_t* __restrict__ ids, i
                                               int32_t* expanded_row_idx,
                                               int (&key)[kIdsPerThread],
                                               int (&rank)[kIdsPerThread]) {
+  // all of the wave's id loads in flight together (unconditional, index clamped)
+  int keys[kIdsPerThread];
+#pragma unroll
   for (int r = 0; r < kIdsPerThread; ++r) {
     const int64_t f = wave_base + r * kWave + lane;
-    int e = route_key(ids, f, n, e_base);
+    const uint32_t raw = n > 0 ? static_cast<uint32_t>(ids[min(f, n - 1)]) : 0u;
+    keys[r] = f < n ? static_cast<int>(raw - static_cast<uint32_t>(e_base)) : -1;
+  }
+  for (int r = 0; r < kIdsPerThread; ++r) {
+    const int64_t f = wave_base + r * kWave + lane;
+    int e = keys[r];
     // An id outside the routed range is dropped (never counted, never scattered) and its
     // position-map entry is -1, so no kernel indexes with it.
     const bool valid = key_valid(e, E);
