@@ -555,7 +555,8 @@ def traffic_from_profile(kernel):
 # Profile summaries: turn the CSV output of the rocprofv3 runs (kernel trace per workload,
 # FETCH_SIZE / WRITE_SIZE counters, and the plain-copy calibration) into the text
 # summaries under profiles/ and the traffic table the roofline line reads.
-PROFILE_WORKLOADS = {"prefill": "PREFILL_16K", "decode": "DECODE_16", "mid": "MID_1024"}
+PROFILE_WORKLOADS = {"prefill": "PREFILL_16K", "decode": "DECODE_16", "mid": "MID_1024",
+                     "decode64": "DECODE_64", "prefill4k": "PREFILL_4K"}
 
 
 def _read_csv(path):
