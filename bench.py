@@ -717,8 +717,9 @@ def _summarize_routing(src, out_dir, cmd_trace):
           "Command (run from the repository root, after "
           "`cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd_trace.format(w="route"), "```", "",
           "Per-kernel statistics (all calls of the run: moe_route on "
-          "route_N8192_H7168_E256_K8_zipf1.1_int8, then the moe_route_v2 cases, each with "
-          "its warmup and timed calls; `at::` kernels are the benchmark's own input setup):", "",
+          "route_N8192_H7168_E256_K8_zipf1.1 with int8 and with NVFP4 rows, then the "
+          "moe_route_v2 cases, each with its warmup and timed calls; `at::` kernels are the "
+          "benchmark's own input setup):", "",
           "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in _read_csv(stats)[:14]:
         md.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
@@ -737,7 +738,11 @@ def _summarize_routing(src, out_dir, cmd_trace):
             if not calls or _short(r["Kernel_Name"]).startswith(starts):
                 calls.append([])
             calls[-1].append(r)
-        cases = [("moe_route", line)] + [(c, r) for c, r in line.get("options", {}).items()]
+        # dispatch order: moe_route (int8), moe_route (NVFP4), then the moe_route_v2 cases
+        cases = [("moe_route", line)]
+        if "nvfp4" in line:
+            cases.append(("moe_route_nvfp4", line["nvfp4"]))
+        cases += [(c, r) for c, r in line.get("options", {}).items()]
         names = sorted({_short(r["Kernel_Name"]) for r in kern})
         per_case = len(calls) // len(cases)
         md += ["", "Per case (kernel average µs over its calls; HIP-event time per call of "
@@ -751,7 +756,7 @@ def _summarize_routing(src, out_dir, cmd_trace):
                 d = [(int(c["End_Timestamp"]) - int(c["Start_Timestamp"])) / 1e3 for c in chunk
                      if _short(c["Kernel_Name"]) == n]
                 cells.append(f"{sum(d) / len(d):.1f}" if d else "—")
-            us = r["ms_per_call"] * 1e3 if case == "moe_route" else r["us_per_call"]
+            us = r["ms_per_call"] * 1e3 if case.startswith("moe_route") else r["us_per_call"]
             label = r["workload"]
             md.append(f"| {label} | " + " | ".join(cells) + f" | {us:.1f} | "
                       f"{100 * r['hbm_frac']:.1f}% |")
@@ -863,7 +868,7 @@ def main():
     hr = results[head]
     hcfg = cfgs[head][0]
     fc1_ms = hr["fc1"]["ms"]
-    if head == "prefill":
+    if hcfg.T >= 4096:                 # the MFMA-bound band; smaller batches stream weights
         roof = {"bound": "mfma", "achieved": hr["fc1"]["flops"] / (fc1_ms * 1e-3) / 1e12,
                 "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s"}
     else:
