@@ -493,12 +493,12 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
         !mark(2))
       return MOE_ERR_HIP;
   } else {
-    if ((!quantized && launch_quantize_nvfp4(x, 1, T, H, qx, x_codes, x_scales,
-                                             layer_writes_x_dec(R, a.cus) ? x_dec : nullptr,
-                                             s) != hipSuccess) ||
-        !mark(1))
+    // the quantization runs in the router's scatter launch (both stage marks after it)
+    const QuantizeArgs qa{x, static_cast<int64_t>(T) * (H / kGroup), H / kGroup, T, qx,
+                          x_codes, x_scales, layer_writes_x_dec(R, a.cus) ? x_dec : nullptr};
+    if (launch_route(expert_ids, R, E, b, s, quantized ? nullptr : &qa) != hipSuccess ||
+        !mark(1) || !mark(2))
       return MOE_ERR_HIP;
-    if (launch_route(expert_ids, R, E, b, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
   }
   if (launch_fc1(a, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
   if (launch_fc2(a, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;

@@ -84,8 +84,7 @@ struct RouteBuffers {
   int32_t capacity;          // > 0: the position map holds slot e*capacity + rank within
                              // the expert, or -1 when rank >= capacity
 };
-hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
-                        hipStream_t stream);
+
 
 // Small batches: NVFP4 quantization of the tokens and the router in one launch, when the
 // router runs as a single workgroup (route_fits_one_workgroup).
@@ -99,6 +98,10 @@ struct QuantizeArgs {
   uint8_t* scales;
   uint16_t* decoded;         // or null
 };
+// The routing pipeline; with `fused`, the token quantization it describes runs in the
+// same launches (the scatter's extra workgroups), else nothing more.
+hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
+                        hipStream_t stream, const QuantizeArgs* fused = nullptr);
 bool route_fits_one_workgroup(int64_t n, int E);
 
 // Routing primitive on a few tokens: routing and token movement in one workgroup (see

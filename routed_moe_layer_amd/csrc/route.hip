@@ -378,9 +378,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_seq_kernel(
   }
 }
 
+// Workgroups past the router tiles (when the layer passes its token quantization along)
+// quantize kRouteThreads 16-value blocks each: the two are independent, so they share the
+// launch instead of running back to back.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b) {
+    const int32_t* __restrict__ ids, int64_t n, int E, int nbits, RouteBuffers b,
+    QuantizeArgs qa) {
   extern __shared__ int32_t wave_hist[];           // [4][E]
+  const int64_t ntiles = (n + kRouteTile - 1) / kRouteTile;
+  if (static_cast<int64_t>(blockIdx.x) >= ntiles) {  // uniform over the workgroup
+    const int64_t blk = static_cast<int64_t>(blockIdx.x - ntiles) * kRouteThreads + threadIdx.x;
+    if (blk < qa.nblocks)
+      quantize_nvfp4_block(qa.src, blk, qa.blocks_per_row, qa.rows_per_group, qa.q, qa.codes,
+                           qa.scales, qa.decoded);
+    return;
+  }
   const int nw = kRouteThreads / kWave;
   for (int i = threadIdx.x; i < nw * E; i += blockDim.x) wave_hist[i] = 0;
   __syncthreads();
@@ -605,9 +617,24 @@ hipError_t launch_quantize_route_small(const QuantizeArgs& qa, const int32_t* id
 }
 
 hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers& b,
-                        hipStream_t stream) {
+                        hipStream_t stream, const QuantizeArgs* fused) {
   const int nt = route_tiles(n);
   if (nt == 0) return hipSuccess;
+  // the token quantization rides along with the scatter launch (the many-expert scatter
+  // and the one-workgroup router run it as a launch of its own first)
+  QuantizeArgs qa{};
+  const bool fuse = fused != nullptr && fused->nblocks > 0 && !route_fits_one_workgroup(n, E) &&
+                    E <= kScatterWaveHistMaxE;
+  if (fused != nullptr && fused->nblocks > 0 && !fuse) {
+    const int64_t rows = fused->nblocks / fused->blocks_per_row;
+    const hipError_t e = launch_quantize_nvfp4(
+        fused->src, rows / fused->rows_per_group, fused->rows_per_group,
+        fused->blocks_per_row * kGroup, fused->q, fused->codes, fused->scales, fused->decoded,
+        stream);
+    if (e != hipSuccess) return e;
+  }
+  if (fuse) qa = *fused;
+  const int64_t qgroups = (qa.nblocks + kRouteThreads - 1) / kRouteThreads;
   const size_t small_lds = (kRouteThreads / kWave + 1) * static_cast<size_t>(E) * sizeof(int32_t);
   if (route_fits_one_workgroup(n, E)) {
     route_small_kernel<<<dim3(1), dim3(kRouteSmallThreads), small_lds, stream>>>(
@@ -622,9 +649,9 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int E, const RouteBuffers
                            dim3(kScanExperts * kScanWaves), 0, stream>>>(b, nt, E);
   route_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(b, nt, E, counted);
   if (E <= kScatterWaveHistMaxE)
-    route_scatter_kernel<<<dim3(nt), dim3(kRouteThreads),
+    route_scatter_kernel<<<dim3(static_cast<unsigned>(nt + qgroups)), dim3(kRouteThreads),
                            (kRouteThreads / kWave) * E * sizeof(int32_t), stream>>>(
-        ids, n, E, bits_for(E), b);
+        ids, n, E, bits_for(E), b, qa);
   else
     route_scatter_seq_kernel<<<dim3(nt), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
         ids, n, E, bits_for(E), b);
