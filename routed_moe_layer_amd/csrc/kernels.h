@@ -86,8 +86,9 @@ struct RouteBuffers {
 };
 
 
-// Small batches: NVFP4 quantization of the tokens and the router in one launch, when the
-// router runs as a single workgroup (route_fits_one_workgroup).
+// The layer's token quantization as extra workgroups of a router launch: with the
+// single-workgroup router (route_fits_one_workgroup; launch_quantize_route_small) or with
+// the scatter of the tiled router (launch_route with `fused`).
 struct QuantizeArgs {
   const uint16_t* src;       // BF16 rows
   int64_t nblocks;           // 16-value blocks in all rows
