@@ -42,6 +42,27 @@ def build_layer_problem(cfg: LayerConfig, calib_tokens=None, w13_bits=None, w2_b
     return p
 
 
+def constant_weight_problem(cfg: LayerConfig, seed=7):
+    """A layer whose FC2 sums reach their bound I * 2688^2: every gate row of an expert holds
+    one value a_e, every up row one value b_e and every W2 entry one value c_e (BF16).  Each
+    weight then quantizes to code 6 with block scale 448 (decoded 2688), FC1 gives a token
+    one gate and one up value, so its SiTU output is the same in every channel, and with a
+    qA per expert the expert's largest-output token requantizes to code 6, scale 448 in
+    every block: its FC2 sums are +-I * 2688^2."""
+    from moe_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w13 = np.empty((E, 2 * I, H), np.uint16)
+    w2 = np.empty((E, H, I), np.uint16)
+    for e in range(E):
+        a, b, c = rng.uniform(0.01, 0.05, 3).astype(np.float32)
+        sign = np.float32(1.0 if e % 2 == 0 else -1.0)
+        w13[e, :I] = f32_to_bf16_bits(np.full((I, H), a, np.float32))
+        w13[e, I:] = f32_to_bf16_bits(np.full((I, H), b, np.float32))
+        w2[e] = f32_to_bf16_bits(np.full((H, I), sign * c, np.float32))
+    return build_layer_problem(cfg, w13_bits=w13, w2_bits=w2, per_expert_qa=True)
+
+
 def oracle_forward(p):
     return oracle.layer_forward(p["x"], p["ids"], p["rw"], p["w13"], p["w13_sf"], p["w2"],
                                 p["w2_sf"], p["qX"], p["alpha1"], p["qA"], p["alpha2"],

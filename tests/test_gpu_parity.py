@@ -13,7 +13,7 @@ import oracle
 import routed_moe_layer_amd as rm
 from moe_inputs import (TINY, ROUTE_8K, LayerConfig, draw_expert_ids, draw_route_inputs,
                         f32_to_bf16_bits)
-from tests.problem import build_layer_problem, oracle_forward
+from tests.problem import build_layer_problem, constant_weight_problem, oracle_forward
 from tests.gpu_harness import (dev, host, empty_bytes, check_guard, quantize_on_gpu, prepare,
                                DeviceLayer)
 from tests import compare
@@ -329,6 +329,32 @@ EDGE = [
     ("qa_per_expert_many_rows", _edge("edge_qa_many", T=8192, E=64, k=8, H=512, I=256,
                                       zipf_s=1.0, seed_index=51), "qa"),
 ]
+
+
+def test_fc2_sums_at_their_bound():
+    """FC2 sums equal to the bound I * 2688^2 the row exponent is taken from (constant
+    weights, a qA per expert; tests.problem.constant_weight_problem): those rows' stored
+    f16 values sit in the top binade [2^14, 2^15] and must neither overflow nor lose bits;
+    the whole layer meets the parity bar."""
+    cfg = _edge("edge_bound", T=32, E=4, k=2, H=256, I=64, seed_index=52)
+    _say("layer edge fc2_sums_at_their_bound")
+    p = constant_weight_problem(cfg)
+    ref = oracle_forward(p)
+    _, out, inter = _run_layer(p)
+    st, res = compare.check_layer(p, out, inter, ref)
+    flat = ref["sorted_row_idx"]
+    o_gpu = inter["o_rows"][flat]
+    assert np.all(np.isfinite(o_gpu))
+    # rows whose intermediate codes match the oracle's: f16 keeps 11 significant bits of
+    # each value (plus one fp32 rounding of the scaled sum)
+    same = np.ones(len(flat), bool)
+    same[st["rows_with_diff"]] = False
+    ref_o = ref["o"].astype(np.float64)
+    assert np.all(np.abs(o_gpu - ref_o)[same] <= 2.0 ** -10 * np.abs(ref_o)[same])
+    s_row = inter["o_exp"][flat].astype(np.int64)
+    stored = np.abs(o_gpu) * np.ldexp(1.0, s_row)[:, None]
+    assert 2.0 ** 14 <= stored.max() <= 2.0 ** 15
+    _say(f"  largest stored value {stored.max():.1f}; {compare.fmt(res)}")
 
 
 @pytest.mark.parametrize("name,cfg,mod", EDGE, ids=[c[0] for c in EDGE])

@@ -11,7 +11,8 @@ import torch
 import oracle
 from oracle import layer as olayer
 from moe_inputs import TINY
-from tests.problem import build_layer_problem, oracle_forward, oracle_dense
+from tests.problem import (build_layer_problem, constant_weight_problem, oracle_forward,
+                           oracle_dense)
 
 
 @pytest.fixture(scope="module")
@@ -189,3 +190,26 @@ def test_intermediate_calibration_against_dense_brute_force(ntok):
     assert len(np.unique(dA[seen])) > 1                       # distinct per expert
     dS, qS = oracle.calibrate_intermediate(*args)
     assert np.all(dS == d_shared) and np.all(qS == np.float32(1.0) / d_shared)
+
+
+def test_constant_weights_reach_the_fc2_bound():
+    """The bound the FC2 row exponent is taken from, |FC2 sum| <= I * 2688^2, is reached:
+    with constant weights and a qA per expert each expert's largest-output row has FC2
+    outputs alpha2 * (+-I * 2688^2) (checked through the decoded intermediate, not the
+    construction's claim)."""
+    cfg = dataclasses.replace(TINY, name="const_w", T=32, E=4, k=2, H=256, I=64)
+    p = constant_weight_problem(cfg)
+    ref = oracle_forward(p)
+    r = oracle.route(p["ids"], cfg.E)
+    start = 0
+    for e in range(cfg.E):
+        cnt = int(r["counts"][e])
+        if cnt == 0:
+            continue
+        pos = np.arange(start, start + cnt)
+        start += cnt
+        adec = oracle.dequantize_nvfp4(ref["a_codes"][pos], ref["a_scales"][pos])
+        top = int(np.argmax(np.max(np.abs(adec), axis=1)))
+        assert np.all(np.abs(adec[top]) == 2688.0)
+        bound = np.float64(cfg.I) * 2688.0 ** 2
+        assert np.all(np.abs(ref["o"][pos[top]]) == np.float32(abs(p["alpha2"][e]) * bound))
