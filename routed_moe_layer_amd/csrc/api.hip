@@ -500,8 +500,13 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
         !mark(1) || !mark(2))
       return MOE_ERR_HIP;
   }
-  if (launch_fc1(a, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
-  if (launch_fc2(a, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+  if (layer_small_fused_fits(a)) {
+    // FC1 and FC2 in one launch (both stage marks after it)
+    if (launch_layer_small_fused(a, s) != hipSuccess || !mark(3) || !mark(4)) return MOE_ERR_HIP;
+  } else {
+    if (launch_fc1(a, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+    if (launch_fc2(a, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+  }
   if (launch_finalize(a, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
 }

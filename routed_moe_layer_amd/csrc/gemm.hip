@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "fc2_tile.h"
 #include "gemm_util.h"
 #include "kernels.h"
 
@@ -617,6 +618,82 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
     launch_variant<MODE, kBigNW, kBigWRG, kBigRows, kBigWPE, kRows>(a, a.max_big, 1, stream);
   } else {
     launch_variant<MODE, 4, 2, kBigRows, 1, kRows>(a, a.max_big, 1, stream);
+  }
+  return hipGetLastError();
+}
+
+// Fused FC1 + FC2 for batches with at most one routed row per compute unit (so at most
+// that many small tiles, one per CU): a workgroup of kFusedNW waves takes one small tile
+// and runs FC1 over all 2I rows of its expert in one sweep (WRG1 = 2I/(16*kFusedNW) row
+// groups per wave, the same tile body as the FC1 kernels), then, once its intermediate
+// codes are written, stages them as FC2's token tile and sweeps all H/(64*kFusedNW) FC2
+// slabs of kFusedNW waves x 4 row groups over it (the FC2 tile body).  There is no launch
+// boundary between FC1 and FC2, and each CU streams its expert's FC1 and FC2 weights back
+// to back with every wave of the workgroup loading.
+constexpr int kFusedNW = 8;
+
+template <int WRG1, int NCH>
+__global__ __launch_bounds__(kFusedNW * 64) void layer_small_fused_kernel(LayerArgs a) {
+  using Stage = StageOf<0, kFusedNW, kSmallRows, true>;
+  __shared__ _Float16 s_tok[2][kSmallRows * Stage::kLdsRow];
+  __shared__ int64_t s_row[kSmallRows];
+  __shared__ float s_enc[128];
+  __shared__ _Float16 s_tok2[kSmallRows * kFc2LdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[kFusedNW * 16 * out_lds_stride<4>()];
+  static_assert(WRG1 % 2 == 0, "gate/up row-group pairs per wave");
+
+  const int tt = blockIdx.x;
+  if (tt >= a.num_tiles[0]) return;
+  TileCtx t;
+  t.td = a.tiles_small[tt];
+  t.e = t.td.expert;
+  t.tid = threadIdx.x; t.lane = t.tid & 63; t.w = t.tid >> 6; t.g = t.lane >> 4;
+  if (t.tid < kSmallRows) {
+    const int r = t.td.row_start + min(t.tid, t.td.nrows - 1);
+    s_row[t.tid] = static_cast<int64_t>(a.sorted_row_idx[r] / a.k);
+  }
+  __syncthreads();
+  t.nchunks = a.H / kChunk;
+  const int RG = 2 * a.I / 16;
+  t.G0 = __builtin_amdgcn_readfirstlane(t.w) * WRG1;
+  {
+    t.groups = RG;
+    const int64_t expert_chunks = static_cast<int64_t>(RG) * t.nchunks;
+    const uint8_t* wc = a.w13_codes + t.e * expert_chunks * 1024;
+    const uint8_t* wsc = a.w13_scales + t.e * expert_chunks * 128;
+    t.wcodes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wc), 0,
+                                                 static_cast<int>(expert_chunks * 1024), kBufferFlags);
+    t.wscales = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wsc), 0,
+                                                  static_cast<int>(expert_chunks * 128), kBufferFlags);
+    t.lane_code_off = 16u * t.lane;
+    t.lane_scale_off = 4u * static_cast<uint32_t>(prepared_scale_index(0, t.lane));
+  }
+  Stage st;
+  st.init(a, s_row, t.w, t.lane);
+  const int ncb = (t.td.nrows + 15) / 16;
+  if (ncb == 1) tile_body<0, kFusedNW, WRG1, kSmallRows, true, 1>(a, t, st, s_tok, s_enc);
+  else tile_body<0, kFusedNW, WRG1, kSmallRows, true, 2>(a, t, st, s_tok, s_enc);
+  __syncthreads();                        // the tile's intermediate codes are written
+  fc2_stage_tile(a, t.td, ncb, s_tok2, t.tid, kFusedNW * 64);
+  __syncthreads();
+  const int n_slabs = a.H / (kFusedNW * 4 * 16);
+  if (ncb == 1) fc2_tile<kFusedNW, 4, kSmallRows, 1, NCH>(a, t.td, 0, n_slabs, s_tok2, s_out);
+  else fc2_tile<kFusedNW, 4, kSmallRows, 2, NCH>(a, t.td, 0, n_slabs, s_tok2, s_out);
+}
+
+bool layer_small_fused_fits(const LayerArgs& a) {
+  const int64_t R = static_cast<int64_t>(a.T) * a.k;
+  return R <= a.cus && R <= kSmallOnlyRows && a.I % 128 == 0 && a.I <= kFc2MaxIp &&
+         a.I == a.Ip && a.H % (kFusedNW * 4 * 16) == 0;
+}
+
+hipError_t launch_layer_small_fused(const LayerArgs& a, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(a.max_small)), b(kFusedNW * 64);
+  if (a.max_small == 0) return hipSuccess;
+  switch (a.I / kChunk) {
+    case 1: layer_small_fused_kernel<2, 1><<<g, b, 0, stream>>>(a); break;
+    case 2: layer_small_fused_kernel<4, 2><<<g, b, 0, stream>>>(a); break;
+    default: layer_small_fused_kernel<6, 3><<<g, b, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }

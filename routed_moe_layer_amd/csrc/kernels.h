@@ -206,6 +206,10 @@ struct LayerArgs {
   uint16_t* out;               // [T, H]
 };
 hipError_t launch_fc1(const LayerArgs& a, hipStream_t stream);
+// FC1 and FC2 in one launch when every routed row can have a CU of its own
+// (layer_small_fused_fits); launch_fc1 + launch_fc2 otherwise.
+bool layer_small_fused_fits(const LayerArgs& a);
+hipError_t launch_layer_small_fused(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream);
 // FC2 with the whole token tile resident in LDS (when the padded I fits; fc2.hip).
 bool fc2_resident_fits(const LayerArgs& a);

@@ -318,6 +318,20 @@ EDGE = [
     # split into 32-row tiles, and no big-tile kernel is launched
     ("small_batch_split_experts", _edge("edge_split", T=90, E=4, k=2, H=256, I=128,
                                         seed_index=47), None),
+    # at most one routed row per compute unit with H a multiple of 512 and I of 128: FC1
+    # and FC2 fused in one workgroup per small tile (I = 128, 256, 384: 2, 4, 6 row groups
+    # per wave in FC1, one to three K chunks in FC2), with ragged tiles, an expert split
+    # over several tiles, duplicate ids and a qA per expert
+    ("fused_small_I128", _edge("edge_fused_a", T=8, E=16, k=4, H=512, I=128, seed_index=53),
+     None),
+    ("fused_small_I256_ragged", _edge("edge_fused_b", T=16, E=8, k=8, H=1024, I=256,
+                                      seed_index=54), None),
+    ("fused_small_I384_qa", _edge("edge_fused_c", T=8, E=32, k=16, H=512, I=384,
+                                  seed_index=55), "qa"),
+    ("fused_small_one_expert_many_tiles", _edge("edge_fused_d", T=40, E=2, k=2, H=512,
+                                                I=128, seed_index=56), None),
+    ("fused_small_duplicate_ids", _edge("edge_fused_e", T=24, E=16, k=4, H=512, I=256,
+                                        seed_index=57), "dup"),
     # a qA per expert (each expert's scale from its own rows): the requantization must use
     # the scale of the row's expert in every kernel instance -- small tiles, big tiles with
     # 2 and 4 row groups per wave, and the 65536-row kernels
