@@ -407,9 +407,12 @@ def test_layer_determinism_poisoned_workspace_and_reuse():
     assert np.array_equal(a, d)
 
 
-def test_layer_graph_capture_replay():
-    _say("layer hipGraph capture/replay")
-    p = build_layer_problem(_edge("edge_graph", T=20, E=16, k=4, seed_index=41))
+@pytest.mark.parametrize("shape", ["separate_gemms", "fused_gemms"])
+def test_layer_graph_capture_replay(shape):
+    _say(f"layer hipGraph capture/replay ({shape})")
+    cfg = (_edge("edge_graph", T=20, E=16, k=4, seed_index=41) if shape == "separate_gemms"
+           else _edge("edge_graph_fused", T=16, E=32, k=8, H=512, I=256, seed_index=58))
+    p = build_layer_problem(cfg)
     prepared = prepare(p["cfg"], p["w13"], p["w13_sf"], p["w2"], p["w2_sf"])
     L = DeviceLayer(p, prepared)
     eager = host(L.forward().clone(), np.uint16)
