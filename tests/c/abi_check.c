@@ -55,6 +55,23 @@ int main(void) {
   CHECK(moe_route_v2(64, 256, 32, 8, (const uint16_t*)0x1000, (const int32_t*)0x2000, NULL, NULL,
                      &o, (void*)0x3000, (int32_t*)0x4000, NULL, NULL, NULL, (void*)0x5000,
                      route, 0) == MOE_ERR_INVALID_ARG);
+  /* layouts and sizes over many batch sizes and expert counts (host arithmetic only) */
+  for (int T = 1; T <= MOE_MAX_TOKENS; T += 997) {
+    size_t n = 0;
+    moe_workspace_layout_t l;
+    CHECK(moe_workspace_size(d, T, MOE_QUANT_NVFP4_G16, &n) == MOE_OK);
+    CHECK(moe_workspace_layout(d, T, &l) == MOE_OK && l.total <= n && l.o_exp < l.total);
+  }
+  size_t sealed = 0;
+  CHECK(moe_sealed_workspace_size(d, 16384, &sealed) == MOE_OK && sealed > 0);
+  for (int E = 1; E <= 10240; E = 2 * E + 1)
+    CHECK(moe_route_workspace_size(4096, 8, E, &route) == MOE_OK && route > 0);
+  CHECK(moe_route_workspace_size(4096, 8, 10241, &route) != MOE_OK);
+  /* the allocation-free entry point rejects batches beyond its fixed array up front */
+  CHECK(moe_forward_noalloc(d, 263, (const uint16_t*)0x1000, (const int32_t*)0x2000,
+                            (const uint16_t*)0x3000, (const void*)0x4000, (const float*)0x5000,
+                            (const float*)0x6000, (const float*)0x7000, (const float*)0x8000,
+                            NULL, NULL, (uint16_t*)0x9000, 0) == MOE_ERR_UNSUPPORTED);
   CHECK(strcmp(moe_status_string(MOE_OK), "ok") == 0);
   CHECK(moe_status_string((moe_status_t)12345) != NULL);
 
