@@ -332,6 +332,20 @@ EDGE = [
                                                 I=128, seed_index=56), None),
     ("fused_small_duplicate_ids", _edge("edge_fused_e", T=24, E=16, k=4, H=512, I=256,
                                         seed_index=57), "dup"),
+    # tokens whose x is all zero (after calibration, so the scales stay those of the
+    # random batch): zero block scales and codes for x, zero FC1 and SiTU rows, zero
+    # intermediate scales and an exact zero output row, in every kernel instance --
+    # separate small tiles, the fused small-batch kernel, big tiles, the 65536-row kernels
+    # -- and a batch that is zero throughout (every expert's amax 0)
+    ("zero_tokens_small", _edge("edge_zero_s", T=24, E=16, k=4, seed_index=58), "zero_rows"),
+    ("zero_tokens_fused", _edge("edge_zero_f", T=16, E=8, k=8, H=1024, I=256,
+                                seed_index=59), "zero_rows"),
+    ("zero_tokens_big", _edge("edge_zero_b", T=300, E=4, k=4, H=256, I=128, seed_index=60),
+     "zero_rows"),
+    ("zero_tokens_many_rows", _edge("edge_zero_m", T=4096, E=64, k=16, H=256, I=128,
+                                    seed_index=61), "zero_rows"),
+    ("zero_batch", _edge("edge_zero_all", T=300, E=4, k=4, H=256, I=128, seed_index=62),
+     "zero_all"),
     # a qA per expert (each expert's scale from its own rows): the requantization must use
     # the scale of the row's expert in every kernel instance -- small tiles, big tiles with
     # 2 and 4 row groups per wave, and the 65536-row kernels
@@ -383,9 +397,17 @@ def test_layer_edge_cases(name, cfg, mod):
     elif mod == "dup":
         p["ids"] = p["ids"].copy()
         p["ids"][:, 1] = p["ids"][:, 0]
+    elif mod in ("zero_rows", "zero_all"):
+        p["x"] = p["x"].copy()
+        zero = slice(None) if mod == "zero_all" else slice(None, None, 3)
+        p["x"][zero] = 0
     ref = oracle_forward(p)
     _, out, inter = _run_layer(p)
     st, res = compare.check_layer(p, out, inter, ref)
+    if mod in ("zero_rows", "zero_all"):
+        # the bound is 0 on a zero row: its output must be exactly zero
+        assert not np.any(ref["out_f64"][zero])
+        assert not np.any(out[zero] & 0x7FFF)
     _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, {compare.fmt(res)}")
 
 
