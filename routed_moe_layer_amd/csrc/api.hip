@@ -478,9 +478,10 @@ static moe_status_t forward_impl(moe_dims_t d, int32_t T, const uint16_t* x,
   b.expanded_row_idx = expanded_row_idx;
   b.tiles_small = reinterpret_cast<TileDesc*>(ws + L.tiles_small);
   b.tiles_big = reinterpret_cast<TileDesc*>(ws + L.tiles_big);
-  b.runs = reinterpret_cast<TileDesc*>(ws + L.runs);
   b.num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   b.small_only = R <= kSmallOnlyRows ? 1 : 0;
+  // FC2's runs group big tiles; a batch of small tiles only has none (and skips their scan)
+  b.runs = b.small_only ? nullptr : reinterpret_cast<TileDesc*>(ws + L.runs);
   b.amax_reset = a.a_amax;
   uint8_t* x_codes = ws + L.pub.x_codes;
   uint8_t* x_scales = ws + L.pub.x_scales;

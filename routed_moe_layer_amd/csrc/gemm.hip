@@ -497,7 +497,7 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
 // multiply-add; rows whose id was dropped (gather-map entry < 0) are skipped.  FC2 stored
 // the rows in flat id order, so a token's k rows are one contiguous run; a stored value is
 // o * 2^s with s the exponent of its row (its expert's), so it enters the sum with the
-// weight w * 2^-s (exact).  A workgroup covers 8*kFinThreads columns of one token; each
+// weight w * 2^-s (exact).  A workgroup covers up to 8*kFinThreads columns of one token; each
 // thread owns 8 columns and issues the 16-byte loads of NB rows at a time before it
 // accumulates them.  The row loads do not wait for the gather map: every row t*k + j lies
 // in the FC2 output, and a dropped row's (unwritten) values are loaded but not used, so
@@ -714,9 +714,14 @@ hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream) {
-  // whole waves covering a token's H/8 vectors in as few workgroups as possible
+  // whole waves covering a token's H/8 vectors in as few workgroups as possible; a batch
+  // of fewer than two tokens per CU splits each token's columns further (down to one wave
+  // per workgroup), since one CU streams only a small share of the HBM bandwidth
   const int vecs = a.H / 8;
-  const int col_blocks = (vecs + kFinThreads - 1) / kFinThreads;
+  const int min_blocks = (vecs + kFinThreads - 1) / kFinThreads;
+  const int max_blocks = (vecs + 63) / 64;
+  const int want = static_cast<int>((2 * static_cast<int64_t>(a.cus) + a.T - 1) / max(a.T, 1));
+  const int col_blocks = max(min_blocks, min(want, max_blocks));
   const int per_block = (vecs + col_blocks - 1) / col_blocks;
   const int threads = (per_block + 63) / 64 * 64;
   const int64_t grid = static_cast<int64_t>(a.T) * col_blocks;

@@ -72,30 +72,52 @@ __device__ __forceinline__ int field(uint64_t v, int i) {
   return static_cast<int>((v >> shift) & ((uint64_t{1} << bits) - 1));
 }
 
+// One DPP step of a wave scan on a 64-bit value: lane i takes the value of the lane the
+// row control selects (zero where that lane lies outside the row or the row is masked).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_take64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, ROW_MASK, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, ROW_MASK, 0xF, true));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Inclusive scan over the 64 lanes of a wave: prefix sums within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8 lanes, then lane 15 of rows 0 and 2 added to rows 1 and 3, and
+// lane 31 (the total of rows 0-1) to rows 2 and 3.
+__device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t x) {
+  x += dpp_take64<0x111, 0xF>(x);      // row_shr:1
+  x += dpp_take64<0x112, 0xF>(x);      // row_shr:2
+  x += dpp_take64<0x114, 0xF>(x);      // row_shr:4
+  x += dpp_take64<0x118, 0xF>(x);      // row_shr:8
+  x += dpp_take64<0x142, 0xA>(x);      // row_bcast:15 into rows 1 and 3
+  x += dpp_take64<0x143, 0xC>(x);      // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Block-wide exclusive scan of one uint64 per thread (any multiple of 64 threads up to
 // 1024); returns the exclusive prefix and writes the total to *total.
 __device__ uint64_t block_excl_scan64(uint64_t v, uint64_t* sh, uint64_t* total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
   const int nw = blockDim.x / kWave;
-  uint64_t incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint64_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const uint64_t incl = wave_incl_scan64(v);
   if (lane == kWave - 1) sh[w] = incl;
   __syncthreads();
-  if (w == 0) {
-    uint64_t x = lane < nw ? sh[lane] : 0;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint64_t o = __shfl_up(x, off);
-      if (lane >= off) x += o;
-    }
-    if (lane < nw) sh[lane] = x;                  // inclusive over waves
-  }
-  __syncthreads();
-  const uint64_t wave_excl = w == 0 ? 0 : sh[w - 1];
-  *total = sh[nw - 1];
-  __syncthreads();
+  // every wave scans the (at most 16) wave totals itself
+  const uint64_t x = wave_incl_scan64(lane < nw ? sh[lane] : 0);
+  const uint64_t wave_excl = w == 0 ? 0 : readlane64(x, w - 1);
+  *total = readlane64(x, nw - 1);
+  __syncthreads();                                // sh is free for the next scan
   return wave_excl + incl - v;
 }
 
@@ -179,7 +201,7 @@ __device__ void scan_experts_finish(const RouteBuffers& b, int E, const int* car
     if (b.num_tiles) {
       b.num_tiles[0] = carry[1];
       b.num_tiles[1] = carry[2];
-      if (b.runs) b.num_tiles[2] = carry[3];
+      b.num_tiles[2] = b.runs ? carry[3] : 0;
     }
   }
   if (b.key_value)
