@@ -238,7 +238,8 @@ using StageOf = typename std::conditional<ROWS, RowStage<NW, BN>, CodeStage<MODE
 // With WRG == 4 the weight fragments are decoded one 32-column K-step at a time and
 // software-pipelined: step s+1's fragments are decoded while step s's MFMAs run.  Chunk
 // c+2's weight loads are issued in step 3, after the last decode of chunk c.  The LDS
-// operand of each 16-token block is read one block ahead, across K-steps within the chunk.
+// operand of each 16-token block is read two blocks ahead, across K-steps within the
+// chunk, and each fragment's block scale comes from one packed FP8 -> f16 conversion.
 template <int WRG, int NCBA, int DEPTH, class Stage>
 __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, int c,
                                            uint4 (&wc)[WRG], uint32_t (&ws)[WRG],
@@ -250,7 +251,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
 #pragma unroll
     for (int r = 0; r < WRG; ++r) {
       const uint32_t cw = s == 0 ? rc[r].x : s == 1 ? rc[r].y : s == 2 ? rc[r].z : rc[r].w;
-      dst[r] = decode8(cw, scale_f16x2((rs[r] >> (8 * s)) & 0xFFu));
+      dst[r] = decode8(cw, scale_f16x2_of(rs[r], s));
     }
   };
   if constexpr (kPerStep) {
@@ -259,7 +260,14 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
     __syncthreads();                                    // LDS buffer of chunk c complete
     f16x8 wf0[WRG], wf1[WRG];
     decode_from(wc, ws, 0, wf0);
-    f16x8 xf = *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, 0, 0, t.lane));
+    // The token operands of the chunk's 4*NCBA (K-step, block) items, in order, are read
+    // two items ahead of their MFMAs.
+    constexpr int kItems = 4 * NCBA;
+    auto frag_of = [&](int i) {
+      return *reinterpret_cast<const f16x8*>(Stage::frag(tb_cur, i % NCBA, i / NCBA, t.lane));
+    };
+    f16x8 xf = frag_of(0);
+    f16x8 x1 = kItems > 1 ? frag_of(1) : xf;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -269,18 +277,16 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
       else load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const bool ahead = cb + 1 < NCBA || s < 3;
-        const f16x8 xn = ahead
-            ? *reinterpret_cast<const f16x8*>(
-                  Stage::frag(tb_cur, cb + 1 < NCBA ? cb + 1 : 0, cb + 1 < NCBA ? s : s + 1, t.lane))
-            : xf;
+        const int i = s * NCBA + cb;
+        const f16x8 x2 = i + 2 < kItems ? frag_of(i + 2) : x1;
 #pragma unroll
         for (int r = 0; r < WRG; ++r) acc[r][cb] = mfma16x16x32(cur[r], xf, acc[r][cb]);
-        xf = xn;
+        xf = x1;
+        x1 = x2;
       }
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        if (cb + 1 < NCBA || s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (s * NCBA + cb + 2 < kItems) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
         for (int r = 0; r < WRG; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
