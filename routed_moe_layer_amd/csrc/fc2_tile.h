@@ -77,34 +77,41 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   auto step = [&](const int j, const int c, W2Regs<WRG>& cur) {
     // Software pipeline over the four 32-column K-steps: the weight fragments of step s+1
     // are decoded while the MFMAs of step s run (interleaved: per 16-token block one LDS
-    // operand read, then each MFMA followed by two VALU instructions).  After the last
-    // decode the set is refilled with step q+2 (slab clamped: surplus loads past the last
-    // slab are unused and unconditional, so the compiler's load counters stay exact).
+    // operand read, two blocks ahead, then each MFMA followed by two VALU instructions).
+    // After the last decode the set is refilled with step q+2 (slab clamped: surplus loads
+    // past the last slab are unused and unconditional, so the compiler's load counters stay
+    // exact).
     f16x8 wf[2][WRG];
     decode(cur, 0, wf[0]);
+    // the token operands of the chunk's 4*NCBA (K-step, block) items, in order, are read
+    // two items ahead of their MFMAs
+    constexpr int kItems = 4 * NCBA;
+    auto frag_of = [&](int i) {
+      return *reinterpret_cast<const f16x8*>(xrow + c * kChunk + 32 * (i / NCBA) +
+                                             (i % NCBA) * 16 * kFc2LdsRow);
+    };
+    f16x8 xf = frag_of(0);
+    f16x8 x1 = kItems > 1 ? frag_of(1) : xf;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) decode(cur, s + 1, wf[(s + 1) & 1]);
       else fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
-      // token operand of block cb+1 is read while block cb's MFMAs run
-      const _Float16* xs = xrow + c * kChunk + 32 * s;
-      f16x8 xf = *reinterpret_cast<const f16x8*>(xs);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
-        const f16x8 xn = cb + 1 < NCBA
-            ? *reinterpret_cast<const f16x8*>(xs + (cb + 1) * 16 * kFc2LdsRow) : xf;
+        const int i = s * NCBA + cb;
+        const f16x8 x2 = i + 2 < kItems ? frag_of(i + 2) : x1;
 #pragma unroll
         for (int r = 0; r < WRG; ++r)
           acc[r][cb] = mfma16x16x32(wf[s & 1][r], xf,
                                     (c == 0 && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[r][cb]);
-        xf = xn;
+        xf = x1;
+        x1 = x2;
       }
       if (s < 3) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read, block 0
 #pragma unroll
         for (int cb = 0; cb < NCBA; ++cb) {
-          if (cb + 1 < NCBA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // block cb+1
+          if (s * NCBA + cb + 2 < kItems) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
           for (int r = 0; r < WRG; ++r) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
