@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fc2_stationary_kernel(LayerArgs a)
 
     W2Regs<WRG> wr[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) fc2_load<NW, WRG>(a, e, w, lane, slab, c, NCH, wr[c]);
+    for (int c = 0; c < NCH; ++c) fc2_load<NW, WRG, kBigRows>(a, e, w, lane, slab, c, NCH, wr[c]);
     // the block scales of K-steps (0, 1) and (2, 3) of every chunk and row group, as f16
     f16x2 wsc[NCH][WRG][2];
 #pragma unroll

@@ -21,17 +21,27 @@ struct W2Regs {
 
 // A wave's weight fragments of (slab j, chunk c): WRG 16-row groups x 16 code bytes and
 // one scale dword per lane.
-template <int NW, int WRG>
+// (TILE_ROWS: the token tile's capacity, which sets the cache policy, weight_load_policy)
+template <int NW, int WRG, int TILE_ROWS>
 __device__ __forceinline__ void fc2_load(const LayerArgs& a, int e, int w, int lane, int j,
                                          int c, int nchunks, W2Regs<WRG>& dst) {
   constexpr int kSlabGroups = NW * WRG;
-  const uint4* __restrict__ wcodes = reinterpret_cast<const uint4*>(a.w2_codes);
+  const u32x4* __restrict__ wcodes = reinterpret_cast<const u32x4*>(a.w2_codes);
   const uint32_t* __restrict__ wscales = reinterpret_cast<const uint32_t*>(a.w2_scales);
   const int64_t chunk0 = prepared_chunk(e, c, j * kSlabGroups + w * WRG, nchunks, a.H / 16);
 #pragma unroll
   for (int r = 0; r < WRG; ++r) {
-    dst.c[r] = wcodes[(chunk0 + r) * 64 + lane];
-    dst.s[r] = wscales[prepared_scale_index(chunk0 + r, lane)];
+    const u32x4* pc = wcodes + (chunk0 + r) * 64 + lane;
+    const uint32_t* ps = wscales + prepared_scale_index(chunk0 + r, lane);
+    if constexpr (weight_load_policy(TILE_ROWS) == kNontemporal) {
+      const u32x4 v = __builtin_nontemporal_load(pc);
+      dst.c[r] = uint4{v[0], v[1], v[2], v[3]};
+      dst.s[r] = __builtin_nontemporal_load(ps);
+    } else {
+      const u32x4 v = *pc;
+      dst.c[r] = uint4{v[0], v[1], v[2], v[3]};
+      dst.s[r] = *ps;
+    }
   }
 }
 
@@ -96,7 +106,7 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) decode(cur, s + 1, wf[(s + 1) & 1]);
-      else fc2_load<NW, WRG>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
+      else fc2_load<NW, WRG, BN>(a, e, w, lane, min(j + (c + 2) / NCH, last), (c + 2) % NCH, NCH, cur);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
         const int i = s * NCBA + cb;
@@ -138,8 +148,8 @@ __device__ __forceinline__ void fc2_tile(const LayerArgs& a, const TileDesc& td,
   };
 
   W2Regs<WRG> setA, setB;
-  fc2_load<NW, WRG>(a, e, w, lane, slab0, 0, NCH, setA);
-  fc2_load<NW, WRG>(a, e, w, lane, min(slab0 + 1 / NCH, last), 1 % NCH, NCH, setB);
+  fc2_load<NW, WRG, BN>(a, e, w, lane, slab0, 0, NCH, setA);
+  fc2_load<NW, WRG, BN>(a, e, w, lane, min(slab0 + 1 / NCH, last), 1 % NCH, NCH, setB);
   int j = slab0;
   for (; j + 1 <= last; j += 2) {
 #pragma unroll

@@ -76,16 +76,16 @@ struct TileCtx {
   uint32_t lane_code_off, lane_scale_off;
 };
 
-template <int WRG>
+template <int WRG, int POLICY>
 __device__ __forceinline__ void load_weights(const TileCtx& t, int c, uint4 (&wc)[WRG],
                                              uint32_t (&ws)[WRG]) {
 #pragma unroll
   for (int r = 0; r < WRG; ++r) {
     const uint32_t chunk = static_cast<uint32_t>(c * t.groups + t.G0 + r);
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(t.wcodes, t.lane_code_off,
-                                                          chunk * 1024u, 0);
+                                                          chunk * 1024u, POLICY);
     wc[r] = uint4{v[0], v[1], v[2], v[3]};
-    ws[r] = __builtin_amdgcn_raw_buffer_load_b32(t.wscales, t.lane_scale_off, chunk * 128u, 0);
+    ws[r] = __builtin_amdgcn_raw_buffer_load_b32(t.wscales, t.lane_scale_off, chunk * 128u, POLICY);
   }
 }
 
@@ -103,6 +103,7 @@ __device__ __forceinline__ void load_weights(const TileCtx& t, int c, uint4 (&wc
 // j ^ (r % 16), so the 16 rows of an operand read hit 16 different slots.
 template <int NW, int BN>
 struct RowStage {
+  static constexpr int kTileRows = BN;
   static constexpr int kPieces = BN / (4 * NW);        // 16-byte pieces per thread
   static constexpr int kLdsRow = kChunk;
   static_assert(BN % (4 * NW) == 0, "row staging split");
@@ -155,6 +156,7 @@ struct RowStage {
 // padded I) read as zero codes with a zero scale.  LDS rows are padded by 16 bytes.
 template <int MODE, int NW, int BN>
 struct CodeStage {
+  static constexpr int kTileRows = BN;
   static constexpr int kThreadsPerRow = NW * 64 / BN;
   static constexpr int kNdw = 16 / kThreadsPerRow;     // code dwords (of 16 per row)
   static constexpr int kLdsRow = kChunk + 8;
@@ -274,7 +276,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
       f16x8 (&cur)[WRG] = (s & 1) ? wf1 : wf0;
       f16x8 (&nxt)[WRG] = (s & 1) ? wf0 : wf1;
       if (s < 3) decode_from(wc, ws, s + 1, nxt);
-      else load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
+      else load_weights<WRG, weight_load_policy(Stage::kTileRows)>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
 #pragma unroll
       for (int cb = 0; cb < NCBA; ++cb) {
         const int i = s * NCBA + cb;
@@ -307,7 +309,7 @@ __device__ __forceinline__ void chunk_step(const TileCtx& t, const Stage& st, in
   // counts stay exact instead of draining every outstanding load.
   const bool more = c + 1 < t.nchunks;
   st.template load<16 * NCBA>(min(c + 1, t.nchunks - 1), tr);
-  load_weights<WRG>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
+  load_weights<WRG, weight_load_policy(Stage::kTileRows)>(t, min(c + DEPTH, t.nchunks - 1), wc, ws);
   __syncthreads();                                      // LDS buffer of chunk c complete
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -342,7 +344,7 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
   uint32_t ws[DEPTH][WRG];
   typename Stage::Regs tr;
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) load_weights<WRG>(t, min(i, t.nchunks - 1), wc[i], ws[i]);
+  for (int i = 0; i < DEPTH; ++i) load_weights<WRG, weight_load_policy(BN)>(t, min(i, t.nchunks - 1), wc[i], ws[i]);
   st.template load<16 * NCBA>(0, tr);
   st.template store<16 * NCBA>(s_tok[0], tr);
   // DEPTH chunks per trip so register sets and LDS buffers are named statically; the

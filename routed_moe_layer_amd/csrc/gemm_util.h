@@ -31,6 +31,15 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
 
+// Cache policy of a weight stream.  Small token tiles (at most kSmallRows rows, one per
+// lightly used expert) read each weight once per layer call, so their streams are
+// nontemporal (the "nt" bit of a buffer load): a CU streams such loads about 15% faster
+// than plain ones (27.6 against 24-25 GB/s per CU on the MI355X).  Big tiles keep the
+// default policy: the several tiles of a heavily used expert reread its weights from the
+// L2, which nontemporal loads would give up.
+constexpr int kNontemporal = 2;
+constexpr int weight_load_policy(int tile_rows) { return tile_rows <= kSmallRows ? kNontemporal : 0; }
+
 // FC2 output rows (workspace "o_rows"): routed row f = t*k + j's FC2 output O[f, h] =
 // alpha2 * acc is kept as the f16 value of O * 2^s, with one exponent s per expert, stored
 // as an int8 in o_exp[f] for the finalization (which recovers O by an exact multiplication
