@@ -177,9 +177,11 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // 2i in the low nibble of byte i).
 __device__ __forceinline__ uint32_t nvfp4_quantize16(const uint16_t* __restrict__ src, float q,
                                                      uint2* codes) {
-  const uint4* p = reinterpret_cast<const uint4*>(src);
-  const uint4 lo = p[0], hi = p[1];
-  const uint32_t wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  // read once: nontemporal (a CU streams such loads faster, and they leave the caches to
+  // the data that is reread)
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  const u32x4 lo = __builtin_nontemporal_load(p), hi = __builtin_nontemporal_load(p + 1);
+  const uint32_t wv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   float v[16];
   float amax = 0.0f;
 #pragma unroll
