@@ -434,23 +434,33 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
   }
 }
 
-template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-void grouped_gemm_kernel(LayerArgs a, int big) {
+// The LDS of one workgroup of a variant: the double-buffered token tile, the tile's
+// token rows and (FC1's requantization) the encode factor qa/s of every E4M3 scale byte s
+// of the tile's expert, divided once per tile instead of once per 16-value block.
+template <int MODE, int NW, int BN, bool ROWS>
+struct GemmLds {
+  _Float16 tok[2][BN * StageOf<MODE, NW, BN, ROWS>::kLdsRow];
+  int64_t row[BN];
+  float enc[128];
+};
+
+// Workgroup b of a variant's grid (b counts from the variant's first workgroup; the grid
+// starts at a multiple of the XCD count): token tile and weight slab from b, then the tile
+// body.
+template <int MODE, int NW, int WRG, int BN, bool ROWS>
+__device__ __forceinline__ void gemm_workgroup(const LayerArgs& a, int big, int b,
+                                               GemmLds<MODE, NW, BN, ROWS>& L) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
   using Stage = StageOf<MODE, NW, BN, ROWS>;
-  __shared__ _Float16 s_tok[2][BN * Stage::kLdsRow];
-  __shared__ int64_t s_row[BN];
-  // FC1's requantization: the encode factor qa/s of every E4M3 scale byte s of this
-  // tile's expert, divided once per tile instead of once per 16-value block
-  __shared__ float s_enc[128];
-
+  auto& s_tok = L.tok;
+  int64_t* s_row = L.row;
+  float* s_enc = L.enc;
   const TileDesc* tiles = big ? a.tiles_big : a.tiles_small;
   const int ntiles = a.num_tiles[big];
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const int n_wt = rows_total / C::kWgRows;
   int tt, wt;
-  map_workgroup(blockIdx.x, n_wt, a.xcds, &tt, &wt);
+  map_workgroup(b, n_wt, a.xcds, &tt, &wt);
   if (tt >= ntiles) return;
   TileCtx t;
   t.td = tiles[tt];
@@ -499,6 +509,31 @@ void grouped_gemm_kernel(LayerArgs a, int big) {
       default: tile_body<MODE, NW, WRG, BN, ROWS, 7>(a, t, st, s_tok, s_enc); break;   // kBigTileRows
     }
   }
+}
+
+
+template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void grouped_gemm_kernel(LayerArgs a, int big) {
+  __shared__ GemmLds<MODE, NW, BN, ROWS> lds;
+  gemm_workgroup<MODE, NW, WRG, BN, ROWS>(a, big, blockIdx.x, lds);
+}
+
+// Both tile lists in one launch: the big tiles' workgroups first (the longest, so they
+// start first), then the small tiles' in the rest of the grid.  The two kinds run side by
+// side: the big tiles of a skewed batch's hot experts are few, long and MFMA-heavy, the
+// small tiles many and bound by the weight stream.
+template <int MODE, int NW, int WRG_B, int BN_B, int WRG_S, int BN_S, int WPE, bool ROWS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void grouped_gemm_pair_kernel(LayerArgs a, int grid_big) {
+  using LB = GemmLds<MODE, NW, BN_B, ROWS>;
+  using LS = GemmLds<MODE, NW, BN_S, ROWS>;
+  __shared__ __attribute__((aligned(16))) char lds[sizeof(LB) > sizeof(LS) ? sizeof(LB) : sizeof(LS)];
+  if (static_cast<int>(blockIdx.x) < grid_big)
+    gemm_workgroup<MODE, NW, WRG_B, BN_B, ROWS>(a, 1, blockIdx.x, *reinterpret_cast<LB*>(lds));
+  else
+    gemm_workgroup<MODE, NW, WRG_S, BN_S, ROWS>(a, 0, blockIdx.x - grid_big,
+                                                *reinterpret_cast<LS*>(lds));
 }
 
 // out[t, 8v..8v+7] = BF16(sum_j w[t, j] * o[t*k + j, 8v..8v+7]), j in order, fp32 fused
@@ -582,12 +617,17 @@ constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
 // workgroups fit the chip in one round instead of 1.3.
 constexpr int kFc1SmallWRG = 4;
 
+template <int MODE, int NW, int WRG, int BN>
+static int64_t variant_grid(const LayerArgs& a, int64_t max_tiles) {
+  using C = GemmCfg<MODE, NW, WRG, BN>;
+  const int rows_total = MODE == 0 ? 2 * a.I : a.H;
+  return round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows), a.xcds * kXcdRun);
+}
+
 template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
 static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipStream_t stream) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
-  const int rows_total = MODE == 0 ? 2 * a.I : a.H;
-  const int64_t grid = round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows),
-                                a.xcds * kXcdRun);
+  const int64_t grid = variant_grid<MODE, NW, WRG, BN>(a, max_tiles);
   if (grid > 0)
     grouped_gemm_kernel<MODE, NW, WRG, BN, WPE, ROWS>
         <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
@@ -605,6 +645,21 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
     if (small_wide) launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, false>(a, a.max_small, 0, stream);
     else launch_variant<MODE, 4, 2, kSmallRows, 1, false>(a, a.max_small, 0, stream);
   } else if (small_wide) {
+    if constexpr (MODE == 0) {
+      // a batch with big tiles and f16 rows of x (the mid-size batches): both lists in one
+      // launch
+      const bool pair = static_cast<int64_t>(a.T) * a.k > kSmallOnlyRows &&
+                        rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
+      if (pair) {
+        const int64_t gb = variant_grid<MODE, kBigNW, kBigWRG, kBigRows>(a, a.max_big);
+        const int64_t gs = variant_grid<MODE, 4, kFc1SmallWRG, kSmallRows>(a, a.max_small);
+        static_assert(kBigNW == 4, "one workgroup size for both tile kinds");
+        if (gb + gs > 0)
+          grouped_gemm_pair_kernel<MODE, 4, kBigWRG, kBigRows, kFc1SmallWRG, kSmallRows, kBigWPE, true>
+              <<<dim3(static_cast<unsigned>(gb + gs)), dim3(256), 0, stream>>>(a, static_cast<int>(gb));
+        return hipGetLastError();
+      }
+    }
     launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, kRows>(a, a.max_small, 0, stream);
   } else {
     launch_variant<MODE, 4, 2, kSmallRows, 1, kRows>(a, a.max_small, 0, stream);
