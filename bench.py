@@ -593,7 +593,8 @@ def _bench_line(log_path):
 
 def _short(name):
     n = name.replace("void ", "").replace("rmoe::", "")
-    if n.startswith(("grouped_gemm_kernel", "fc2_kernel", "fc2_stationary_kernel", "finalize",
+    if n.startswith(("grouped_gemm_kernel", "grouped_gemm_pair_kernel", "fc2_kernel",
+                     "fc2_stationary_kernel", "finalize",
                      "quantize", "route", "prepare", "topk", "layer_small_fused_kernel")):
         return n.split("(")[0]
     return n if len(n) <= 72 else n[:72] + "..."
@@ -601,7 +602,7 @@ def _short(name):
 
 def _role(name):
     n = _short(name)
-    if n.startswith("grouped_gemm_kernel<0"):
+    if n.startswith(("grouped_gemm_kernel<0", "grouped_gemm_pair_kernel<0")):
         return "fc1_kernel"
     if n.startswith(("grouped_gemm_kernel<1", "fc2_kernel", "fc2_stationary_kernel")):
         return "fc2_kernel"
