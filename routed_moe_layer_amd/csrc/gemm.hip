@@ -633,6 +633,16 @@ static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipSt
         <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
 }
 
+// Both of FC1's tile lists in one launch (grouped_gemm_pair_kernel), 4-wave workgroups.
+template <int WRG_B, int WRG_S, int WPE, bool ROWS>
+static void launch_fc1_pair(const LayerArgs& a, hipStream_t stream) {
+  const int64_t gb = variant_grid<0, 4, WRG_B, kBigRows>(a, a.max_big);
+  const int64_t gs = variant_grid<0, 4, WRG_S, kSmallRows>(a, a.max_small);
+  if (gb + gs > 0)
+    grouped_gemm_pair_kernel<0, 4, WRG_B, kBigRows, WRG_S, kSmallRows, WPE, ROWS>
+        <<<dim3(static_cast<unsigned>(gb + gs)), dim3(256), 0, stream>>>(a, static_cast<int>(gb));
+}
+
 template <int MODE>
 static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   constexpr bool kRows = MODE == 0;
@@ -641,6 +651,16 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   const bool small_wide =
       MODE == 0 && rows_total % GemmCfg<MODE, 4, kFc1SmallWRG, kSmallRows>::kWgRows == 0;
   if (kRows && many) {
+    if constexpr (MODE == 0) {
+      // Both lists in one launch: a batch this large has few small tiles (none when the
+      // routing is even), and their workgroups then finish the big tiles' grid instead of
+      // filling a launch of their own.
+      if (small_wide && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
+        static_assert(kBigNW == 4, "one workgroup size for both tile kinds");
+        launch_fc1_pair<kFc1WideWRG, kFc1SmallWRG, kFc1WideWPE, false>(a, stream);
+        return hipGetLastError();
+      }
+    }
     // no f16 copy of x: the small tiles stage codes too
     if (small_wide) launch_variant<MODE, 4, kFc1SmallWRG, kSmallRows, 2, false>(a, a.max_small, 0, stream);
     else launch_variant<MODE, 4, 2, kSmallRows, 1, false>(a, a.max_small, 0, stream);
@@ -651,12 +671,7 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
       const bool pair = static_cast<int64_t>(a.T) * a.k > kSmallOnlyRows &&
                         rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
       if (pair) {
-        const int64_t gb = variant_grid<MODE, kBigNW, kBigWRG, kBigRows>(a, a.max_big);
-        const int64_t gs = variant_grid<MODE, 4, kFc1SmallWRG, kSmallRows>(a, a.max_small);
-        static_assert(kBigNW == 4, "one workgroup size for both tile kinds");
-        if (gb + gs > 0)
-          grouped_gemm_pair_kernel<MODE, 4, kBigWRG, kBigRows, kFc1SmallWRG, kSmallRows, kBigWPE, true>
-              <<<dim3(static_cast<unsigned>(gb + gs)), dim3(256), 0, stream>>>(a, static_cast<int>(gb));
+        launch_fc1_pair<kBigWRG, kFc1SmallWRG, kBigWPE, true>(a, stream);
         return hipGetLastError();
       }
     }
@@ -666,12 +681,6 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
   }
   // batches of at most kSmallOnlyRows routed rows have small tiles only
   if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows) return hipGetLastError();
-  if constexpr (MODE == 0) {
-    if (many && rows_total % GemmCfg<MODE, kBigNW, kFc1WideWRG, kBigRows>::kWgRows == 0) {
-      launch_variant<MODE, kBigNW, kFc1WideWRG, kBigRows, kFc1WideWPE, false>(a, a.max_big, 1, stream);
-      return hipGetLastError();
-    }
-  }
   // (with many rows there is no f16 copy of x: FC1's fallback slabs stage codes too)
   const bool big_slabs = rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
   if (kRows && many) {
