@@ -100,6 +100,22 @@ def out_exponents(alpha2, I):
     return np.clip(141 - e.astype(np.int64), -126, 126)
 
 
+def flip_widening(p, gc, gs, ref, rows):
+    """dy [T, H]: the exact output effect of the differing intermediate codes of the given
+    rows (reference sorted order; gc unpacked codes and gs scales in that order)."""
+    cfg = p["cfg"]
+    dy = np.zeros((cfg.T, cfg.H))
+    for i in rows:
+        e = int(ref["sorted_ids"][i])
+        f = int(ref["sorted_row_idx"][i])
+        t, j = f // cfg.k, f % cfg.k
+        _, w2d = oracle.expert_weights_decoded(p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], e)
+        dO = flip_effect(gc[i], gs[i], ref["a_codes"][i], ref["a_scales"][i], w2d,
+                         p["alpha2"][e])
+        dy[t] += float(oracle.bf16_bits_to_f32(p["rw"][t, j])) * dO
+    return dy
+
+
 def check_layer(p, gpu_out, inter, ref):
     """All parity checks of one moe_forward call against the grouped oracle (see above)."""
     cfg = p["cfg"]
@@ -119,16 +135,7 @@ def check_layer(p, gpu_out, inter, ref):
     assert st["max_step_same_scale"] <= 1, st
     assert st["frac"] <= CODE_DIFF_FRAC, st
     # output, widened by the exact effect of differing codes
-    dy = np.zeros((cfg.T, cfg.H))
-    k = cfg.k
-    for i in st["rows_with_diff"]:
-        e = int(ref["sorted_ids"][i])
-        f = int(ref["sorted_row_idx"][i])
-        t, j = f // k, f % k
-        _, w2d = oracle.expert_weights_decoded(p["w13"], p["w13_sf"], p["w2"], p["w2_sf"], e)
-        dO = flip_effect(gc[i], inter["a_scales"][i], ref["a_codes"][i], ref["a_scales"][i],
-                         w2d, p["alpha2"][e])
-        dy[t] += float(oracle.bf16_bits_to_f32(p["rw"][t, j])) * dO
+    dy = flip_widening(p, gc, inter["a_scales"], ref, st["rows_with_diff"])
     res = check_output(gpu_out, ref["out_f64"], dy)
     # FC2 row exponents: the expert's, for every row of an in-range id
     f, e = ref["sorted_row_idx"], ref["sorted_ids"]

@@ -71,8 +71,10 @@ def prepare(cfg, w13, w13_sf, w2, w2_sf):
 
 def _fc2_rows(vals, exps):
     """FC2 output rows [R, H] as float64 from the stored f16 values and the exponent s of
-    each row (value = stored * 2^-s)."""
-    return vals.astype(np.float64) * np.ldexp(1.0, -exps.astype(np.int64))[:, None]
+    each row (value = stored * 2^-s).  Rows of dropped ids are never written, so they may
+    hold anything; no check reads them."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        return vals.astype(np.float64) * np.ldexp(1.0, -exps.astype(np.int64))[:, None]
 
 
 class DeviceLayer:

@@ -411,6 +411,40 @@ def test_layer_edge_cases(name, cfg, mod):
     _say(f"  code diffs {st['n_diff']}/{st['n_codes']}, {compare.fmt(res)}")
 
 
+def test_layer_dropped_ids_many_tokens():
+    """Out-of-range expert ids are dropped: their rows add nothing to the output, and a
+    token whose picks are all dropped gets exact zeros.  4096 tokens, so that the
+    finalization runs its persistent form.  The reference is the oracle on the original
+    (valid) ids with the dropped picks' route weights set to zero: 0 * o adds nothing to
+    the float64 sum, and every other row's value does not depend on the dropped ones."""
+    _say("layer dropped ids, 4096 tokens")
+    cfg = _edge("edge_drop", T=4096, E=64, k=8, H=256, I=128, seed_index=63)
+    p = build_layer_problem(cfg)
+    drop = np.zeros(p["ids"].shape, bool)
+    drop[::3, 2] = True
+    drop[5, :] = True                        # every pick of token 5
+    drop[7, 0] = drop[7, 7] = True
+    ref = oracle_forward(dict(p, rw=np.where(drop, np.uint16(0), p["rw"]).astype(np.uint16)))
+    gpu_p = dict(p, ids=np.where(drop, np.int32(cfg.E), p["ids"]).astype(np.int32))
+    _, out, inter = _run_layer(gpu_p)
+    assert np.array_equal(inter["expanded_row_idx"].reshape(drop.shape) < 0, drop)
+    # the kept rows' intermediate codes, in the reference's row order (a dropped row keeps
+    # the reference's codes: its weight there is zero), then the output bound widened by
+    # the exact effect of differing codes, as for every layer case
+    pos = inter["expanded_row_idx"][ref["sorted_row_idx"]]
+    keep = pos >= 0
+    gc, gs = ref["a_codes"].copy(), ref["a_scales"].copy()
+    gc[keep] = compare.unpack(inter["a_codes"])[pos[keep]]
+    gs[keep] = inter["a_scales"][pos[keep]]
+    st = compare.code_diff_stats(gc, gs, ref["a_codes"], ref["a_scales"])
+    assert st["max_step_same_scale"] <= 1 and st["frac"] <= compare.CODE_DIFF_FRAC, st
+    ref_p = dict(p, rw=np.where(drop, np.uint16(0), p["rw"]).astype(np.uint16))
+    res = compare.check_output(out, ref["out_f64"],
+                               compare.flip_widening(ref_p, gc, gs, ref, st["rows_with_diff"]))
+    assert not np.any(out[5] & 0x7FFF)
+    _say(f"  {int(drop.sum())} dropped picks; {compare.fmt(res)}")
+
+
 def test_layer_determinism_poisoned_workspace_and_reuse():
     _say("layer determinism / poisoned workspace")
     p = build_layer_problem(_edge("edge_det", T=48, E=16, k=4, seed_index=40))
