@@ -41,6 +41,12 @@ moe_status_t check_dims(const moe_dims_t& d) {
   return MOE_OK;
 }
 
+// The FC2 row stores index 16-byte pieces of the row output in 32 bits (flat id times
+// H/8 through a 24-bit multiply): the limits above keep both factors and the index in range.
+static_assert(int64_t{MOE_MAX_TOKENS} * 64 <= (int64_t{1} << 20), "flat ids below 2^20");
+static_assert(int64_t{MOE_MAX_TOKENS} * 64 * (16384 / 8) <= (int64_t{1} << 31),
+              "FC2 row piece indices fit 32 bits");
+
 int padded_inter(int I) { return (I + kChunk - 1) / kChunk * kChunk; }
 
 // Streamed front end: ring carving and the device wall-clock rate for wait deadlines.

@@ -93,12 +93,24 @@ __device__ __forceinline__ void store_out_block(const f32x4 (&acc)[WRG], const O
   __builtin_amdgcn_wave_barrier();
   constexpr int kPieces = 2 * WRG;                 // 16-byte pieces per row
   constexpr int kRowsPerPass = 64 / kPieces;
+  constexpr int kPasses = 16 / kRowsPerPass;
+  // every pass's LDS read and row id first, then the stores: one wait for all of them
+  u32x4 v[kPasses];
+  uint32_t flat[kPasses];
 #pragma unroll
-  for (int pass = 0; pass < 16 / kRowsPerPass; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int row = pass * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * S + 8 * piece);
-    const int64_t flat = __shfl(flat_lane, row);
-    if (row < ntok) *reinterpret_cast<u32x4*>(o_rows + flat * H + col0 + 8 * piece) = v;
+    v[pass] = *reinterpret_cast<const u32x4*>(lds + row * S + 8 * piece);
+    flat[pass] = static_cast<uint32_t>(__shfl(flat_lane, row));
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int row = pass * kRowsPerPass + lane / kPieces, piece = lane % kPieces;
+    // the row's 16-byte piece index, flat * H/8 + ..., in 32 bits from one 24-bit multiply
+    // (a flat id is below 2^20 and H/8 at most 2^11; H and col0 are multiples of 8)
+    const uint32_t q = __umul24(flat[pass], static_cast<uint32_t>(H / 8)) +
+                       static_cast<uint32_t>(col0 / 8 + piece);
+    if (row < ntok) reinterpret_cast<u32x4*>(o_rows)[q] = v[pass];
   }
   __builtin_amdgcn_wave_barrier();                 // (the wave's LDS operations run in order)
   if (col0 == 0 && g == 0 && n16 < ntok) o_exp[flat_lane] = static_cast<int8_t>(sc.s);
