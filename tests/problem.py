@@ -4,6 +4,8 @@ Test helper: uses ``moe_inputs`` for the random draws and ``oracle`` for every v
 derived from them.  Nothing here comes from the HIP path.
 """
 
+import sys
+
 import numpy as np
 
 import oracle
@@ -106,7 +108,8 @@ class ExpertStore:
         with ThreadPoolExecutor(threads) as ex:
             for n, _ in enumerate(ex.map(one, experts)):
                 if (n + 1) % 128 == 0:
-                    print(f"    quantized {n + 1}/{len(experts)} experts", flush=True)
+                    print(f"    quantized {n + 1}/{len(experts)} experts", file=sys.stderr,
+                          flush=True)
         E, H, I = cfg.E, cfg.H, cfg.I
         self.experts = experts
         self.w13 = self._View(d13, (E, 2 * I, H // 2))
