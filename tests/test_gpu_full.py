@@ -1,6 +1,8 @@
-"""GPU parity at the full TP8-local shape (H=3584, I=384, E=896, top-16) for the decode
-(T=16), mid (T=1024, Zipf 1.0) and prefill (T=16384, per-expert SiTU, outliers) batches,
-in the launch configuration the benchmark times.
+"""GPU parity at the full TP8-local shape (H=3584, I=384, E=896, top-16) for every batch
+the benchmark times, in its launch configuration: decode (T=16: the fused small-batch
+kernel), T=64 (small tiles, separate FC1 and FC2), mid (T=1024, Zipf 1.0: both FC1 tile
+lists in one launch), T=4096 (per-expert SiTU: code-staged FC1, token-resident FC2 on big
+tiles) and prefill (T=16384, per-expert SiTU, outliers: weight-stationary FC2).
 
 Routing is compared bit for bit in full.  The oracle then evaluates routed rows chosen by
 their position in the expert-sorted order (the GEMMs' token tiles are runs of 16-row blocks
@@ -11,8 +13,8 @@ of one expert's rows, so these cover every position a row can take in a tile):
   * the whole output of 64 tokens: those of the first and last row of every 16-row block
     of the two most loaded experts, then the first and last token (all 16 at T=16), with
     the input codes of those tokens and the codes and FC2 rows of all their picks.
-The mid and prefill batches take a per-expert qA (each expert calibrated on its own rows
-of the calibration tokens), the decode batch one shared qA."""
+The T=1024, T=4096 and T=16384 batches take a per-expert qA (each expert calibrated on
+its own rows of the calibration tokens), the decode batches one shared qA."""
 
 import sys
 
@@ -21,7 +23,8 @@ import pytest
 import torch
 
 import oracle
-from moe_inputs import DECODE_16, MID_1024, PREFILL_16K, draw_all_expert_weights
+from moe_inputs import (DECODE_16, DECODE_64, MID_1024, PREFILL_4K, PREFILL_16K,
+                        draw_all_expert_weights)
 from tests.problem import build_full_problem, oracle_pairs
 from tests.gpu_harness import dev, host, quantize_on_gpu, prepare, DeviceLayer
 from tests import compare
@@ -88,11 +91,16 @@ def selection(cfg):
         first = [t for t in tok if t in in_first]
         second = [t for t in tok if t not in in_first]
         tokens = list(dict.fromkeys(first[:half] + second[:half] + [0, T - 1]))
-        for t in tok:                                    # top up to N_TOKENS
+        # top up to N_TOKENS: the remaining block-edge tokens, then the tokens of the
+        # experts compared row by row, then evenly spaced ones (a batch whose two most
+        # loaded experts have few blocks, T=4096, needs all three)
+        extra = tok + (r["sorted_row_idx"][rows] // k).tolist() + \
+            np.linspace(0, T - 1, N_TOKENS).astype(np.int64).tolist()
+        for t in extra:
             if len(tokens) >= N_TOKENS:
                 break
             if t not in tokens:
-                tokens.append(t)
+                tokens.append(int(t))
         tokens = np.array(tokens[:N_TOKENS])
         flat = r["sorted_row_idx"][rows].astype(np.int64)
         tj = np.stack([flat // k, flat % k], 1)
@@ -102,7 +110,8 @@ def selection(cfg):
     return select
 
 
-CASES = [(DECODE_16, False), (MID_1024, True), (PREFILL_16K, True)]
+CASES = [(DECODE_16, False), (DECODE_64, False), (MID_1024, True), (PREFILL_4K, True),
+         (PREFILL_16K, True)]
 
 
 # the oracle side of one case takes one to two minutes of host time (hundreds of experts)
