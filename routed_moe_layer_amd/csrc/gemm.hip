@@ -434,6 +434,15 @@ __device__ __forceinline__ void tile_body(const LayerArgs& a, const TileCtx& t,
   }
 }
 
+// Consecutive logical workgroups kept on one XCD.  FC1 with code-staged token tiles (many
+// routed rows) keeps a whole group of kTileGroup token tiles with all its n_wt slabs on one
+// XCD, so that the group's token rows, reread for every slab, and each slab's weights,
+// reread for every tile, are both fetched into one L2; elsewhere kXcdRun.
+template <int MODE, bool ROWS>
+__host__ __device__ constexpr int xcd_run(int n_wt) {
+  return MODE == 0 && !ROWS ? kTileGroup * n_wt : kXcdRun;
+}
+
 // The LDS of one workgroup of a variant: the double-buffered token tile, the tile's
 // token rows and (FC1's requantization) the encode factor qa/s of every E4M3 scale byte s
 // of the tile's expert, divided once per tile instead of once per 16-value block.
@@ -460,7 +469,7 @@ __device__ __forceinline__ void gemm_workgroup(const LayerArgs& a, int big, int 
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
   const int n_wt = rows_total / C::kWgRows;
   int tt, wt;
-  map_workgroup(b, n_wt, a.xcds, &tt, &wt);
+  map_workgroup(b, n_wt, a.xcds, &tt, &wt, xcd_run<MODE, ROWS>(n_wt));
   if (tt >= ntiles) return;
   TileCtx t;
   t.td = tiles[tt];
@@ -617,17 +626,19 @@ constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
 // workgroups fit the chip in one round instead of 1.3.
 constexpr int kFc1SmallWRG = 4;
 
-template <int MODE, int NW, int WRG, int BN>
+template <int MODE, int NW, int WRG, int BN, bool ROWS>
 static int64_t variant_grid(const LayerArgs& a, int64_t max_tiles) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
   const int rows_total = MODE == 0 ? 2 * a.I : a.H;
-  return round_up(round_up(max_tiles, kTileGroup) * (rows_total / C::kWgRows), a.xcds * kXcdRun);
+  const int n_wt = rows_total / C::kWgRows;
+  return round_up(round_up(max_tiles, kTileGroup) * n_wt,
+                  static_cast<int64_t>(a.xcds) * xcd_run<MODE, ROWS>(n_wt));
 }
 
 template <int MODE, int NW, int WRG, int BN, int WPE, bool ROWS>
 static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipStream_t stream) {
   using C = GemmCfg<MODE, NW, WRG, BN>;
-  const int64_t grid = variant_grid<MODE, NW, WRG, BN>(a, max_tiles);
+  const int64_t grid = variant_grid<MODE, NW, WRG, BN, ROWS>(a, max_tiles);
   if (grid > 0)
     grouped_gemm_kernel<MODE, NW, WRG, BN, WPE, ROWS>
         <<<dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream>>>(a, big);
@@ -636,8 +647,8 @@ static void launch_variant(const LayerArgs& a, int64_t max_tiles, int big, hipSt
 // Both of FC1's tile lists in one launch (grouped_gemm_pair_kernel), 4-wave workgroups.
 template <int WRG_B, int WRG_S, int WPE, bool ROWS>
 static void launch_fc1_pair(const LayerArgs& a, hipStream_t stream) {
-  const int64_t gb = variant_grid<0, 4, WRG_B, kBigRows>(a, a.max_big);
-  const int64_t gs = variant_grid<0, 4, WRG_S, kSmallRows>(a, a.max_small);
+  const int64_t gb = variant_grid<0, 4, WRG_B, kBigRows, ROWS>(a, a.max_big);
+  const int64_t gs = variant_grid<0, 4, WRG_S, kSmallRows, ROWS>(a, a.max_small);
   if (gb + gs > 0)
     grouped_gemm_pair_kernel<0, 4, WRG_B, kBigRows, WRG_S, kSmallRows, WPE, ROWS>
         <<<dim3(static_cast<unsigned>(gb + gs)), dim3(256), 0, stream>>>(a, static_cast<int>(gb));

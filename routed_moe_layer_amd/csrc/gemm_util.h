@@ -16,9 +16,11 @@ namespace rmoe {
 // slabs while it is still cached.  Grids are whole multiples of xcds * kXcdRun.
 constexpr int kXcdRun = 4, kTileGroup = 4;
 
-__device__ __forceinline__ void map_workgroup(int b, int n_wt, int xcds, int* tt, int* wt) {
+// (run: the number of consecutive logical ids kept on one XCD, kXcdRun unless given)
+__device__ __forceinline__ void map_workgroup(int b, int n_wt, int xcds, int* tt, int* wt,
+                                              int run = kXcdRun) {
   const int xcd = b % xcds, slot = b / xcds;
-  const int L = ((slot / kXcdRun) * xcds + xcd) * kXcdRun + slot % kXcdRun;
+  const int L = ((slot / run) * xcds + xcd) * run + slot % run;
   const int per_group = n_wt * kTileGroup;
   *tt = (L / per_group) * kTileGroup + L % kTileGroup;
   *wt = (L / kTileGroup) % n_wt;
