@@ -36,8 +36,12 @@ __global__ __launch_bounds__(NW * 64) void fc2_kernel(LayerArgs a, int big) {
   const int tt = ts / SPLIT, part = ts % SPLIT;
   if (tt >= ntiles) return;
   TileDesc td = tiles[tt];
-  td.row_start += part * BN;
-  td.nrows = min(BN, td.nrows - part * BN);
+  // a tile of more than BN rows is split into SPLIT sub-tiles of about equal size (whole
+  // 16-row blocks), so that no sub-tile streams all of the expert's weights for a few rows
+  const int blocks = (td.nrows + 15) / 16;
+  const int per = blocks * 16 <= BN ? BN / 16 : (blocks + SPLIT - 1) / SPLIT;
+  td.row_start += part * per * 16;
+  td.nrows = min(per * 16, td.nrows - part * per * 16);
   if (td.nrows <= 0) return;
   // decode the tile's codes, columns [0, Ip), rows below 16*ncb, into LDS (zero past I)
   const int ncb = (td.nrows + 15) / 16;
