@@ -622,9 +622,10 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(LayerArgs a, int 
 // A slab that does not divide the rows falls back to 128-row slabs.
 constexpr int kBigNW = 4, kBigWRG = 2, kBigWPE = 2;
 constexpr int kFc1WideWRG = 4, kFc1WideWPE = 2;
-// FC1 small tiles: 4 row groups per wave (256-row slabs), so that a decode-size batch's
-// workgroups fit the chip in one round instead of 1.3.
-constexpr int kFc1SmallWRG = 4;
+// FC1 small tiles: 4 row groups per wave (256-row slabs) beside big tiles; in batches of
+// small tiles only, 6 (384-row slabs: each expert's 2I = 768 rows in two workgroups
+// instead of three, so each streams a longer run of weights; T=64 FC1 -5%).
+constexpr int kFc1SmallWRG = 4, kFc1SmallOnlyWRG = 6;
 
 template <int MODE, int NW, int WRG, int BN, bool ROWS>
 static int64_t variant_grid(const LayerArgs& a, int64_t max_tiles) {
@@ -683,6 +684,13 @@ static hipError_t launch_gemm(const LayerArgs& a, hipStream_t stream) {
                         rows_total % GemmCfg<MODE, kBigNW, kBigWRG, kBigRows>::kWgRows == 0;
       if (pair) {
         launch_fc1_pair<kBigWRG, kFc1SmallWRG, kBigWPE, true>(a, stream);
+        return hipGetLastError();
+      }
+    }
+    if constexpr (MODE == 0) {
+      if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows &&
+          rows_total % GemmCfg<MODE, 4, kFc1SmallOnlyWRG, kSmallRows>::kWgRows == 0) {
+        launch_variant<MODE, 4, kFc1SmallOnlyWRG, kSmallRows, 2, kRows>(a, a.max_small, 0, stream);
         return hipGetLastError();
       }
     }
