@@ -273,6 +273,13 @@ void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
   launch_fc2_variant<4, 2, kSmallRows, 7>(a, a.max_small, 0, stream);
 }
 
+// Big tiles of a mid-size batch (fewer routed rows than many_rows): 64-row sub-tiles in
+// two groups of 7 slabs, so that each tile spreads over four workgroups (H a multiple of
+// 256).
+void launch_fc2_resident_big_spread(const LayerArgs& a, hipStream_t stream) {
+  launch_fc2_variant<4, 4, kBigRows / 2, 7, 2>(a, a.max_big, 1, stream);
+}
+
 void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream) {
   // The stationary kernel loads a slab's weights once per run, so it pays off when runs
   // span several passes: experts with at least kFc2StationaryRows routed rows on average.

@@ -794,9 +794,10 @@ hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream) {
   if (!fc2_resident_fits(a)) return launch_gemm<1>(a, stream);
   launch_fc2_resident_small(a, stream);
   if (static_cast<int64_t>(a.T) * a.k <= kSmallOnlyRows) return hipGetLastError();
-  // The resident kernel gives each big tile one workgroup; below about two big tiles per
-  // CU that leaves the chip idle, and the grouped kernel (tiles x row slabs) is faster.
+  // With fewer than about two big tiles per CU, each tile is spread over four workgroups
+  // (two sub-tiles x two slab groups); with more, over two (sub-tiles, all slabs each).
   if (many_rows(static_cast<int64_t>(a.T) * a.k, a.cus)) launch_fc2_resident_big(a, stream);
+  else if (a.H % 256 == 0) launch_fc2_resident_big_spread(a, stream);
   else if (a.H % GemmCfg<1, kBigNW, kBigWRG, kBigRows>::kWgRows == 0)
     launch_variant<1, kBigNW, kBigWRG, kBigRows, kBigWPE, false>(a, a.max_big, 1, stream);
   else

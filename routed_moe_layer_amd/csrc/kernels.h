@@ -215,6 +215,7 @@ hipError_t launch_fc2(const LayerArgs& a, hipStream_t stream);
 bool fc2_resident_fits(const LayerArgs& a);
 void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream);
 void launch_fc2_resident_big(const LayerArgs& a, hipStream_t stream);
+void launch_fc2_resident_big_spread(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_finalize(const LayerArgs& a, hipStream_t stream);
 
 // Prepared-weight layout (private).  For a matrix of R rows (multiple of 16) and K columns
