@@ -262,15 +262,17 @@ static void launch_fc2_variant(const LayerArgs& a, int64_t max_tiles, int big,
         <<<dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, stream>>>(a, big);
 }
 
-// Small tiles: 128-row slabs in groups of 7 (four workgroups per tile at H = 3584, each
-// staging the token tile once: fewer stagings than groups of 4, more workgroups than 14);
+// Small tiles: 256-column slabs in groups of 7 (two workgroups per tile at H = 3584, each
+// staging the token tile once: fewer stagings than smaller groups, twice the workgroups
+// of one group of 14), 128-column slabs when H is not a multiple of 256;
 // big tiles: the weight-stationary kernel on 256-column slabs (H a multiple of 256, I of
 // 128, long runs), else the token-resident kernel on 256-column slabs (128 when H is not a
 // multiple of 256), all slabs in one group.
 bool fc2_resident_fits(const LayerArgs& a) { return a.Ip <= kFc2MaxIp; }
 
 void launch_fc2_resident_small(const LayerArgs& a, hipStream_t stream) {
-  launch_fc2_variant<4, 2, kSmallRows, 7>(a, a.max_small, 0, stream);
+  if (a.H % 256 == 0) launch_fc2_variant<4, 4, kSmallRows, 7>(a, a.max_small, 0, stream);
+  else launch_fc2_variant<4, 2, kSmallRows, 7>(a, a.max_small, 0, stream);
 }
 
 // Big tiles of a mid-size batch (fewer routed rows than many_rows): 64-row sub-tiles in
